@@ -1,0 +1,200 @@
+/*
+ * dsv4.h — C ABI of the MI355X (gfx950) sparse MLA hot path for DeepSeek-V4-style
+ * attention over an FP8 paged latent KV cache.
+ *
+ * Sources (the four prhub.com.cn digests of vLLM pull requests):
+ *   [p1] PR #40860 "DeepSeek V4 full model support" — Implementation breakdown, item 2
+ *        (MLA wrapper calls a fused RMSNorm+RoPE+Quant kernel; indexer + sparse SWA backend).
+ *   [p2] PR #42953 "feat: add DeepSeek-V4 XPU attention decode path" — Implementation
+ *        breakdown, items 4 and 6; Key source excerpts (xpu_sparse.py forward_mqa,
+ *        xpu_sparse_decode_fp8.py _dequant_gather_slots_kernel); Review highlights (FP8 type).
+ *   [p3] PR #43385 "[ROCm][DSv4][Perf] Support DeepSeek v4 MTP" — Implementation breakdown,
+ *        item 3; Key source excerpts (rocm.py _combine_topk_swa_indices_kernel).
+ *   [p4] PR #43477 "Enable DeepSeek V4 and GLM-5.1 on SM120" — Key source excerpts
+ *        (flashinfer_mla_sparse_sm120.py forward_mqa; flashinfer_sparse.py supports_sink,
+ *        get_kv_cache_shape; supported kernel block sizes).
+ *
+ * Geometry (fixed): latent D = 576 = 512 no-PE ("nope") + 64 RoPE dims; value/output
+ * Dv = kv_lora_rank = 512 [p4 forward_mqa output shape (T, H, kv_lora_rank)].
+ *
+ * ---------------------------------------------------------------------------------
+ * KV cache byte layout (this library's own specification; the pages name the content
+ * of a record but give no byte order, and disagree across architectures [p2 Motivation
+ * vs p4 get_kv_cache_shape]).  The cache is an array of pages of P slots each
+ * (P = page_size, only 64 is accepted).  Page p starts at byte p * P * 648 and holds
+ *     +0          nope codes  uint8 [P][512]   FP8 OCP E4M3 ("e4m3fn", max 448)
+ *     +P*512      rope values bf16  [P][64]    stored already rotated
+ *     +P*640      scale bytes uint8 [P][8]     UE8M0, one per 64 nope dims
+ * Slot s lives in page s / P at row s % P [p2 dequant kernel: block_idx / pos_in_block].
+ * Dequantised nope value d of slot s = e4m3(code) * 2^(scale[d/64] - 127) [p2 dequant
+ * kernel], which is exactly representable in bf16.  648 bytes per token record.
+ * ---------------------------------------------------------------------------------
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are device pointers owned by the caller.  The library never
+ *    allocates, frees or synchronises; it enqueues kernels on `stream` (a hipStream_t,
+ *    NULL = the legacy default stream) and returns.  Results are visible after the
+ *    stream is synchronised.
+ *  - Host-side argument checks run before any launch.  On failure the call returns a
+ *    non-zero dsv4_status, sets a thread-local reason string (dsv4_last_error) and
+ *    touches no memory [p4 supports_combination returns a reason string].
+ *  - A launch failure returns DSV4_ERR_HIP with the HIP error text as the reason.
+ *  - Bad values inside device arrays are defined behaviour, never faults: out-of-range
+ *    slots, -1 entries, entries at or beyond a row's length and causally invalid top-k
+ *    entries contribute nothing; out-of-range positions leave a token untouched.
+ *  - Non-finite floating inputs give unspecified (but memory-safe) results.
+ *  - Calls on one stream are ordered; calls on different streams that touch the same
+ *    buffers must be ordered by the caller.
+ */
+#ifndef DSV4_H_
+#define DSV4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSV4_LATENT_DIM 576
+#define DSV4_NOPE_DIM 512
+#define DSV4_ROPE_DIM 64
+#define DSV4_SCALE_BLOCK 64
+#define DSV4_RECORD_BYTES 648
+#define DSV4_COMBINE_ALIGN 128 /* [p3 rocm.py: top-k rows padded to a multiple of 128] */
+
+typedef enum {
+  DSV4_OK = 0,
+  DSV4_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  DSV4_ERR_SHAPE = 2,       /* a size or stride is negative or inconsistent       */
+  DSV4_ERR_ALIGN = 3,       /* a pointer is not aligned as documented             */
+  DSV4_ERR_UNSUPPORTED = 4, /* a valid but unsupported configuration (H, P, ...)  */
+  DSV4_ERR_HIP = 6          /* the HIP runtime reported an error at launch        */
+} dsv4_status;
+
+/* Name of a status code ("DSV4_OK", ...). Never NULL. */
+const char* dsv4_status_str(int status);
+
+/* Reason for the last failing call on this thread ("" after a successful call).
+ * The pointer stays valid until the next dsv4_* call on the same thread. */
+const char* dsv4_last_error(void);
+
+/* Bytes of one cache page of `page_size` slots (page_size * 648), 0 if page_size <= 0. */
+size_t dsv4_cache_page_bytes(int page_size);
+
+/*
+ * dsv4_kv_insert — fused per-head q RMSNorm + GPT-J RoPE, and FP8/UE8M0 insert of the
+ * new latent rows into the cache [p2 Implementation breakdown item 4: fused q per-head
+ * RMSNorm, GPT-J RoPE and FP8 UE8M0 KV insert; Key source excerpts xpu_sparse.py
+ * _fused_qnorm_rope_kv_insert(q, kv, positions) writing at slot_mapping; p1 item 2].
+ *
+ *   q            bf16 [T][H][576], updated in place:
+ *                  y = x / sqrt(mean(x^2) + eps) * w   over all 576 dims of a head,
+ *                  then dims 512..575 rotated in GPT-J (interleaved) pairs
+ *                  (y[512+2i], y[513+2i]) -> (a*c_i - b*s_i, a*s_i + b*c_i),
+ *                  rounded once to bf16.
+ *   kv           bf16 [T][576] (read only): dims 512..575 rotated the same way and
+ *                  stored as bf16; dims 0..511 split into 8 blocks of 64, each block
+ *                  stored as E4M3 codes of k * 2^-e with scale byte e + 127, where e is
+ *                  the smallest integer with max|k| <= 448 * 2^e (clamped to [-127,127],
+ *                  e = -127 for an all-zero block); round to nearest even, sign kept.
+ *   positions    int64 [T]; cos_sin fp32 [max_pos][64] = cos[32] | sin[32] per
+ *                  position (caller supplies the table). A token whose position is
+ *                  outside [0, max_pos) is left untouched (q and cache).
+ *   slot_mapping int64 [T]; the cache row written for token t; a value outside
+ *                  [0, num_pages*page_size) (e.g. -1) skips the cache write only.
+ *                  Duplicate slots: one of the writers wins (unspecified which).
+ *   q_norm_weight bf16 [576], shared by all heads.
+ *   kv_cache     uint8, num_pages pages in the layout above (16-byte aligned).
+ * Supported: page_size == 64, H in 1..128, T >= 0 (T == 0 is a no-op).
+ * Alignment: q, kv, kv_cache 16-byte aligned.
+ */
+int dsv4_kv_insert(void* q, const void* kv, const int64_t* positions,
+                   const int64_t* slot_mapping, const float* cos_sin, int max_pos,
+                   const void* q_norm_weight, float eps, uint8_t* kv_cache, int num_pages,
+                   int page_size, int T, int H, void* stream);
+
+/*
+ * dsv4_combine_indices — merge each query token's indexer top-k with its sliding
+ * window into one index row, deduplicated, mapped to physical cache slots and padded
+ * with -1 [p3 Key source excerpts: rocm.py _combine_topk_swa_indices_kernel;
+ * p4 forward_mqa: per-request logical index -> physical slot through the block table;
+ * p2 Implementation breakdown item 6: per-row topk_lens].
+ *
+ * For request b with qlen = qsl[b+1]-qsl[b] query tokens, its i-th token
+ * t = qsl[b]-qsl[0]+i sits at position pos = seq_lens[b]-qlen+i and gets
+ *   tk = max(0, min(pos+1, top_k, topk_lens[t] if topk_lens)),  sw = max(0, min(pos+1, window)),
+ *   combined[t][j]    = phys(b, topk[t][j]) for j < tk, or -1 if that entry is < 0, > pos,
+ *                       inside the window [pos-sw+1, pos] (the window supplies it), or
+ *                       at a column >= topk_width;
+ *   combined[t][tk+r] = phys(b, pos-sw+1+r) for r < sw (window, ascending);
+ *   combined[t][j]    = -1 for tk+sw <= j < combined_stride;
+ *   combined_lens[t]  = tk + sw,
+ * where phys(b, x) = block_table[b][x/P]*P + x%P, or -1 if x/P >= block_table_stride or
+ * the table entry is negative.  Tokens t >= T are skipped; rows of tokens that belong to
+ * no request are not written.
+ *   topk            int32 [T][topk_stride], topk_width <= topk_stride valid columns
+ *   topk_lens       int32 [T] or NULL
+ *   query_start_loc int32 [B+1]; seq_lens int32 [B]
+ *   block_table     int32 [B][block_table_stride] (physical page ids)
+ *   combined        int32 [T][combined_stride], combined_lens int32 [T]
+ * Requires combined_stride >= round_up(top_k + window, 128) and top_k <= topk_width.
+ */
+int dsv4_combine_indices(const int32_t* topk, int topk_stride, int topk_width,
+                         const int32_t* topk_lens, const int32_t* query_start_loc,
+                         const int32_t* seq_lens, const int32_t* block_table,
+                         int block_table_stride, int B, int T, int top_k, int window,
+                         int page_size, int32_t* combined, int combined_stride,
+                         int32_t* combined_lens, void* stream);
+
+/*
+ * dsv4_sparse_mla_decode — sparse MQA-form MLA attention of every head over the
+ * listed cache slots [p2 Key source excerpts xpu_sparse_decode_fp8: dequantise the
+ * gathered FP8 slots, then bf16 sparse MLA with topk_lens; p4 forward_mqa: output
+ * (T, H, kv_lora_rank) from physical indices; p4 supports_sink].  For token t, head h:
+ *   J      = { j < min(lens[t], idx_stride) : 0 <= indices[t][j] < num_pages*page_size }
+ *            (a multiset: a repeated slot counts twice),
+ *   K_j    = dequantised 576-d record of slot indices[t][j],  V_j = K_j[0:512],
+ *   s_j    = softmax_scale * <q[t][h], K_j>,   z = sinks[h] (absent: -inf),
+ *   m      = max(z, max_j s_j),  den = e^(z-m) + sum_j e^(s_j-m),
+ *   out[t][h] = sum_j e^(s_j-m) V_j / den  (0 when den == 0),
+ *   lse[t][h] = m + ln(den)  (-inf when den == 0).
+ * The sink adds to the denominator only (logit units, not multiplied by softmax_scale).
+ *   q        bf16 [T][H][576];  out bf16 [T][H][512];  lse fp32 [T][H] or NULL
+ *   indices  int32 [T][idx_stride];  lens int32 [T];  sinks fp32 [H] or NULL
+ * Arithmetic: bf16 operands, fp32 accumulation, probabilities rounded to bf16 for the
+ * value product.  Supported: H in {16, 32, 64, 128}, page_size == 64.
+ * Alignment: q, out, kv_cache 16-byte aligned; indices 4-byte aligned.
+ */
+int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages,
+                           int page_size, const int32_t* indices, int idx_stride,
+                           const int32_t* lens, const float* sinks, float softmax_scale,
+                           void* out, float* lse, int T, int H, void* stream);
+
+/*
+ * dsv4_sparse_mla_prefill — the same result as dsv4_sparse_mla_decode, scheduled for
+ * many query tokens per call (prefill: each token of a long sequence attends its own
+ * combined index row) [p3 Motivation/Implementation breakdown: sparse prefill index
+ * combining; p4 decoder self-attention].  Same arguments, contract and limits.
+ */
+int dsv4_sparse_mla_prefill(const void* q, const uint8_t* kv_cache, int num_pages,
+                            int page_size, const int32_t* indices, int idx_stride,
+                            const int32_t* lens, const float* sinks, float softmax_scale,
+                            void* out, float* lse, int T, int H, void* stream);
+
+/*
+ * dsv4_gather_dequant — gather + dequantise slots into bf16 rows [p2 Key source
+ * excerpts: _dequant_gather_slots_kernel, one program per slot; a negative slot gives
+ * a zero row; FP8 -> fp32 times 2^(byte-127) -> bf16; the bf16 RoPE part is copied].
+ * Slots >= num_pages*page_size also give zero rows.  The attention entry points fuse
+ * this step; it is exported as a separately testable step.
+ *   slots int32 [n];  out bf16 [n][576]
+ */
+int dsv4_gather_dequant(const uint8_t* kv_cache, int num_pages, int page_size,
+                        const int32_t* slots, int n, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSV4_H_ */
