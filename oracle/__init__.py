@@ -125,10 +125,15 @@ def combine(topk, topk_lens, qsl, seq_lens, block_table, T, top_k, window, page_
 
 
 def kv_insert(q_bits, kv_bits, positions, slot_mapping, cos_sin, weight_bits, eps, cache,
-              num_pages, page_size):
-    """In-place on copies: returns (q_out_bits, cache_out)."""
-    q = np.array(q_bits, dtype=np.uint16, order="C", copy=True)
-    c = np.array(cache, dtype=np.uint8, order="C", copy=True)
+              num_pages, page_size, inplace=False):
+    """Returns (q_out_bits, cache_out); works on copies unless ``inplace`` (then q_bits and
+    cache must be C-contiguous uint16 / uint8 arrays and are updated)."""
+    if inplace:
+        q, c = q_bits, cache
+        assert q.dtype == np.uint16 and c.dtype == np.uint8
+    else:
+        q = np.array(q_bits, dtype=np.uint16, order="C", copy=True)
+        c = np.array(cache, dtype=np.uint8, order="C", copy=True)
     kv = _c(kv_bits, np.uint16)
     pos = _c(positions, np.int64)
     sm = _c(slot_mapping, np.int64)

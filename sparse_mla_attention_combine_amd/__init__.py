@@ -1,0 +1,165 @@
+"""Python binding of libdsv4.so, the MI355X (gfx950) sparse MLA hot path.
+
+Thin ctypes marshalling over the C ABI declared in ``include/dsv4.h``: each function
+has the C entry point's name, takes torch tensors that already live on the GPU, passes
+their device pointers and the current HIP stream, and raises on a non-zero status.
+Every step of the path runs in the library's HIP kernels; there is no fallback.  If
+the library has not been built the import fails (run
+``python -m sparse_mla_attention_combine_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libdsv4.so")
+
+LATENT_DIM, NOPE_DIM, ROPE_DIM, RECORD_BYTES, COMBINE_ALIGN = 576, 512, 64, 648, 128
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m sparse_mla_attention_combine_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i32, _f32, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
+
+_lib.dsv4_status_str.argtypes, _lib.dsv4_status_str.restype = [_i32], ctypes.c_char_p
+_lib.dsv4_last_error.argtypes, _lib.dsv4_last_error.restype = [], ctypes.c_char_p
+_lib.dsv4_cache_page_bytes.argtypes, _lib.dsv4_cache_page_bytes.restype = [_i32], ctypes.c_size_t
+_lib.dsv4_kv_insert.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _vp, _i32, _i32, _i32,
+                                _i32, _vp]
+_lib.dsv4_combine_indices.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _vp, _i32, _vp, _vp]
+_attn_args = [_vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _vp]
+_lib.dsv4_sparse_mla_decode.argtypes = _attn_args
+_lib.dsv4_sparse_mla_prefill.argtypes = _attn_args
+_lib.dsv4_gather_dequant.argtypes = [_vp, _i32, _i32, _vp, _i32, _vp, _vp]
+for _f in (_lib.dsv4_kv_insert, _lib.dsv4_combine_indices, _lib.dsv4_sparse_mla_decode,
+           _lib.dsv4_sparse_mla_prefill, _lib.dsv4_gather_dequant):
+    _f.restype = _i32
+
+EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4_kv_insert",
+            "dsv4_combine_indices", "dsv4_sparse_mla_decode", "dsv4_sparse_mla_prefill",
+            "dsv4_gather_dequant"]
+
+
+class Dsv4Error(RuntimeError):
+    def __init__(self, status: int, reason: str):
+        super().__init__(f"{_lib.dsv4_status_str(status).decode()}: {reason}")
+        self.status = status
+        self.reason = reason
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise Dsv4Error(status, _lib.dsv4_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TypeError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise TypeError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _want(t, dtype, name):
+    if t is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def cache_page_bytes(page_size: int = 64) -> int:
+    return int(_lib.dsv4_cache_page_bytes(page_size))
+
+
+def new_cache(num_pages: int, page_size: int = 64, device="cuda") -> torch.Tensor:
+    """Zero-filled uint8 cache of ``num_pages`` pages (caller-owned device memory)."""
+    return torch.zeros(num_pages * cache_page_bytes(page_size), dtype=torch.uint8, device=device)
+
+
+def dsv4_kv_insert(q, kv, positions, slot_mapping, cos_sin, q_norm_weight, eps, kv_cache,
+                   page_size=64, stream=None):
+    """q bf16 [T, H, 576] (in place), kv bf16 [T, 576], positions/slot_mapping int64 [T],
+    cos_sin fp32 [max_pos, 64], q_norm_weight bf16 [576], kv_cache uint8 pages."""
+    _want(q, torch.bfloat16, "q"), _want(kv, torch.bfloat16, "kv")
+    _want(positions, torch.int64, "positions"), _want(slot_mapping, torch.int64, "slot_mapping")
+    _want(cos_sin, torch.float32, "cos_sin"), _want(q_norm_weight, torch.bfloat16, "q_norm_weight")
+    _want(kv_cache, torch.uint8, "kv_cache")
+    T, H = (q.shape[0], q.shape[1]) if q is not None else (kv.shape[0], 0)
+    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    _check(_lib.dsv4_kv_insert(_ptr(q) if H else None, _ptr(kv), _ptr(positions),
+                               _ptr(slot_mapping), _ptr(cos_sin), cos_sin.shape[0],
+                               _ptr(q_norm_weight) if H else None, float(eps), _ptr(kv_cache),
+                               num_pages, page_size, T, H, _stream(stream)))
+    return q
+
+
+def dsv4_combine_indices(topk, topk_lens, query_start_loc, seq_lens, block_table, top_k, window,
+                         combined, combined_lens, page_size=64, topk_width=None, stream=None):
+    """topk int32 [T, width], topk_lens int32 [T] or None, query_start_loc int32 [B+1],
+    seq_lens int32 [B], block_table int32 [B, pages]; writes combined int32
+    [T, stride] and combined_lens int32 [T]."""
+    for t, n in ((topk, "topk"), (topk_lens, "topk_lens"), (query_start_loc, "query_start_loc"),
+                 (seq_lens, "seq_lens"), (block_table, "block_table"), (combined, "combined"),
+                 (combined_lens, "combined_lens")):
+        _want(t, torch.int32, n)
+    T = combined.shape[0]
+    B = seq_lens.shape[0]
+    width = topk.shape[1] if topk_width is None else topk_width
+    _check(_lib.dsv4_combine_indices(_ptr(topk), topk.shape[1], width, _ptr(topk_lens),
+                                     _ptr(query_start_loc), _ptr(seq_lens), _ptr(block_table),
+                                     block_table.shape[1], B, T, top_k, window, page_size,
+                                     _ptr(combined), combined.shape[1], _ptr(combined_lens),
+                                     _stream(stream)))
+
+
+def _attention(fn, q, kv_cache, indices, lens, sinks, softmax_scale, out, lse, page_size, stream):
+    _want(q, torch.bfloat16, "q"), _want(kv_cache, torch.uint8, "kv_cache")
+    _want(indices, torch.int32, "indices"), _want(lens, torch.int32, "lens")
+    _want(sinks, torch.float32, "sinks"), _want(out, torch.bfloat16, "out")
+    _want(lse, torch.float32, "lse")
+    T, H = q.shape[0], q.shape[1]
+    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    _check(fn(_ptr(q), _ptr(kv_cache), num_pages, page_size, _ptr(indices), indices.shape[1],
+              _ptr(lens), _ptr(sinks), float(softmax_scale), _ptr(out), _ptr(lse), T, H,
+              _stream(stream)))
+    return out
+
+
+def dsv4_sparse_mla_decode(q, kv_cache, indices, lens, sinks, softmax_scale, out, lse=None,
+                           page_size=64, stream=None):
+    """q bf16 [T, H, 576], indices int32 [T, stride] physical slots, lens int32 [T],
+    sinks fp32 [H] or None -> out bf16 [T, H, 512] (and lse fp32 [T, H] if given)."""
+    return _attention(_lib.dsv4_sparse_mla_decode, q, kv_cache, indices, lens, sinks,
+                      softmax_scale, out, lse, page_size, stream)
+
+
+def dsv4_sparse_mla_prefill(q, kv_cache, indices, lens, sinks, softmax_scale, out, lse=None,
+                            page_size=64, stream=None):
+    """Same contract as dsv4_sparse_mla_decode, scheduled for many query tokens."""
+    return _attention(_lib.dsv4_sparse_mla_prefill, q, kv_cache, indices, lens, sinks,
+                      softmax_scale, out, lse, page_size, stream)
+
+
+def dsv4_gather_dequant(kv_cache, slots, out, page_size=64, stream=None):
+    """slots int32 [n] -> out bf16 [n, 576] (dequantised rows; zeros for invalid slots)."""
+    _want(kv_cache, torch.uint8, "kv_cache"), _want(slots, torch.int32, "slots")
+    _want(out, torch.bfloat16, "out")
+    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    _check(_lib.dsv4_gather_dequant(_ptr(kv_cache), num_pages, page_size, _ptr(slots),
+                                    slots.shape[0], _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,189 @@
+// C ABI of the library (declared in include/dsv4.h).  Every entry point checks its
+// arguments on the host before launching anything; a failure returns a status and a
+// thread-local reason string and touches no memory.  The error style follows the
+// capability checks of PR #43477 (Key source excerpts, flashinfer_sparse.py
+// supports_combination returning a reason string; NotImplementedError for an
+// unsupported cache layout).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/dsv4.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return DSV4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSV4_ERR_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_page(const char* fn, int page_size, int num_pages) {
+  if (page_size != 64)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: page_size %d not supported (only 64)", fn, page_size);
+  if (num_pages < 0) return fail(DSV4_ERR_SHAPE, "%s: num_pages %d < 0", fn, num_pages);
+  if ((int64_t)num_pages * page_size >= ((int64_t)1 << 31))
+    return fail(DSV4_ERR_SHAPE, "%s: num_pages * page_size exceeds the int32 slot range", fn);
+  return DSV4_OK;
+}
+
+int check_attention(const char* fn, const void* q, const uint8_t* kv_cache, int num_pages,
+                    int page_size, const int32_t* indices, int idx_stride, const int32_t* lens,
+                    const float* /*sinks*/, float softmax_scale, const void* out, int T, int H) {
+  if (T < 0) return fail(DSV4_ERR_SHAPE, "%s: T = %d < 0", fn, T);
+  if (H != 16 && H != 32 && H != 64 && H != 128)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: H = %d not in {16, 32, 64, 128}", fn, H);
+  int st = check_page(fn, page_size, num_pages);
+  if (st) return st;
+  if (idx_stride < 0) return fail(DSV4_ERR_SHAPE, "%s: idx_stride %d < 0", fn, idx_stride);
+  if (!(softmax_scale == softmax_scale)) return fail(DSV4_ERR_SHAPE, "%s: softmax_scale is NaN", fn);
+  if (T == 0) return DSV4_OK;
+  if (!q || !out || !lens || (!indices && idx_stride > 0) || (!kv_cache && num_pages > 0))
+    return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(q, 16) || !aligned(out, 16) || (kv_cache && !aligned(kv_cache, 16)))
+    return fail(DSV4_ERR_ALIGN, "%s: q, out and kv_cache must be 16-byte aligned", fn);
+  if (!aligned(lens, 4) || (indices && !aligned(indices, 4)))
+    return fail(DSV4_ERR_ALIGN, "%s: indices and lens must be 4-byte aligned", fn);
+  return DSV4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsv4_status_str(int status) {
+  switch (status) {
+    case DSV4_OK: return "DSV4_OK";
+    case DSV4_ERR_NULL: return "DSV4_ERR_NULL";
+    case DSV4_ERR_SHAPE: return "DSV4_ERR_SHAPE";
+    case DSV4_ERR_ALIGN: return "DSV4_ERR_ALIGN";
+    case DSV4_ERR_UNSUPPORTED: return "DSV4_ERR_UNSUPPORTED";
+    case DSV4_ERR_HIP: return "DSV4_ERR_HIP";
+    default: return "DSV4_UNKNOWN_STATUS";
+  }
+}
+
+const char* dsv4_last_error(void) { return g_err; }
+
+size_t dsv4_cache_page_bytes(int page_size) {
+  return page_size > 0 ? (size_t)page_size * DSV4_RECORD_BYTES : 0;
+}
+
+int dsv4_kv_insert(void* q, const void* kv, const int64_t* positions, const int64_t* slot_mapping,
+                   const float* cos_sin, int max_pos, const void* q_norm_weight, float eps,
+                   uint8_t* kv_cache, int num_pages, int page_size, int T, int H, void* stream) {
+  const char* fn = "dsv4_kv_insert";
+  if (T < 0 || H < 0 || H > 128) return fail(DSV4_ERR_SHAPE, "%s: T = %d, H = %d out of range (T >= 0, 0 <= H <= 128)", fn, T, H);
+  int st = check_page(fn, page_size, num_pages);
+  if (st) return st;
+  if (max_pos < 0) return fail(DSV4_ERR_SHAPE, "%s: max_pos %d < 0", fn, max_pos);
+  if (!(eps >= 0.f)) return fail(DSV4_ERR_SHAPE, "%s: eps must be >= 0", fn);
+  if (T == 0) return ok();
+  if (!kv || !positions || !slot_mapping || !cos_sin || (!kv_cache && num_pages > 0) ||
+      (H > 0 && (!q || !q_norm_weight)))
+    return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if ((H > 0 && (!aligned(q, 16) || !aligned(q_norm_weight, 16))) || !aligned(kv, 16) ||
+      (kv_cache && !aligned(kv_cache, 16)) || !aligned(cos_sin, 16) || !aligned(positions, 8) ||
+      !aligned(slot_mapping, 8))
+    return fail(DSV4_ERR_ALIGN, "%s: q, kv, q_norm_weight, cos_sin, kv_cache must be 16-byte aligned; positions, slot_mapping 8-byte", fn);
+  return hip_status(dsv4::launch_insert(q, kv, positions, slot_mapping, cos_sin, max_pos,
+                                        q_norm_weight, eps, kv_cache, num_pages, T, H,
+                                        static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int dsv4_combine_indices(const int32_t* topk, int topk_stride, int topk_width,
+                         const int32_t* topk_lens, const int32_t* query_start_loc,
+                         const int32_t* seq_lens, const int32_t* block_table,
+                         int block_table_stride, int B, int T, int top_k, int window,
+                         int page_size, int32_t* combined, int combined_stride,
+                         int32_t* combined_lens, void* stream) {
+  const char* fn = "dsv4_combine_indices";
+  if (B < 0 || T < 0 || top_k < 0 || window < 0 || topk_width < 0 || topk_stride < topk_width ||
+      block_table_stride < 0)
+    return fail(DSV4_ERR_SHAPE, "%s: negative size or topk_stride < topk_width", fn);
+  if (page_size != 64) return fail(DSV4_ERR_UNSUPPORTED, "%s: page_size %d not supported (only 64)", fn, page_size);
+  if (top_k > topk_width) return fail(DSV4_ERR_SHAPE, "%s: top_k %d > topk_width %d", fn, top_k, topk_width);
+  const int64_t need = ((int64_t)top_k + window + DSV4_COMBINE_ALIGN - 1) / DSV4_COMBINE_ALIGN * DSV4_COMBINE_ALIGN;
+  if (combined_stride < need)
+    return fail(DSV4_ERR_SHAPE, "%s: combined_stride %d < round_up(top_k + window, 128) = %lld", fn,
+                combined_stride, (long long)need);
+  if (B == 0 || T == 0) return ok();
+  if (!query_start_loc || !seq_lens || !combined || !combined_lens || (!topk && topk_width > 0) ||
+      (!block_table && block_table_stride > 0))
+    return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(combined, 4) || !aligned(combined_lens, 4) || (topk && !aligned(topk, 4)))
+    return fail(DSV4_ERR_ALIGN, "%s: int32 arrays must be 4-byte aligned", fn);
+  return hip_status(dsv4::launch_combine(topk, topk_stride, topk_width, topk_lens, query_start_loc,
+                                         seq_lens, block_table, block_table_stride, B, T, top_k,
+                                         window, combined, combined_stride, combined_lens,
+                                         static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
+                           const int32_t* indices, int idx_stride, const int32_t* lens,
+                           const float* sinks, float softmax_scale, void* out, float* lse, int T,
+                           int H, void* stream) {
+  const char* fn = "dsv4_sparse_mla_decode";
+  int st = check_attention(fn, q, kv_cache, num_pages, page_size, indices, idx_stride, lens, sinks,
+                           softmax_scale, out, T, H);
+  if (st) return st;
+  if (T == 0) return ok();
+  return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, indices, idx_stride, lens, sinks,
+                                           softmax_scale, out, lse, T, H, false,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int dsv4_sparse_mla_prefill(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
+                            const int32_t* indices, int idx_stride, const int32_t* lens,
+                            const float* sinks, float softmax_scale, void* out, float* lse, int T,
+                            int H, void* stream) {
+  const char* fn = "dsv4_sparse_mla_prefill";
+  int st = check_attention(fn, q, kv_cache, num_pages, page_size, indices, idx_stride, lens, sinks,
+                           softmax_scale, out, T, H);
+  if (st) return st;
+  if (T == 0) return ok();
+  return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, indices, idx_stride, lens, sinks,
+                                           softmax_scale, out, lse, T, H, true,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int dsv4_gather_dequant(const uint8_t* kv_cache, int num_pages, int page_size, const int32_t* slots,
+                        int n, void* out, void* stream) {
+  const char* fn = "dsv4_gather_dequant";
+  if (n < 0) return fail(DSV4_ERR_SHAPE, "%s: n = %d < 0", fn, n);
+  int st = check_page(fn, page_size, num_pages);
+  if (st) return st;
+  if (n == 0) return ok();
+  if (!slots || !out || (!kv_cache && num_pages > 0))
+    return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(out, 16) || (kv_cache && !aligned(kv_cache, 16)) || !aligned(slots, 4))
+    return fail(DSV4_ERR_ALIGN, "%s: out and kv_cache must be 16-byte aligned, slots 4-byte", fn);
+  return hip_status(dsv4::launch_gather(kv_cache, num_pages, slots, n, out,
+                                        static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

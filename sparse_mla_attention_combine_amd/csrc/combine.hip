@@ -1,0 +1,75 @@
+// Index combining: top-k + sliding window -> one deduplicated, physical, -1-padded row
+// per query token.  Follows the ROCm combine step of PR #43385 (Key source excerpts,
+// rocm.py combine kernel: per-token top-k part, then the window part, then the length),
+// with the logical -> physical mapping of PR #43477 (forward_mqa excerpt) fused in and
+// the per-row topk_lens of PR #42953 (Implementation breakdown item 6).
+//
+// Schedule: workgroup (b, y) owns tokens y, y+Y, ... of request b; its 256 threads
+// sweep one row at a time, so every load of the top-k row and every store of the
+// combined row is a coalesced 1 KiB wave access.  Integer only: bit-exact by design.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace dsv4 {
+
+__device__ __forceinline__ int32_t phys_slot(const int32_t* __restrict__ bt_row, int bt_stride,
+                                             int64_t x) {
+  int64_t lp = x >> 6;  // logical page (page size 64)
+  if (x < 0 || lp >= bt_stride) return -1;
+  int32_t page = bt_row[lp];
+  return page < 0 ? -1 : (int32_t)((int64_t)page * kPage + (x & (kPage - 1)));
+}
+
+__global__ void __launch_bounds__(256) combine_kernel(
+    const int32_t* __restrict__ topk, int topk_stride, int topk_width,
+    const int32_t* __restrict__ topk_lens, const int32_t* __restrict__ qsl,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table, int bt_stride,
+    int T, int top_k, int window, int32_t* __restrict__ combined, int combined_stride,
+    int32_t* __restrict__ combined_lens) {
+  const int b = blockIdx.x;
+  const int base = qsl[0];
+  const int q0 = qsl[b] - base;
+  const int qlen = qsl[b + 1] - qsl[b];
+  const int seq_len = seq_lens[b];
+  const int32_t* bt_row = block_table + (int64_t)b * bt_stride;
+  for (int i = blockIdx.y; i < qlen; i += gridDim.y) {
+    const int64_t t = (int64_t)q0 + i;
+    if (t < 0 || t >= T) continue;
+    const int64_t pos = (int64_t)seq_len - qlen + i;
+    int64_t tk = min(pos + 1, (int64_t)top_k);
+    if (topk_lens) tk = min(tk, (int64_t)topk_lens[t]);
+    tk = max(tk, (int64_t)0);
+    const int64_t sw = max(min(pos + 1, (int64_t)window), (int64_t)0);
+    const int64_t lo = pos - sw + 1;
+    const int32_t* trow = topk + t * topk_stride;
+    int32_t* crow = combined + t * combined_stride;
+    for (int j = threadIdx.x; j < combined_stride; j += blockDim.x) {
+      int32_t v = -1;
+      if (j < tk) {
+        const int64_t x = j < topk_width ? (int64_t)trow[j] : -1;
+        if (x >= 0 && x < lo) v = phys_slot(bt_row, bt_stride, x);  // x >= lo: window has it
+      } else if (j < tk + sw) {
+        v = phys_slot(bt_row, bt_stride, lo + (j - tk));
+      }
+      crow[j] = v;
+    }
+    if (threadIdx.x == 0) combined_lens[t] = (int32_t)(tk + sw);
+  }
+}
+
+hipError_t launch_combine(const int32_t* topk, int topk_stride, int topk_width,
+                          const int32_t* topk_lens, const int32_t* qsl, const int32_t* seq_lens,
+                          const int32_t* block_table, int bt_stride, int B, int T, int top_k,
+                          int window, int32_t* combined, int combined_stride,
+                          int32_t* combined_lens, hipStream_t stream) {
+  if (B == 0 || T == 0) return hipSuccess;
+  // tokens per request are device data; size the second grid axis from the average
+  int per_req = (T + B - 1) / B;
+  int Y = per_req < 1 ? 1 : (per_req > 2048 ? 2048 : per_req);
+  hipLaunchKernelGGL(combine_kernel, dim3(B, Y), dim3(256), 0, stream, topk, topk_stride,
+                     topk_width, topk_lens, qsl, seq_lens, block_table, bt_stride, T, top_k,
+                     window, combined, combined_stride, combined_lens);
+  return hipGetLastError();
+}
+
+}  // namespace dsv4

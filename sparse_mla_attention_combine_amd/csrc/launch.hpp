@@ -1,0 +1,28 @@
+// Host-side launchers of the gfx950 kernels.  Arguments are validated by the C ABI
+// layer before any of these is called; each returns the HIP launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsv4 {
+
+hipError_t launch_combine(const int32_t* topk, int topk_stride, int topk_width,
+                          const int32_t* topk_lens, const int32_t* qsl, const int32_t* seq_lens,
+                          const int32_t* block_table, int bt_stride, int B, int T, int top_k,
+                          int window, int32_t* combined, int combined_stride,
+                          int32_t* combined_lens, hipStream_t stream);
+
+hipError_t launch_insert(void* q, const void* kv, const int64_t* positions,
+                         const int64_t* slot_mapping, const float* cos_sin, int max_pos,
+                         const void* weight, float eps, uint8_t* cache, int num_pages, int T,
+                         int H, hipStream_t stream);
+
+hipError_t launch_gather(const uint8_t* cache, int num_pages, const int32_t* slots, int n,
+                         void* out, hipStream_t stream);
+
+hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages,
+                            const int32_t* indices, int idx_stride, const int32_t* lens,
+                            const float* sinks, float softmax_scale, void* out, float* lse,
+                            int T, int H, bool prefill, hipStream_t stream);
+
+}  // namespace dsv4

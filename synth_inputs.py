@@ -93,14 +93,15 @@ def _block_table(rng, seq_lens, P=PAGE):
 
 
 def attention_workload(cfg: int, seed: int | None = None, instances: int = 1,
-                       context_kv: str = "referenced"):
+                       context_kv: str = "referenced", ctx_tokens=None):
     """Inputs of the combine + attention steps for configs 0, 2, 3, 4.
 
     Returns a dict.  ``instances`` > 1 draws independent (q, topk, topk_lens, sinks)
     sets over the same cache geometry (used to rotate the benchmark's working set).
     ``ctx_*`` describe the context tokens whose latent rows must be inserted into the
     cache before attention: every position a top-k row or a window may touch
-    ("referenced"), or every context position ("all")."""
+    ("referenced"), or every context position ("all").  ``ctx_tokens`` restricts the
+    referenced set to the rows of those query tokens (sampled parity checks)."""
     seed = cfg if seed is None else seed
     r = _streams(seed)
     if cfg == 0:
@@ -163,13 +164,17 @@ def attention_workload(cfg: int, seed: int | None = None, instances: int = 1,
         if context_kv == "all" or cfg in (0, 4):
             xs = np.arange(L, dtype=np.int64)
         else:
-            parts = []
+            parts = [np.zeros(0, np.int64)]
             t0, t1 = int(qsl[b]), int(qsl[b + 1])
-            for it in inst:
-                rows = it["topk"][t0:t1].ravel()
-                parts.append(rows[(rows >= 0) & (rows < L)].astype(np.int64))
-            lo = max(0, L - int(qlens[b]) - window + 1)
-            parts.append(np.arange(lo, L, dtype=np.int64))
+            toks = np.arange(t0, t1)
+            if ctx_tokens is not None:
+                toks = np.intersect1d(toks, np.asarray(ctx_tokens))
+            for t in toks:
+                pos = L - int(qlens[b]) + (int(t) - t0)
+                for it in inst:
+                    row = it["topk"][t]
+                    parts.append(row[(row >= 0) & (row <= pos)].astype(np.int64))
+                parts.append(np.arange(max(0, pos - window + 1), pos + 1, dtype=np.int64))
             xs = np.unique(np.concatenate(parts))
         ctx_b.append(np.full(xs.size, b, np.int64))
         ctx_x.append(xs)

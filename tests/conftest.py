@@ -18,3 +18,14 @@ def orc():
     oracle.build()
     oracle.lib()
     return oracle
+
+
+@pytest.fixture(scope="session")
+def dsv4():
+    """The HIP library's binding (built in-tree first if it is missing)."""
+    lib = os.path.join(ROOT, "sparse_mla_attention_combine_amd", "_lib", "libdsv4.so")
+    if not os.path.exists(lib):
+        from sparse_mla_attention_combine_amd import build as _b
+        _b.build()
+    import sparse_mla_attention_combine_amd as m
+    return m

@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every symbol include/dsv4.h declares, and rejects
+bad arguments on the host (these calls return before any HIP call, so they run
+without a GPU)."""
+import ctypes
+import os
+import re
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dsv4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsv4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(dsv4):
+    lib = dsv4.library()
+    names = declared_functions()
+    assert {"dsv4_kv_insert", "dsv4_combine_indices", "dsv4_sparse_mla_decode",
+            "dsv4_sparse_mla_prefill", "dsv4_gather_dequant"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(dsv4.EXPORTED)
+
+
+def test_status_strings_and_page_bytes(dsv4):
+    lib = dsv4.library()
+    assert lib.dsv4_status_str(0) == b"DSV4_OK"
+    assert lib.dsv4_status_str(4) == b"DSV4_ERR_UNSUPPORTED"
+    assert lib.dsv4_cache_page_bytes(64) == 64 * 648
+    assert lib.dsv4_cache_page_bytes(0) == 0
+
+
+def _fake(n=1 << 20):
+    """A host buffer only used as a non-NULL, aligned address (never dereferenced:
+    every call below fails validation before any launch)."""
+    buf = (ctypes.c_uint8 * (n + 64))()
+    addr = ctypes.addressof(buf)
+    return buf, ctypes.c_void_p((addr + 63) // 64 * 64)
+
+
+def test_attention_validation(dsv4):
+    lib = dsv4.library()
+    keep, p = _fake()
+    args = dict(q=p, cache=p, num_pages=4, page_size=64, idx=p, stride=128, lens=p, sinks=None,
+                scale=0.04, out=p, lse=None, T=2, H=16)
+
+    def call(fn, **kw):
+        a = dict(args, **kw)
+        return fn(a["q"], a["cache"], a["num_pages"], a["page_size"], a["idx"], a["stride"],
+                  a["lens"], a["sinks"], a["scale"], a["out"], a["lse"], a["T"], a["H"], None)
+
+    for fn in (lib.dsv4_sparse_mla_decode, lib.dsv4_sparse_mla_prefill):
+        assert call(fn, H=24) == 4 and b"H = 24" in lib.dsv4_last_error()
+        assert call(fn, page_size=32) == 4
+        assert call(fn, q=None) == 1
+        assert call(fn, lens=None) == 1
+        assert call(fn, T=-1) == 2
+        assert call(fn, num_pages=-3) == 2
+        assert call(fn, out=ctypes.c_void_p(p.value + 2)) == 3
+        assert call(fn, T=0, q=None) == 0 and lib.dsv4_last_error() == b""
+
+
+def test_combine_validation(dsv4):
+    lib = dsv4.library()
+    keep, p = _fake()
+
+    def call(**kw):
+        a = dict(topk=p, ts=2048, tw=2048, tl=None, qsl=p, sl=p, bt=p, bts=512, B=64, T=64,
+                 top_k=2048, window=128, P=64, comb=p, cs=2176, cl=p)
+        a.update(kw)
+        return lib.dsv4_combine_indices(a["topk"], a["ts"], a["tw"], a["tl"], a["qsl"], a["sl"],
+                                        a["bt"], a["bts"], a["B"], a["T"], a["top_k"], a["window"],
+                                        a["P"], a["comb"], a["cs"], a["cl"], None)
+
+    assert call(cs=2100) == 2 and b"2176" in lib.dsv4_last_error()
+    assert call(top_k=4096) == 2
+    assert call(P=128) == 4
+    assert call(qsl=None) == 1
+    assert call(ts=100, tw=2048) == 2
+    assert call(T=0) == 0
+
+
+def test_insert_and_gather_validation(dsv4):
+    lib = dsv4.library()
+    keep, p = _fake()
+
+    def ins(**kw):
+        a = dict(q=p, kv=p, pos=p, sm=p, cs=p, maxp=100, w=p, eps=1e-6, cache=p, npg=4, P=64, T=4, H=8)
+        a.update(kw)
+        return lib.dsv4_kv_insert(a["q"], a["kv"], a["pos"], a["sm"], a["cs"], a["maxp"], a["w"],
+                                  a["eps"], a["cache"], a["npg"], a["P"], a["T"], a["H"], None)
+
+    assert ins(H=129) == 2
+    assert ins(P=16) == 4
+    assert ins(kv=None) == 1
+    assert ins(q=None) == 1
+    assert ins(q=None, w=None, H=0, kv=None) == 1
+    assert ins(eps=-1.0) == 2
+    assert ins(q=ctypes.c_void_p(p.value + 8)) == 3
+    assert ins(T=0) == 0
+    assert lib.dsv4_gather_dequant(p, 4, 64, None, 5, p, None) == 1
+    assert lib.dsv4_gather_dequant(p, 4, 64, p, -1, p, None) == 2
+    assert lib.dsv4_gather_dequant(p, 4, 48, p, 5, p, None) == 4
+    assert lib.dsv4_gather_dequant(p, 4, 64, p, 0, p, None) == 0
+
+
+def test_binding_rejects_host_tensors(dsv4):
+    import pytest
+    import torch
+    q = torch.zeros(1, 16, 576, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        dsv4.dsv4_sparse_mla_decode(q, torch.zeros(64 * 648, dtype=torch.uint8),
+                                    torch.zeros(1, 128, dtype=torch.int32),
+                                    torch.zeros(1, dtype=torch.int32), None, 0.04,
+                                    torch.zeros(1, 16, 512, dtype=torch.bfloat16))
