@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MLA decode hot path on one MI355X.
+
+A step is one pass of the whole path over one decode batch (B = 64 requests, one query
+token each, H = 128 heads, context 32768, top-k 2048 with lengths ~ U{1024..2048}, a
+128-token sliding window, per-head sinks):
+    dsv4_kv_insert        q RMSNorm + RoPE in place, new latent rows -> FP8 cache
+    dsv4_combine_indices  top-k + window -> one physical index row per token (width 2176)
+    dsv4_sparse_mla_decode
+Steps rotate over independent (q, top-k, lengths, sinks) instances so the gathered
+cache records (~69 MB per step, ~550 MB over 8 instances) cannot stay in the 256 MB
+Infinity Cache.  Inputs are resident in HBM before timing starts.
+
+Output: one JSON line (metric, value = query tokens/s, roofline of the dominant kernel
+from HIP events around each of its launches in the timed region, and the CPU oracle
+timed on the host as a reported baseline).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--instances I] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "sparse MLA decode query-tokens/s + % of HBM/MFMA roofline (B=64,H=128,k=2048)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (spec)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (spec)
+LATENT, NOPE, RECORD = 576, 512, 648
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    readings (each scaled by the reading of a 256 MiB copy), or None when the kernel's
+    sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(HERE, "profiles", "sparse_mla_decode_b64_h128_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        h = hashlib.sha256()
+        for src in d["kernel_sources"]:
+            with open(os.path.join(HERE, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != d["kernel_source_sha256"]:
+            return None
+        return (d["fetch_size_kib_per_dispatch"] * 1024 * d["fetch_factor"] +
+                d["write_size_kib_per_dispatch"] * 1024 * d["write_factor"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--instances", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 256 MiB device-to-device copy 3 times (the known-size "
+                         "kernel that scales FETCH_SIZE / WRITE_SIZE counter readings)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); multi-GPU runs are not part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 256 MiB x 3")
+        return
+    import sparse_mla_attention_combine_amd as dsv4
+    from synth_inputs import attention_workload, bf16_normal
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    wl = attention_workload(2, seed=args.seed, instances=args.instances)
+    T, H, W = wl["T"], wl["H"], wl["W"]
+    npg = wl["num_pages"]
+    log(f"[bench] workload generated in {time.time() - t0:.1f}s: T={T} H={H} W={W} "
+        f"pages={npg} context rows={wl['ctx_kv'].shape[0]}")
+
+    def to_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def to_dev(a, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).to(dev)
+
+    # cache filled by the library's own insert (cache-only: no q heads)
+    cache = dsv4.new_cache(npg)
+    cos_sin = to_dev(wl["cos_sin"], np.float32)
+    weight = to_bf16(wl["q_norm_weight"])
+    dsv4.dsv4_kv_insert(None, to_bf16(wl["ctx_kv"]), to_dev(wl["ctx_pos"], np.int64),
+                        to_dev(wl["ctx_slot"], np.int64), cos_sin, None, wl["eps"], cache)
+    qsl = to_dev(wl["qsl"], np.int32)
+    seq_lens = to_dev(wl["seq_lens"], np.int32)
+    bt = to_dev(wl["block_table"], np.int32)
+    pos_np = (wl["seq_lens"].astype(np.int64) - 1)
+    slot_np = wl["block_table"][np.arange(T), pos_np // 64].astype(np.int64) * 64 + pos_np % 64
+    positions = to_dev(pos_np, np.int64)
+    slot_mapping = to_dev(slot_np, np.int64)
+    rng = np.random.default_rng(1000 + args.seed)
+
+    inst = []
+    for it in wl["instances"]:
+        d = dict(q=to_bf16(it["q"]), kv=to_bf16(bf16_normal(rng, (T, LATENT))),
+                 topk=to_dev(it["topk"], np.int32), topk_lens=to_dev(it["topk_lens"], np.int32),
+                 sinks=to_dev(it["sinks"], np.float32),
+                 comb=torch.empty(T, W, dtype=torch.int32, device=dev),
+                 lens=torch.empty(T, dtype=torch.int32, device=dev),
+                 out=torch.empty(T, H, NOPE, dtype=torch.bfloat16, device=dev))
+        inst.append(d)
+    torch.cuda.synchronize()
+
+    lib = dsv4.library()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.c_void_p
+
+    # pre-marshalled C-ABI argument tuples (pointers never change between steps)
+    calls = []
+    for d in inst:
+        ins = (P(d["q"].data_ptr()), P(d["kv"].data_ptr()), P(positions.data_ptr()),
+               P(slot_mapping.data_ptr()), P(cos_sin.data_ptr()), cos_sin.shape[0],
+               P(weight.data_ptr()), ctypes.c_float(wl["eps"]), P(cache.data_ptr()), npg, 64, T, H, sp)
+        comb = (P(d["topk"].data_ptr()), d["topk"].shape[1], d["topk"].shape[1],
+                P(d["topk_lens"].data_ptr()), P(qsl.data_ptr()), P(seq_lens.data_ptr()),
+                P(bt.data_ptr()), bt.shape[1], wl["B"], T, wl["top_k"], wl["window"], 64,
+                P(d["comb"].data_ptr()), W, P(d["lens"].data_ptr()), sp)
+        dec = (P(d["q"].data_ptr()), P(cache.data_ptr()), npg, 64, P(d["comb"].data_ptr()), W,
+               P(d["lens"].data_ptr()), P(d["sinks"].data_ptr()),
+               ctypes.c_float(wl["softmax_scale"]), P(d["out"].data_ptr()), None, T, H, sp)
+        calls.append((ins, comb, dec))
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(lib.dsv4_last_error().decode())
+
+    # valid slots per instance (algorithmic work), from one combine per instance
+    n_valid = []
+    num_slots = npg * 64
+    for (ins, comb, dec), d in zip(calls, inst):
+        check(lib.dsv4_combine_indices(*comb))
+    torch.cuda.synchronize()
+    for d in inst:
+        c = d["comb"].cpu().numpy()
+        L = d["lens"].cpu().numpy()
+        mask = (np.arange(W)[None, :] < L[:, None]) & (c >= 0) & (c < num_slots)
+        n_valid.append(int(mask.sum()))
+    lens_sum = [int(d["lens"].cpu().numpy().sum()) for d in inst]
+
+    n_inst = len(inst)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6 * (args.steps))]
+
+    def step(i, timed_idx=None):
+        ins, comb, dec = calls[i % n_inst]
+        if timed_idx is None:
+            check(lib.dsv4_kv_insert(*ins))
+            check(lib.dsv4_combine_indices(*comb))
+            check(lib.dsv4_sparse_mla_decode(*dec))
+            return
+        e = ev[6 * timed_idx:6 * timed_idx + 6]
+        e[0].record(stream)
+        check(lib.dsv4_kv_insert(*ins))
+        e[1].record(stream)
+        e[2].record(stream)
+        check(lib.dsv4_combine_indices(*comb))
+        e[3].record(stream)
+        e[4].record(stream)
+        check(lib.dsv4_sparse_mla_decode(*dec))
+        e[5].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(k, timed_idx=k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    ins_ms = np.array([ev[6 * k].elapsed_time(ev[6 * k + 1]) for k in range(args.steps)])
+    comb_ms = np.array([ev[6 * k + 2].elapsed_time(ev[6 * k + 3]) for k in range(args.steps)])
+    dec_ms = np.array([ev[6 * k + 4].elapsed_time(ev[6 * k + 5]) for k in range(args.steps)])
+    dec_s = float(dec_ms.mean()) * 1e-3
+
+    # algorithmic work per decode launch, averaged over the rotation actually timed
+    used = [k % n_inst for k in range(args.steps)]
+    nv = float(np.mean([n_valid[i] for i in used]))
+    ls = float(np.mean([lens_sum[i] for i in used]))
+    flops = 2.0 * H * (LATENT + NOPE) * nv
+    bytes_alg = RECORD * nv + T * H * (LATENT + NOPE) * 2 + 4.0 * ls + 4.0 * T + 4.0 * H
+    achieved_tflops = flops / dec_s / 1e12
+    achieved_gbs = bytes_alg / dec_s / 1e9
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = bytes_alg / (PEAK_HBM_GBS * 1e9)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+
+    value = T * args.steps / elapsed
+    log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms -> {elapsed / args.steps * 1e6:.1f} us/step; "
+        f"kernel means: insert {ins_ms.mean() * 1e3:.1f} us, combine {comb_ms.mean() * 1e3:.1f} us, "
+        f"decode {dec_ms.mean() * 1e3:.1f} us (median {np.median(dec_ms) * 1e3:.1f}, "
+        f"min {dec_ms.min() * 1e3:.1f})")
+    log(f"[bench] decode: valid slots/launch {nv:.0f}, {flops / 1e9:.2f} GFLOP, {bytes_alg / 1e6:.1f} MB "
+        f"-> {achieved_tflops:.0f} TFLOP/s ({achieved_tflops / PEAK_BF16_TFLOPS * 100:.1f}% of bf16 MFMA), "
+        f"{achieved_gbs:.0f} GB/s ({achieved_gbs / PEAK_HBM_GBS * 100:.1f}% of HBM)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "sparse MLA decode step: fused q-norm/RoPE/FP8 insert + top-k/window "
+                        "index combine + sparse MLA over an FP8/UE8M0 paged latent cache",
+            "batch": T, "heads": H, "top_k": wl["top_k"], "topk_lens": "U{1024..2048}",
+            "window": wl["window"], "combined_width": W, "context": int(wl["seq_lens"][0]),
+            "page_size": 64, "latent_dim": LATENT, "value_dim": NOPE, "sinks": True,
+            "instances_rotated": n_inst, "cache": "FP8 e4m3 nope + UE8M0 scales + bf16 rope",
+        },
+        "roofline": {
+            "bound": bound,
+            "achieved": round(achieved_tflops if bound == "mfma" else achieved_gbs, 2),
+            "peak": PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS,
+            "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+            "frac": round((achieved_tflops / PEAK_BF16_TFLOPS) if bound == "mfma"
+                          else (achieved_gbs / PEAK_HBM_GBS), 4),
+            "traffic": measured_traffic(),
+            "kernel": "sparse_mla_kernel<2> (dsv4_sparse_mla_decode)",
+            "launch_us": round(dec_s * 1e6, 2),
+            "alg_flops": flops, "alg_bytes": bytes_alg,
+            "hbm_frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+        },
+        "kernels_us": {"kv_insert": round(float(ins_ms.mean()) * 1e3, 2),
+                       "combine_indices": round(float(comb_ms.mean()) * 1e3, 2),
+                       "sparse_mla_decode": round(float(dec_ms.mean()) * 1e3, 2)},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, inst[0], calls, H, T, W)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, d0, calls, H, T, W):
+    """The CPU oracle (fp64, as it stands) timed on this host on one full step of
+    instance 0: insert + combine + attention for all 64 query tokens."""
+    import oracle
+    from synth_inputs import bf16_normal  # noqa: F401
+    oracle.build()
+    cores = len(os.sched_getaffinity(0))
+    it = wl["instances"][0]
+    npg = wl["num_pages"]
+    # host cache holding the rows instance 0 references (built untimed)
+    idx0, lens0 = oracle.combine(it["topk"], it["topk_lens"], wl["qsl"], wl["seq_lens"],
+                                 wl["block_table"], T, wl["top_k"], wl["window"], 64, W)
+    need = np.unique(idx0[idx0 >= 0])
+    sel = np.isin(wl["ctx_slot"], need)
+    cache = np.zeros(npg * 64 * RECORD, np.uint8)
+    oracle.kv_insert(np.zeros((int(sel.sum()), 0, LATENT), np.uint16), wl["ctx_kv"][sel],
+                     wl["ctx_pos"][sel], wl["ctx_slot"][sel], wl["cos_sin"],
+                     np.zeros(LATENT, np.uint16), wl["eps"], cache, npg, 64, inplace=True)
+    q = np.array(it["q"], copy=True)
+    kv_new = d0["kv"].cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+    pos = wl["seq_lens"].astype(np.int64) - 1
+    slots = wl["block_table"][np.arange(T), pos // 64].astype(np.int64) * 64 + pos % 64
+    t0 = time.perf_counter()
+    oracle.kv_insert(q, kv_new, pos, slots, wl["cos_sin"], wl["q_norm_weight"], wl["eps"], cache,
+                     npg, 64, inplace=True)
+    idx, lens = oracle.combine(it["topk"], it["topk_lens"], wl["qsl"], wl["seq_lens"],
+                               wl["block_table"], T, wl["top_k"], wl["window"], 64, W)
+    oracle.sparse_mla(q, cache, npg, 64, idx, lens, it["sinks"], wl["softmax_scale"],
+                      nthreads=cores, with_lse=False)
+    el = time.perf_counter() - t0
+    log(f"[bench] cpu oracle: one step ({T} query tokens) in {el:.2f} s on {cores} threads")
+    return {"value": round(T / el, 3), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one full decode step of the same workload (instance 0: {T} query tokens, "
+                      f"H={H}; fp64 insert + combine + attention), {el:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

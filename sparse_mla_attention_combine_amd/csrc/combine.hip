@@ -12,6 +12,8 @@
 
 namespace dsv4 {
 
+constexpr int kColsPerThread = 9;  // 2304 columns per pass covers the 2176-wide rows
+
 __device__ __forceinline__ int32_t phys_slot(const int32_t* __restrict__ bt_row, int bt_stride,
                                              int64_t x) {
   int64_t lp = x >> 6;  // logical page (page size 64)
@@ -43,15 +45,27 @@ __global__ void __launch_bounds__(256) combine_kernel(
     const int64_t lo = pos - sw + 1;
     const int32_t* trow = topk + t * topk_stride;
     int32_t* crow = combined + t * combined_stride;
-    for (int j = threadIdx.x; j < combined_stride; j += blockDim.x) {
-      int32_t v = -1;
-      if (j < tk) {
-        const int64_t x = j < topk_width ? (int64_t)trow[j] : -1;
-        if (x >= 0 && x < lo) v = phys_slot(bt_row, bt_stride, x);  // x >= lo: window has it
-      } else if (j < tk + sw) {
-        v = phys_slot(bt_row, bt_stride, lo + (j - tk));
+    // columns j = threadIdx.x + 256k: all top-k loads, then all block-table loads, are
+    // issued before any is consumed (one memory round trip each per row, not per column)
+    for (int jb = 0; jb < combined_stride; jb += 256 * kColsPerThread) {
+      int64_t x[kColsPerThread];
+#pragma unroll
+      for (int k = 0; k < kColsPerThread; ++k) {
+        const int j = jb + threadIdx.x + 256 * k;
+        x[k] = -1;
+        if (j < tk) x[k] = j < topk_width ? (int64_t)trow[j] : -1;
+        else if (j < tk + sw) x[k] = lo + (j - tk);
+        // top-k entries that are invalid, beyond pos, or inside the window -> -1
+        if (j < tk && !(x[k] >= 0 && x[k] < lo)) x[k] = -1;
       }
-      crow[j] = v;
+      int32_t v[kColsPerThread];
+#pragma unroll
+      for (int k = 0; k < kColsPerThread; ++k) v[k] = x[k] >= 0 ? phys_slot(bt_row, bt_stride, x[k]) : -1;
+#pragma unroll
+      for (int k = 0; k < kColsPerThread; ++k) {
+        const int j = jb + threadIdx.x + 256 * k;
+        if (j < combined_stride) crow[j] = v[k];
+      }
     }
     if (threadIdx.x == 0) combined_lens[t] = (int32_t)(tk + sw);
   }

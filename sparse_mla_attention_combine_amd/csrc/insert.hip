@@ -17,10 +17,10 @@
 
 namespace dsv4 {
 
-__global__ void __launch_bounds__(256) q_norm_rope_kernel(
+__device__ __forceinline__ void q_norm_rope(
     uint16_t* __restrict__ q, const int64_t* __restrict__ positions,
     const float* __restrict__ cos_sin, int max_pos, const uint16_t* __restrict__ weight, float eps,
-    int64_t rows, int H) {
+    int64_t rows, int H, int qblocks) {
   const int lane = threadIdx.x & 63;
   const int r8 = lane >> 3, c8 = lane & 7;
   // this lane always touches chunks c8 + 8k (k = 0..8) of a row: keep their weights
@@ -36,7 +36,7 @@ __global__ void __launch_bounds__(256) q_norm_rope_kernel(
     }
   }
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const int64_t nwaves = ((int64_t)qblocks * blockDim.x) >> 6;
   for (int64_t g = wave; g * 8 < rows; g += nwaves) {
     const int64_t row = g * 8 + r8;
     if (row >= rows) continue;
@@ -87,12 +87,12 @@ __global__ void __launch_bounds__(256) q_norm_rope_kernel(
   }
 }
 
-__global__ void __launch_bounds__(256) kv_quant_insert_kernel(
+__device__ __forceinline__ void kv_quant_insert(
     const uint16_t* __restrict__ kv, const int64_t* __restrict__ positions,
     const int64_t* __restrict__ slot_mapping, const float* __restrict__ cos_sin, int max_pos,
-    uint8_t* __restrict__ cache, int64_t num_slots, int T) {
+    uint8_t* __restrict__ cache, int64_t num_slots, int T, int block) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t t = ((int64_t)block * blockDim.x + threadIdx.x) >> 6;
   if (t >= T) return;
   const int64_t p = positions[t];
   const int64_t slot = slot_mapping[t];
@@ -156,24 +156,33 @@ __global__ void __launch_bounds__(256) kv_quant_insert_kernel(
   }
 }
 
+// One launch: blocks [0, qblocks) stream the q rows, the remaining blocks quantise the
+// new latent rows (4 tokens per block).
+__global__ void __launch_bounds__(256) insert_kernel(
+    uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int64_t* __restrict__ positions,
+    const int64_t* __restrict__ slot_mapping, const float* __restrict__ cos_sin, int max_pos,
+    const uint16_t* __restrict__ weight, float eps, uint8_t* __restrict__ cache, int64_t num_slots,
+    int T, int H, int qblocks) {
+  if ((int)blockIdx.x < qblocks)
+    q_norm_rope(q, positions, cos_sin, max_pos, weight, eps, (int64_t)T * H, H, qblocks);
+  else
+    kv_quant_insert(kv, positions, slot_mapping, cos_sin, max_pos, cache, num_slots, T,
+                    (int)blockIdx.x - qblocks);
+}
+
 hipError_t launch_insert(void* q, const void* kv, const int64_t* positions,
                          const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                          const void* weight, float eps, uint8_t* cache, int num_pages, int T,
                          int H, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int64_t rows = (int64_t)T * H;
-  if (rows > 0) {
-    int64_t groups = (rows + 31) / 32;  // 32 rows per 256-thread block
-    int blocks = (int)(groups < 8192 ? groups : 8192);
-    hipLaunchKernelGGL(q_norm_rope_kernel, dim3(blocks), dim3(256), 0, stream,
-                       static_cast<uint16_t*>(q), positions, cos_sin, max_pos,
-                       static_cast<const uint16_t*>(weight), eps, rows, H);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  hipLaunchKernelGGL(kv_quant_insert_kernel, dim3((T + 3) / 4), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(kv), positions, slot_mapping, cos_sin, max_pos,
-                     cache, (int64_t)num_pages * kPage, T);
+  const int64_t groups = (rows + 31) / 32;  // 32 q rows per 256-thread block per pass
+  const int qblocks = rows > 0 ? (int)(groups < 8192 ? groups : 8192) : 0;
+  const int kvblocks = (T + 3) / 4;
+  hipLaunchKernelGGL(insert_kernel, dim3(qblocks + kvblocks), dim3(256), 0, stream,
+                     static_cast<uint16_t*>(q), static_cast<const uint16_t*>(kv), positions,
+                     slot_mapping, cos_sin, max_pos, static_cast<const uint16_t*>(weight), eps,
+                     cache, (int64_t)num_pages * kPage, T, H, qblocks);
   return hipGetLastError();
 }
 
