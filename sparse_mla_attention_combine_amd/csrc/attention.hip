@@ -221,7 +221,9 @@ __device__ __forceinline__ void chunk_step(AttnSmem<NHB>& sm, AttnState<NHB>& st
   }
   __syncthreads();
 
-  // ---- O^T[c][h] += V^T[c][j] P^T[j][h] for c in 128w..128w+127
+  // ---- O^T[c][h] += V^T[c][j] P^T[j][h] for c in 128w..128w+127.  All LDS reads of a
+  // 32-slot step are issued before its MFMAs, so their latencies overlap instead of
+  // being paid one by one.
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     bf16x8 pf[NHB];
@@ -233,14 +235,18 @@ __device__ __forceinline__ void chunk_step(AttnSmem<NHB>& sm, AttnState<NHB>& st
     // j0..j0+3.  Rows j0 = 32ks+8g (+4 for the second read).
     const int j0 = 32 * ks + 8 * g + (l16 >> 2);
     const int q4 = l16 & 3;
+    bf16x4 t0[8], t1[8];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       const int unit = 16 * w + 2 * mb + (q4 >> 1);
-      const bf16x4 t0 = lds_read_tr16(vtile + v_off(j0, unit) + 4 * (q4 & 1));
-      const bf16x4 t1 = lds_read_tr16(vtile + v_off(j0 + 4, unit) + 4 * (q4 & 1));
+      t0[mb] = lds_read_tr16(vtile + v_off(j0, unit) + 4 * (q4 & 1));
+      t1[mb] = lds_read_tr16(vtile + v_off(j0 + 4, unit) + 4 * (q4 & 1));
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
       bf16x8 vf;
-      vf[0] = t0[0]; vf[1] = t0[1]; vf[2] = t0[2]; vf[3] = t0[3];
-      vf[4] = t1[0]; vf[5] = t1[1]; vf[6] = t1[2]; vf[7] = t1[3];
+      vf[0] = t0[mb][0]; vf[1] = t0[mb][1]; vf[2] = t0[mb][2]; vf[3] = t0[mb][3];
+      vf[4] = t1[mb][0]; vf[5] = t1[mb][1]; vf[6] = t1[mb][2]; vf[7] = t1[mb][3];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) st.oacc[mb][hb] = mfma16(vf, pf[hb], st.oacc[mb][hb]);
     }
