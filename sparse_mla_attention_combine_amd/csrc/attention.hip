@@ -37,9 +37,6 @@ namespace dsv4 {
 constexpr int kChunk = 64;
 constexpr int kVStride = 512;  // bf16 per LDS value row (1024 B, 16 B units XOR-swizzled)
 constexpr int kPStride = 72;   // bf16 per LDS probability row: 144 B
-// The running max is only moved (and O rescaled) when a chunk beats it by more than
-// 2^8 in probability units; in between, probabilities up to 256 are exact in bf16/fp32.
-constexpr float kRescaleSlack = 8.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -94,12 +91,10 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
 }
 
 // V tile layout: row j of the chunk occupies 1024 B; its 16 B unit k (value dims
-// 8k..8k+7) is stored at unit k ^ swz(j).  swz spreads the b128 row writes of a wave
-// (16 rows x 4 k-groups) over all banks, and keeps the 4 rows x 2 units that one
-// 16-lane group of a transposing read touches on distinct banks.
-__device__ __forceinline__ int v_swz(int row) {
-  return (2 * (row & 3)) | ((row >> 2) & 1) | (((row >> 3) & 1) << 3);
-}
+// 8k..8k+7) is stored at unit k ^ swz(j), swz(j) = 4*(j & 3) + ((j >> 2) & 3).  The four
+// rows that one 16-lane group of a transposing read touches then sit on disjoint banks,
+// and the 16 rows of a wave's 16 B row writes are spread over all of them.
+__device__ __forceinline__ int v_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int v_off(int row, int unit) {  // in bf16 elements
   return row * kVStride + ((unit ^ v_swz(row)) << 3);
 }
@@ -124,57 +119,207 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// A probability may exceed 1 by up to 2^kPLimit before the reference max must move:
+// the reference agreed on after a chunk's barrier applies to the next chunk, and a
+// chunk that beats it by more than this is recomputed (fp32/bf16 hold it exactly).
+constexpr float kPLimit = 20.0f;
+
 template <int NHB>
 struct AttnState {
   bf16x8 qf[NHB][18];  // Q^T fragments (registers for the whole kernel)
-  float m_run[NHB];    // running max per head (log2 domain), same in every wave
+  float m_run[NHB];    // reference max per head (log2 domain), same in every wave
   float l_part[NHB];   // this lane's share of the softmax denominator
-  f32x4 oacc[8][NHB];  // O^T for output dims 128w + 16mb + 4g + i, head l16 of block hb
+  // O^T, per wave 128 of the 512 output dims:
+  //   NHB == 1: o16[mb] = dims 128w + 16mb + 4g + i, head l16 (16x16 MFMA layout)
+  //   NHB == 2: o32[mb] = dims 128mb + 32w + 8(r/4) + 4(lane/32) + r%4, head lane%32
+  f32x4 o16[8];
+  f32x16 o32[4];
 };
 
-// One chunk of 64 listed slots: dequantise + stage V + S^T = K Q^T, online softmax,
-// O^T += V^T P^T.  `cur` holds this wave's 16 slots (row l16, k-group g) of the chunk.
+// Dequantise this lane's slot of a chunk (row 16w + l16, k-group g), stage its value
+// dims as bf16 into `vtile` and return S^T fragments: sacc[hb][i] = q.k of chunk row
+// 16w + 4g + i and head 16hb + l16.  Two accumulator chains per head block.
 template <int NHB>
-__device__ __forceinline__ void chunk_step(AttnSmem<NHB>& sm, AttnState<NHB>& st,
-                                           const RawSlot& cur, RawSlot& pf, int pf_jj, int n_blk,
-                                           const uint8_t* __restrict__ cache, int64_t num_slots,
-                                           int buf, int w, int l16, int g, float scale_log2) {
-  // ---- dequantise, stage V, S^T = K Q^T
-  f32x4 sacc[NHB];
+__device__ __forceinline__ void stage_chunk(__bf16* __restrict__ vtile, const RawSlot& cur,
+                                            const AttnState<NHB>& st, f32x4 (&sacc)[NHB], int w,
+                                            int l16, int g) {
+  f32x4 sa[NHB], sb[NHB];
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  __bf16* vtile = &sm.v[buf][0][0];
+  for (int hb = 0; hb < NHB; ++hb) {
+    sa[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sb[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const int vr = 16 * w + l16;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const uint32_t sb = ((u < 4 ? cur.sc.x : cur.sc.y) >> (8 * (u & 3))) & 0xFF;
-    const float scale = e8m0_as_scale(sb);
+    const uint32_t sbyte = ((u < 4 ? cur.sc.x : cur.sc.y) >> (8 * (u & 3))) & 0xFF;
+    const float scale = e8m0_as_scale(sbyte);
     const bf16x8 k0 = dequant8(cur.nope[u].x, cur.nope[u].y, scale);
     const bf16x8 k1 = dequant8(cur.nope[u].z, cur.nope[u].w, scale);
     *reinterpret_cast<bf16x8*>(vtile + v_off(vr, 8 * u + 2 * g)) = k0;
     *reinterpret_cast<bf16x8*>(vtile + v_off(vr, 8 * u + 2 * g + 1)) = k1;
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      sacc[hb] = mfma16(k0, st.qf[hb][2 * u], sacc[hb]);
-      sacc[hb] = mfma16(k1, st.qf[hb][2 * u + 1], sacc[hb]);
+      sa[hb] = mfma16(k0, st.qf[hb][2 * u], sa[hb]);
+      sb[hb] = mfma16(k1, st.qf[hb][2 * u + 1], sb[hb]);
     }
   }
-  {
-    const bf16x8 k16 = as_bf16x8(cur.rope[0]);
-    const bf16x8 k17 = as_bf16x8(cur.rope[1]);
+  const bf16x8 k16 = as_bf16x8(cur.rope[0]);
+  const bf16x8 k17 = as_bf16x8(cur.rope[1]);
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-      sacc[hb] = mfma16(k16, st.qf[hb][16], sacc[hb]);
-      sacc[hb] = mfma16(k17, st.qf[hb][17], sacc[hb]);
+  for (int hb = 0; hb < NHB; ++hb) {
+    sa[hb] = mfma16(k16, st.qf[hb][16], sa[hb]);
+    sb[hb] = mfma16(k17, st.qf[hb][17], sb[hb]);
+    sacc[hb] = sa[hb] + sb[hb];
+  }
+}
+
+// O^T[c][h] += V^T[c][j] P^T[j][h] over the 64 rows of a staged chunk, for this wave's
+// 128 output dims.  Transposing reads: input lane 4r+q of a 16-lane group addresses row
+// row0+r, dims col0+4q..col0+4q+3 (16 B unit col0/8 + q/2, half q&1); lane L of the
+// group receives dim col0+L of rows row0..row0+3.
+// NHB == 1: O^T[c][h] += V^T[c][j] P^T[j][h] over the 64 rows of a staged chunk for
+// this wave's 128 output dims, on 16x16x32 MFMA: A = V^T (16 dims x 32 rows), B = P^T
+// (32 rows x 16 heads).  Transposing reads: input lane 4r+q of a 16-lane group addresses
+// row row0+r, dims col0+4q..col0+4q+3; lane L of the group receives dim col0+L of rows
+// row0..row0+3.
+template <int NHB>
+__device__ __forceinline__ void pv_chunk(const __bf16* __restrict__ vtile,
+                                         const __bf16 (*__restrict__ ptile)[kPStride],
+                                         AttnState<NHB>& st, int w, int lane) {
+  static_assert(NHB == 1, "the two-block path uses pv_reads2 / pv_mfma2");
+  const int l16 = lane & 15, G = lane >> 4;
+  const int r = l16 >> 2, q4 = l16 & 3;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8 pf = *reinterpret_cast<const bf16x8*>(&ptile[l16][32 * ks + 8 * G]);
+    const int row0 = 32 * ks + 8 * G + r;
+    bf16x4 t0[8], t1[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const int unit = 16 * w + 2 * mb + (q4 >> 1);
+      t0[mb] = lds_read_tr16(vtile + v_off(row0, unit) + 4 * (q4 & 1));
+      t1[mb] = lds_read_tr16(vtile + v_off(row0 + 4, unit) + 4 * (q4 & 1));
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      bf16x8 vf;
+      vf[0] = t0[mb][0]; vf[1] = t0[mb][1]; vf[2] = t0[mb][2]; vf[3] = t0[mb][3];
+      vf[4] = t1[mb][0]; vf[5] = t1[mb][1]; vf[6] = t1[mb][2]; vf[7] = t1[mb][3];
+      st.o16[mb] = mfma16(vf, pf, st.o16[mb]);
     }
   }
+}
 
-  // ---- request the records of a later chunk now that `cur` has been consumed
-  const uint64_t vmask = __ballot(cur.valid);  // bit j (j < 16) = row j of this wave valid
-  load_raw(pf, cache, num_slots, sm.idx, pf_jj, n_blk, g);
+// NHB == 2 pieces of a pipelined chunk step.  Output dims of wave w are the 32-dim
+// blocks 128mb + 32w (mb = 0..3), so that in the transposing reads the lane-dependent
+// part of the swizzle lands on the wave's own unit bits and every LDS access of a lane
+// is one base register plus a compile-time constant.
 
-  // ---- online softmax (log2 domain). sacc[hb][i] = score of row 4g+i, head l16.
-  float s[NHB][4];
+// Staging of one chunk: dequantise this lane's slot (row 16w + l16, k-group g), write its
+// value dims into `vn`, S^T fragments into sacc (two accumulator chains per head block).
+__device__ __forceinline__ void stage2(__bf16* __restrict__ vn, const RawSlot& cur,
+                                       const AttnState<2>& st, f32x4 (&sacc)[2], int w,
+                                       int lane) {
+  const int l16 = lane & 15, g = lane >> 4;
+  const int vr = 16 * w + l16;
+  // unit 8u + 2g + h of row vr goes to unit (8u + 2g + h) ^ swz(vr): bit 3 of swz flips
+  // the parity of u, bit 0 flips h, bits 1-2 act on g only.
+  const int sw = v_swz(vr);
+  const int ub = (sw >> 3) & 1;
+  const int c0 = (2 * g) ^ (sw & 6);
+  __bf16* const rowp = vn + vr * kVStride + 8 * c0;
+  __bf16* const wb[2][2] = {{rowp + 64 * ub + 8 * (sw & 1), rowp + 64 * ub + 8 * (1 - (sw & 1))},
+                            {rowp - 64 * ub + 8 * (sw & 1), rowp - 64 * ub + 8 * (1 - (sw & 1))}};
+  f32x4 sa[2], sb[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    sa[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sb[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t sbyte = ((u < 4 ? cur.sc.x : cur.sc.y) >> (8 * (u & 3))) & 0xFF;
+    const float scale = e8m0_as_scale(sbyte);
+    const bf16x8 k0 = dequant8(cur.nope[u].x, cur.nope[u].y, scale);
+    const bf16x8 k1 = dequant8(cur.nope[u].z, cur.nope[u].w, scale);
+    *reinterpret_cast<bf16x8*>(wb[u & 1][0] + 64 * u) = k0;
+    *reinterpret_cast<bf16x8*>(wb[u & 1][1] + 64 * u) = k1;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      sa[hb] = mfma16(k0, st.qf[hb][2 * u], sa[hb]);
+      sb[hb] = mfma16(k1, st.qf[hb][2 * u + 1], sb[hb]);
+    }
+  }
+  const bf16x8 k16 = as_bf16x8(cur.rope[0]);
+  const bf16x8 k17 = as_bf16x8(cur.rope[1]);
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    sa[hb] = mfma16(k16, st.qf[hb][16], sa[hb]);
+    sb[hb] = mfma16(k17, st.qf[hb][17], sb[hb]);
+    sacc[hb] = sa[hb] + sb[hb];
+  }
+}
+
+// P.V operands of a staged chunk.  32x32x16 MFMA: A = V^T (32 dims x 16 rows), lane L
+// holding dim L%32 of rows 8(L/32)..+7; B = P^T, lane L holding head L%32 of the same rows.
+// Transposing read: input lane 4r+q of a 16-lane group addresses row row0+r, dims
+// col0+4q..+3 (unit col0/8 + q/2, half q&1); lane L of the group receives dim col0+L of
+// rows row0..row0+3.  Row 16ks + 8hi + r (+4) has swz 4r + 2hi (+1).
+struct PvFrags {
+  bf16x8 pf[4];
+  bf16x4 t0[4][4], t1[4][4];
+};
+__device__ __forceinline__ void pv_reads2(const __bf16* __restrict__ vt,
+                                          const __bf16 (*__restrict__ pt)[kPStride], PvFrags& f,
+                                          int w, int lane) {
+  const int l16 = lane & 15, G = lane >> 4, hi = lane >> 5;
+  const int r = l16 >> 2, q4 = l16 & 3;
+  const int lo = 2 * (G & 1) + (q4 >> 1);  // unit bits 0-1 before the swizzle
+  const __bf16* const rb0 =
+      vt + (8 * hi + r) * kVStride + 8 * (4 * (w ^ r) + (lo ^ (2 * hi))) + 4 * (q4 & 1);
+  const __bf16* const rb1 =
+      vt + (8 * hi + r + 4) * kVStride + 8 * (4 * (w ^ r) + (lo ^ (2 * hi + 1))) + 4 * (q4 & 1);
+  const __bf16* const pb = &pt[lane & 31][8 * hi];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    f.pf[ks] = *reinterpret_cast<const bf16x8*>(pb + 16 * ks);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      f.t0[ks][mb] = lds_read_tr16(rb0 + 16 * ks * kVStride + 128 * mb);
+      f.t1[ks][mb] = lds_read_tr16(rb1 + 16 * ks * kVStride + 128 * mb);
+    }
+  }
+}
+__device__ __forceinline__ void pv_mfma2(const PvFrags& f, AttnState<2>& st) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      bf16x8 vf;
+      vf[0] = f.t0[ks][mb][0]; vf[1] = f.t0[ks][mb][1]; vf[2] = f.t0[ks][mb][2]; vf[3] = f.t0[ks][mb][3];
+      vf[4] = f.t1[ks][mb][0]; vf[5] = f.t1[ks][mb][1]; vf[6] = f.t1[ks][mb][2]; vf[7] = f.t1[ks][mb][3];
+      st.o32[mb] = mfma32(vf, f.pf[ks], st.o32[mb]);
+    }
+}
+
+// Scores of the freshly staged chunk -> log2-domain s (invalid rows -inf), this wave's
+// per-head maxima into `red`, probabilities against the current reference into
+// `ptile` (clamped at 2^kPLimit; a chunk that needs more is recomputed after the
+// barrier), and their per-lane sums into psum.
+template <int NHB>
+__device__ __forceinline__ void softmax_local(__bf16 (*__restrict__ ptile)[kPStride],
+                                              float (*__restrict__ red)[16 * NHB],
+                                              const f32x4 (&sacc)[NHB], uint64_t vmask,
+                                              const AttnState<NHB>& st, float scale_log2,
+                                              float (&s)[NHB][4], float (&psum)[NHB], int w,
+                                              int l16, int g) {
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     float mx = -INFINITY;
@@ -185,71 +330,115 @@ __device__ __forceinline__ void chunk_step(AttnSmem<NHB>& sm, AttnState<NHB>& st
       mx = fmaxf(mx, s[hb][i]);
     }
     mx = max_xor32(max_xor16(mx));
-    if (g == 0) sm.red[buf][w][16 * hb + l16] = mx;
-  }
-  __syncthreads();
-  float alpha[NHB];
-  bool rescale = false;
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    float cm = sm.red[buf][0][16 * hb + l16];
-#pragma unroll
-    for (int ww = 1; ww < 4; ++ww) cm = fmaxf(cm, sm.red[buf][ww][16 * hb + l16]);
-    // move the reference max only when this chunk beats it by more than the slack
-    alpha[hb] = 1.f;
-    if (cm > st.m_run[hb] + kRescaleSlack) {
-      alpha[hb] = (st.m_run[hb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m_run[hb] - cm);
-      st.m_run[hb] = cm;
-      rescale = true;
-    }
+    if (g == 0) red[w][16 * hb + l16] = mx;
     const float mr = st.m_run[hb];
-    float p[4], sum = 0.f;
+    float p[4];
+    psum[hb] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = (s[hb][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[hb][i] - mr);
-      sum += p[i];
+      p[i] = (s[hb][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(fminf(s[hb][i] - mr, kPLimit));
+      psum[hb] += p[i];
     }
-    st.l_part[hb] = st.l_part[hb] * alpha[hb] + sum;
-    *reinterpret_cast<uint2*>(&sm.p[buf][16 * hb + l16][16 * w + 4 * g]) =
+    *reinterpret_cast<uint2*>(&ptile[16 * hb + l16][16 * w + 4 * g]) =
         make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
   }
-  if (__builtin_amdgcn_ballot_w64(rescale)) {  // wave-uniform, rare after the first chunk
+}
+
+// After the barrier that publishes a chunk's maxima: if any head's chunk max beats the
+// reference by more than kPLimit (always the case for the first chunk with a valid
+// row), every wave moves the reference, rescales O and the denominator, rewrites the
+// chunk's probabilities and meets at one more barrier.  The decision reads the same LDS
+// words in every wave, so the workgroup takes the branch together.
+template <int NHB>
+__device__ __forceinline__ void resolve_chunk(__bf16 (*__restrict__ ptile)[kPStride],
+                                              const float (*__restrict__ red)[16 * NHB],
+                                              AttnState<NHB>& st, const float (&s)[NHB][4],
+                                              float (&psum)[NHB], int w, int l16, int g) {
+  float cm[NHB];
+  bool fix = false;
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
+  for (int hb = 0; hb < NHB; ++hb) {
+    cm[hb] = fmaxf(fmaxf(red[0][16 * hb + l16], red[1][16 * hb + l16]),
+                   fmaxf(red[2][16 * hb + l16], red[3][16 * hb + l16]));
+    fix |= cm[hb] > st.m_run[hb] + kPLimit;
+  }
+  if (__builtin_amdgcn_ballot_w64(fix)) {
+    float alpha[NHB];
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) st.oacc[mb][hb] *= alpha[hb];
+    for (int hb = 0; hb < NHB; ++hb) {
+      const float mn = fmaxf(st.m_run[hb], cm[hb]);
+      alpha[hb] = (mn == st.m_run[hb]) ? 1.f : __builtin_amdgcn_exp2f(st.m_run[hb] - mn);
+      st.m_run[hb] = mn;
+      st.l_part[hb] *= alpha[hb];
+      float p[4];
+      psum[hb] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = (s[hb][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(fminf(s[hb][i] - mn, kPLimit));
+        psum[hb] += p[i];
+      }
+      *reinterpret_cast<uint2*>(&ptile[16 * hb + l16][16 * w + 4 * g]) =
+          make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    }
+    if constexpr (NHB == 2) {
+      const float a = (g & 1) ? alpha[1] : alpha[0];  // this lane's head is lane % 32
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) st.o32[mb] *= a;
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) st.o16[mb] *= alpha[0];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) st.l_part[hb] += psum[hb];
+}
+
+// Chunk i's P.V (tiles vt/pt, published by the last barrier) in the same basic block as
+// chunk i+1's staging (raw -> vn, scores), so the matrix cores, the LDS and the VALU
+// work on both at once; then chunk i+1's softmax, the chunk's only barrier, and its
+// reference check.
+template <int NHB>
+__device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnState<NHB>& st,
+                                               RawSlot& raw, int pf_jj, int n_blk,
+                                               const uint8_t* __restrict__ cache,
+                                               int64_t num_slots, int w, int lane,
+                                               float scale_log2) {
+  const int l16 = lane & 15, g = lane >> 4;
+  const int nb = cb ^ 1;
+  f32x4 sacc[NHB];
+  float s[NHB][4], psum[NHB];
+  if constexpr (NHB == 2) {
+    // staging + S first, so the scores are ready by the softmax; the P.V operands are
+    // requested next and consumed last, so their MFMAs run across the barrier.
+    stage2(&sm.v[nb][0][0], raw, st, sacc, w, lane);
+    PvFrags f;
+    pv_reads2(&sm.v[cb][0][0], sm.p[cb], f, w, lane);
+    const uint64_t vmask = __ballot(raw.valid);  // bit j (j < 16) = row 16w + j valid
+    load_raw(raw, cache, num_slots, sm.idx, pf_jj, n_blk, g);
+    softmax_local<NHB>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
+    pv_mfma2(f, st);
+  } else {
+    stage_chunk<NHB>(&sm.v[nb][0][0], raw, st, sacc, w, l16, g);
+    pv_chunk<NHB>(&sm.v[cb][0][0], sm.p[cb], st, w, lane);
+    const uint64_t vmask = __ballot(raw.valid);
+    load_raw(raw, cache, num_slots, sm.idx, pf_jj, n_blk, g);
+    softmax_local<NHB>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
   }
   __syncthreads();
+  resolve_chunk<NHB>(sm.p[nb], sm.red[nb], st, s, psum, w, l16, g);
+}
 
-  // ---- O^T[c][h] += V^T[c][j] P^T[j][h] for c in 128w..128w+127.  All LDS reads of a
-  // 32-slot step are issued before its MFMAs, so their latencies overlap instead of
-  // being paid one by one.
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    bf16x8 pf[NHB];
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
-      pf[hb] = *reinterpret_cast<const bf16x8*>(&sm.p[buf][16 * hb + l16][32 * ks + 8 * g]);
-    // transposing reads: input lane 4r+q of a 16-lane group addresses row j0+r, value
-    // dims c0+4q..c0+4q+3 (unit c0/8 + q/2, half q&1); lane L receives dim c0+L of rows
-    // j0..j0+3.  Rows j0 = 32ks+8g (+4 for the second read).
-    const int j0 = 32 * ks + 8 * g + (l16 >> 2);
-    const int q4 = l16 & 3;
-    bf16x4 t0[8], t1[8];
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const int unit = 16 * w + 2 * mb + (q4 >> 1);
-      t0[mb] = lds_read_tr16(vtile + v_off(j0, unit) + 4 * (q4 & 1));
-      t1[mb] = lds_read_tr16(vtile + v_off(j0 + 4, unit) + 4 * (q4 & 1));
-    }
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      bf16x8 vf;
-      vf[0] = t0[mb][0]; vf[1] = t0[mb][1]; vf[2] = t0[mb][2]; vf[3] = t0[mb][3];
-      vf[4] = t1[mb][0]; vf[5] = t1[mb][1]; vf[6] = t1[mb][2]; vf[7] = t1[mb][3];
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) st.oacc[mb][hb] = mfma16(vf, pf[hb], st.oacc[mb][hb]);
-    }
+// The block's last chunk: P.V only.
+template <int NHB>
+__device__ __forceinline__ void pv_last(AttnSmem<NHB>& sm, int cb, AttnState<NHB>& st,
+                                        int w, int lane) {
+  if constexpr (NHB == 2) {
+    PvFrags f;
+    pv_reads2(&sm.v[cb][0][0], sm.p[cb], f, w, lane);
+    pv_mfma2(f, st);
+  } else {
+    pv_chunk<NHB>(&sm.v[cb][0][0], sm.p[cb], st, w, lane);
   }
 }
 
@@ -295,18 +484,21 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     st.qf[hb][17] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kNope + 32 + 8 * g));
     st.m_run[hb] = -INFINITY;
     st.l_part[hb] = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) st.oacc[mb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) st.o16[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o32[mb][r] = 0.f;
 
-  // Index blocks of up to 4096 entries are staged in LDS; inside a block, the records of
-  // chunk c+2 are requested as soon as chunk c's contraction has consumed its buffer,
-  // so two register buffers keep two chunks in flight (2x unrolled, never copied).
+  // Index blocks of up to 4096 entries are staged in LDS.  Inside a block chunk c lives
+  // in register buffer c&1 and LDS tiles c&1; a buffer is refilled with chunk c+2 as
+  // soon as staging has consumed it, so two chunks of records are always in flight.
   const int row = 16 * w + l16;
-  int gch = 0;  // chunks done so far (parity of the LDS double buffers)
   for (int blk0 = 0; blk0 < n; blk0 += kIdxBlock) {
     const int n_blk = min(n - blk0, kIdxBlock);
-    __syncthreads();  // the previous block's entries are no longer read
+    __syncthreads();  // the previous block's entries and tiles are no longer read
 #pragma unroll 4
     for (int i = tid; i < n_blk; i += 256) sm.idx[i] = idx_row[blk0 + i];
     __syncthreads();
@@ -314,18 +506,33 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     RawSlot A, B;
     load_raw(A, cache, num_slots, sm.idx, row, n_blk, g);
     load_raw(B, cache, num_slots, sm.idx, kChunk + row, n_blk, g);
-    int c = 0;
-    // chunk c computes from one buffer and refills it with chunk c+2 once consumed
-    for (; c + 2 <= nch; c += 2) {
-      chunk_step<NHB>(sm, st, A, A, (c + 2) * kChunk + row, n_blk, cache, num_slots,
-                      (gch + c) & 1, w, l16, g, scale_log2);
-      chunk_step<NHB>(sm, st, B, B, (c + 3) * kChunk + row, n_blk, cache, num_slots,
-                      (gch + c + 1) & 1, w, l16, g, scale_log2);
+    {  // prologue: stage chunk 0 and settle its probabilities
+      f32x4 sacc[NHB];
+      if constexpr (NHB == 2)
+        stage2(&sm.v[0][0][0], A, st, sacc, w, lane);
+      else
+        stage_chunk<NHB>(&sm.v[0][0][0], A, st, sacc, w, l16, g);
+      const uint64_t vmask = __ballot(A.valid);
+      load_raw(A, cache, num_slots, sm.idx, 2 * kChunk + row, n_blk, g);
+      float s[NHB][4], psum[NHB];
+      softmax_local<NHB>(sm.p[0], sm.red[0], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
+      __syncthreads();
+      resolve_chunk<NHB>(sm.p[0], sm.red[0], st, s, psum, w, l16, g);
     }
-    if (c < nch)
-      chunk_step<NHB>(sm, st, A, A, (c + 2) * kChunk + row, n_blk, cache, num_slots,
-                      (gch + c) & 1, w, l16, g, scale_log2);
-    gch += nch;
+    int i = 0;
+    for (; i + 2 < nch; i += 2) {
+      pipelined_step<NHB>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cache, num_slots, w, lane,
+                          scale_log2);
+      pipelined_step<NHB>(sm, 1, st, A, (i + 4) * kChunk + row, n_blk, cache, num_slots, w, lane,
+                          scale_log2);
+    }
+    if (i + 1 < nch) {
+      pipelined_step<NHB>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cache, num_slots, w, lane,
+                          scale_log2);
+      pv_last<NHB>(sm, 1, st, w, lane);
+    } else {
+      pv_last<NHB>(sm, 0, st, w, lane);
+    }
   }
 
   // ---- finalise: sum the waves' partial denominators, add the sink, normalise
@@ -335,25 +542,39 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     if (g == 0) sm.lsum[w][16 * hb + l16] = lp;
   }
   __syncthreads();
+  // this lane's output head: l16 (NHB == 1) or lane % 32 (NHB == 2)
+  const int hl = NHB == 2 ? (lane & 31) : l16;
+  const int h = h0 + hl;
+  const float lt = sm.lsum[0][hl] + sm.lsum[1][hl] + sm.lsum[2][hl] + sm.lsum[3][hl];
+  const float mr = (NHB == 2 && (g & 1)) ? st.m_run[NHB - 1] : st.m_run[0];
+  const float z2 = sinks ? sinks[h] * kLog2e : -INFINITY;
+  const float M = fmaxf(mr, z2);
+  const float f = (mr == -INFINITY) ? 0.f : exp2f(mr - M);
+  const float den = lt * f + ((z2 == -INFINITY) ? 0.f : exp2f(z2 - M));
+  const float inv = den > 0.f ? f / den : 0.f;
+  uint16_t* orow = out + ((int64_t)t * H + h) * kNope;
+  if constexpr (NHB == 2) {
+    const int hi = lane >> 5;
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    const int h = h0 + 16 * hb + l16;
-    const float lt = sm.lsum[0][16 * hb + l16] + sm.lsum[1][16 * hb + l16] +
-                     sm.lsum[2][16 * hb + l16] + sm.lsum[3][16 * hb + l16];
-    const float mr = st.m_run[hb];
-    const float z2 = sinks ? sinks[h] * kLog2e : -INFINITY;
-    const float M = fmaxf(mr, z2);
-    const float f = (mr == -INFINITY) ? 0.f : exp2f(mr - M);
-    const float den = lt * f + ((z2 == -INFINITY) ? 0.f : exp2f(z2 - M));
-    const float inv = den > 0.f ? f / den : 0.f;
-    uint16_t* orow = out + ((int64_t)t * H + h) * kNope + 128 * w + 4 * g;
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const f32x16& o = st.o32[mb];
+        *reinterpret_cast<uint2*>(orow + 128 * mb + 32 * w + 8 * qd + 4 * hi) =
+            make_uint2(pack_bf16x2(o[4 * qd] * inv, o[4 * qd + 1] * inv),
+                       pack_bf16x2(o[4 * qd + 2] * inv, o[4 * qd + 3] * inv));
+      }
+    if (lse && w == 0 && hi == 0)
+      lse[(int64_t)t * H + h] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+  } else {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
-      const f32x4 o = st.oacc[mb][hb];
-      *reinterpret_cast<uint2*>(orow + 16 * mb) =
+      const f32x4 o = st.o16[mb];
+      *reinterpret_cast<uint2*>(orow + 128 * w + 16 * mb + 4 * g) =
           make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
     }
-    if (lse && w == 0 && g == 0) lse[(int64_t)t * H + h] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    if (lse && w == 0 && g == 0)
+      lse[(int64_t)t * H + h] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
   }
 }
 
