@@ -63,10 +63,8 @@ struct RawSlot {
   int valid;
 };
 
-__device__ __forceinline__ void load_raw(RawSlot& r, const uint8_t* __restrict__ cache,
-                                         int64_t num_slots, const int32_t* idx_lds, int jj,
-                                         int n_blk, int g) {
-  const int64_t slot = jj < n_blk ? (int64_t)idx_lds[jj] : -1;
+__device__ __forceinline__ void load_raw_slot(RawSlot& r, const uint8_t* __restrict__ cache,
+                                              int64_t num_slots, int64_t slot, int g) {
   r.valid = (slot >= 0 && slot < num_slots) ? 1 : 0;
   const uint8_t* base = r.valid ? cache + page_base(slot >> 6) : g_zero_page;
   const int off = r.valid ? (int)(slot & (kPage - 1)) : 0;
@@ -77,6 +75,11 @@ __device__ __forceinline__ void load_raw(RawSlot& r, const uint8_t* __restrict__
   r.rope[0] = *reinterpret_cast<const uint4*>(rp);
   r.rope[1] = *reinterpret_cast<const uint4*>(rp + 64);
   r.sc = *reinterpret_cast<const uint2*>(base + scale_off(off));
+}
+
+// Entry jj of the staged index block (-1 past its end).
+__device__ __forceinline__ int64_t idx_at(const int32_t* idx_lds, int jj, int n_blk) {
+  return jj < n_blk ? (int64_t)idx_lds[jj] : -1;
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -129,6 +132,9 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // the reference agreed on after a chunk's barrier applies to the next chunk, and a
 // chunk that beats it by more than this is recomputed (fp32/bf16 hold it exactly).
 constexpr float kPLimit = 20.0f;
+// Starting reference: finite, so that masked scores (-inf) give exp2(-inf) = 0 without a
+// test, and below any real score, so the first valid chunk always moves it.
+constexpr float kMFloor = -1.0e30f;
 
 template <int NHB>
 struct AttnState {
@@ -309,8 +315,8 @@ __device__ __forceinline__ void pv_mfma2(const PvFrags& f, AttnState<2>& st) {
     }
 }
 
-// Scores of the freshly staged chunk -> log2-domain s (invalid rows -inf), this wave's
-// per-head maxima into `red`, probabilities against the current reference into
+// Scores of the freshly staged chunk -> s (raw q.k, invalid rows -inf), this wave's
+// per-head maxima (log2 domain) into `red`, probabilities against the current reference into
 // `ptile` (clamped at 2^kPLimit; a chunk that needs more is recomputed after the
 // barrier), and their per-lane sums into psum.
 template <int NHB>
@@ -322,23 +328,17 @@ __device__ __forceinline__ void softmax_local(__bf16 (*__restrict__ ptile)[kPStr
                                               int l16, int g) {
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = (vmask >> (4 * g + i)) & 1;
-      s[hb][i] = ok ? sacc[hb][i] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[hb][i]);
-    }
+    for (int i = 0; i < 4; ++i) s[hb][i] = ((vmask >> (4 * g + i)) & 1) ? sacc[hb][i] : -INFINITY;
+    float mx = fmaxf(fmaxf(s[hb][0], s[hb][1]), fmaxf(s[hb][2], s[hb][3]));
     mx = max_xor32(max_xor16(mx));
-    if (g == 0) red[w][16 * hb + l16] = mx;
-    const float mr = st.m_run[hb];
+    if (g == 0) red[w][16 * hb + l16] = mx * scale_log2;
+    const float nmr = -st.m_run[hb];
     float p[4];
-    psum[hb] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = (s[hb][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(fminf(s[hb][i] - mr, kPLimit));
-      psum[hb] += p[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      p[i] = __builtin_amdgcn_exp2f(fminf(__builtin_fmaf(s[hb][i], scale_log2, nmr), kPLimit));
+    psum[hb] = (p[0] + p[1]) + (p[2] + p[3]);
     *reinterpret_cast<uint2*>(&ptile[16 * hb + l16][16 * w + 4 * g]) =
         make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
   }
@@ -353,7 +353,8 @@ template <int NHB>
 __device__ __forceinline__ void resolve_chunk(__bf16 (*__restrict__ ptile)[kPStride],
                                               const float (*__restrict__ red)[16 * NHB],
                                               AttnState<NHB>& st, const float (&s)[NHB][4],
-                                              float (&psum)[NHB], int w, int l16, int g) {
+                                              float scale_log2, float (&psum)[NHB], int w, int l16,
+                                              int g) {
   float cm[NHB];
   bool fix = false;
 #pragma unroll
@@ -367,16 +368,14 @@ __device__ __forceinline__ void resolve_chunk(__bf16 (*__restrict__ ptile)[kPStr
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       const float mn = fmaxf(st.m_run[hb], cm[hb]);
-      alpha[hb] = (mn == st.m_run[hb]) ? 1.f : __builtin_amdgcn_exp2f(st.m_run[hb] - mn);
+      alpha[hb] = __builtin_amdgcn_exp2f(st.m_run[hb] - mn);
       st.m_run[hb] = mn;
       st.l_part[hb] *= alpha[hb];
       float p[4];
-      psum[hb] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = (s[hb][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(fminf(s[hb][i] - mn, kPLimit));
-        psum[hb] += p[i];
-      }
+      for (int i = 0; i < 4; ++i)
+        p[i] = __builtin_amdgcn_exp2f(fminf(__builtin_fmaf(s[hb][i], scale_log2, -mn), kPLimit));
+      psum[hb] = (p[0] + p[1]) + (p[2] + p[3]);
       *reinterpret_cast<uint2*>(&ptile[16 * hb + l16][16 * w + 4 * g]) =
           make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
     }
@@ -406,6 +405,7 @@ __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnSt
                                                float scale_log2) {
   const int l16 = lane & 15, g = lane >> 4;
   const int nb = cb ^ 1;
+  const int64_t next_slot = idx_at(sm.idx, pf_jj, n_blk);  // read early: off the LDS queue
   f32x4 sacc[NHB];
   float s[NHB][4], psum[NHB];
   if constexpr (NHB == 2) {
@@ -415,18 +415,18 @@ __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnSt
     PvFrags f;
     pv_reads2(&sm.v[cb][0][0], sm.p[cb], f, w, lane);
     const uint64_t vmask = __ballot(raw.valid);  // bit j (j < 16) = row 16w + j valid
-    load_raw(raw, cache, num_slots, sm.idx, pf_jj, n_blk, g);
+    load_raw_slot(raw, cache, num_slots, next_slot, g);
     softmax_local<NHB>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
     pv_mfma2(f, st);
   } else {
     stage_chunk<NHB>(&sm.v[nb][0][0], raw, st, sacc, w, l16, g);
     pv_chunk<NHB>(&sm.v[cb][0][0], sm.p[cb], st, w, lane);
     const uint64_t vmask = __ballot(raw.valid);
-    load_raw(raw, cache, num_slots, sm.idx, pf_jj, n_blk, g);
+    load_raw_slot(raw, cache, num_slots, next_slot, g);
     softmax_local<NHB>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
   }
   __syncthreads();
-  resolve_chunk<NHB>(sm.p[nb], sm.red[nb], st, s, psum, w, l16, g);
+  resolve_chunk<NHB>(sm.p[nb], sm.red[nb], st, s, scale_log2, psum, w, l16, g);
 }
 
 // The block's last chunk: P.V only.
@@ -482,7 +482,7 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     }
     st.qf[hb][16] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kNope + 8 * g));
     st.qf[hb][17] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kNope + 32 + 8 * g));
-    st.m_run[hb] = -INFINITY;
+    st.m_run[hb] = kMFloor;
     st.l_part[hb] = 0.f;
   }
 #pragma unroll
@@ -504,8 +504,8 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     __syncthreads();
     const int nch = (n_blk + kChunk - 1) / kChunk;
     RawSlot A, B;
-    load_raw(A, cache, num_slots, sm.idx, row, n_blk, g);
-    load_raw(B, cache, num_slots, sm.idx, kChunk + row, n_blk, g);
+    load_raw_slot(A, cache, num_slots, idx_at(sm.idx, row, n_blk), g);
+    load_raw_slot(B, cache, num_slots, idx_at(sm.idx, kChunk + row, n_blk), g);
     {  // prologue: stage chunk 0 and settle its probabilities
       f32x4 sacc[NHB];
       if constexpr (NHB == 2)
@@ -513,11 +513,11 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
       else
         stage_chunk<NHB>(&sm.v[0][0][0], A, st, sacc, w, l16, g);
       const uint64_t vmask = __ballot(A.valid);
-      load_raw(A, cache, num_slots, sm.idx, 2 * kChunk + row, n_blk, g);
+      load_raw_slot(A, cache, num_slots, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
       float s[NHB][4], psum[NHB];
       softmax_local<NHB>(sm.p[0], sm.red[0], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
       __syncthreads();
-      resolve_chunk<NHB>(sm.p[0], sm.red[0], st, s, psum, w, l16, g);
+      resolve_chunk<NHB>(sm.p[0], sm.red[0], st, s, scale_log2, psum, w, l16, g);
     }
     int i = 0;
     for (; i + 2 < nch; i += 2) {
@@ -549,7 +549,7 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   const float mr = (NHB == 2 && (g & 1)) ? st.m_run[NHB - 1] : st.m_run[0];
   const float z2 = sinks ? sinks[h] * kLog2e : -INFINITY;
   const float M = fmaxf(mr, z2);
-  const float f = (mr == -INFINITY) ? 0.f : exp2f(mr - M);
+  const float f = exp2f(mr - M);
   const float den = lt * f + ((z2 == -INFINITY) ? 0.f : exp2f(z2 - M));
   const float inv = den > 0.f ? f / den : 0.f;
   uint16_t* orow = out + ((int64_t)t * H + h) * kNope;
