@@ -82,6 +82,25 @@ __device__ __forceinline__ int64_t idx_at(const int32_t* idx_lds, int jj, int n_
   return jj < n_blk ? (int64_t)idx_lds[jj] : -1;
 }
 
+// Where this lane's pieces of a slot's record live (the zero page for an invalid slot).
+struct RecPtr {
+  const uint8_t* np;  // value codes, already offset by 16g
+  const uint8_t* rp;  // rope, already offset by 16g
+  const uint8_t* sp;  // scale bytes
+  int valid;
+};
+__device__ __forceinline__ RecPtr rec_ptr(const uint8_t* __restrict__ cache, int64_t num_slots,
+                                          int64_t slot, int g) {
+  RecPtr p;
+  p.valid = (slot >= 0 && slot < num_slots) ? 1 : 0;
+  const uint8_t* base = p.valid ? cache + page_base(slot >> 6) : g_zero_page;
+  const int off = p.valid ? (int)(slot & (kPage - 1)) : 0;
+  p.np = base + nope_off(off) + 16 * g;
+  p.rp = base + rope_off(off) + 16 * g;
+  p.sp = base + scale_off(off);
+  return p;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -230,7 +249,12 @@ __device__ __forceinline__ void pv_chunk(const __bf16* __restrict__ vtile,
 
 // Staging of one chunk: dequantise this lane's slot (row 16w + l16, k-group g), write its
 // value dims into `vn`, S^T fragments into sacc (two accumulator chains per head block).
-__device__ __forceinline__ void stage2(__bf16* __restrict__ vn, const RawSlot& cur,
+// If REFILL, each piece of `cur` is re-requested for the chunk at `nxt` as soon as it has
+// been converted, so the record loads of a chunk go out one by one across the staging
+// work instead of as one burst: a burst fills the memory pipeline's queue and stalls
+// the wave's in-order issue until it drains.
+template <bool REFILL>
+__device__ __forceinline__ void stage2(__bf16* __restrict__ vn, RawSlot& cur, const RecPtr& nxt,
                                        const AttnState<2>& st, f32x4 (&sacc)[2], int w,
                                        int lane) {
   const int l16 = lane & 15, g = lane >> 4;
@@ -255,6 +279,7 @@ __device__ __forceinline__ void stage2(__bf16* __restrict__ vn, const RawSlot& c
     const float scale = e8m0_as_scale(sbyte);
     const bf16x8 k0 = dequant8(cur.nope[u].x, cur.nope[u].y, scale);
     const bf16x8 k1 = dequant8(cur.nope[u].z, cur.nope[u].w, scale);
+    if constexpr (REFILL) cur.nope[u] = *reinterpret_cast<const uint4*>(nxt.np + 64 * u);
     *reinterpret_cast<bf16x8*>(wb[u & 1][0] + 64 * u) = k0;
     *reinterpret_cast<bf16x8*>(wb[u & 1][1] + 64 * u) = k1;
 #pragma unroll
@@ -265,6 +290,12 @@ __device__ __forceinline__ void stage2(__bf16* __restrict__ vn, const RawSlot& c
   }
   const bf16x8 k16 = as_bf16x8(cur.rope[0]);
   const bf16x8 k17 = as_bf16x8(cur.rope[1]);
+  if constexpr (REFILL) {
+    cur.rope[0] = *reinterpret_cast<const uint4*>(nxt.rp);
+    cur.rope[1] = *reinterpret_cast<const uint4*>(nxt.rp + 64);
+    cur.sc = *reinterpret_cast<const uint2*>(nxt.sp);
+    cur.valid = nxt.valid;
+  }
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     sa[hb] = mfma16(k16, st.qf[hb][16], sa[hb]);
@@ -411,11 +442,11 @@ __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnSt
   if constexpr (NHB == 2) {
     // staging + S first, so the scores are ready by the softmax; the P.V operands are
     // requested next and consumed last, so their MFMAs run across the barrier.
-    stage2(&sm.v[nb][0][0], raw, st, sacc, w, lane);
+    const uint64_t vmask = __ballot(raw.valid);  // bit j (j < 16) = row 16w + j valid
+    const RecPtr nxt = rec_ptr(cache, num_slots, next_slot, g);
+    stage2<true>(&sm.v[nb][0][0], raw, nxt, st, sacc, w, lane);
     PvFrags f;
     pv_reads2(&sm.v[cb][0][0], sm.p[cb], f, w, lane);
-    const uint64_t vmask = __ballot(raw.valid);  // bit j (j < 16) = row 16w + j valid
-    load_raw_slot(raw, cache, num_slots, next_slot, g);
     softmax_local<NHB>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
     pv_mfma2(f, st);
   } else {
@@ -508,12 +539,14 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     load_raw_slot(B, cache, num_slots, idx_at(sm.idx, kChunk + row, n_blk), g);
     {  // prologue: stage chunk 0 and settle its probabilities
       f32x4 sacc[NHB];
-      if constexpr (NHB == 2)
-        stage2(&sm.v[0][0][0], A, st, sacc, w, lane);
-      else
-        stage_chunk<NHB>(&sm.v[0][0][0], A, st, sacc, w, l16, g);
       const uint64_t vmask = __ballot(A.valid);
-      load_raw_slot(A, cache, num_slots, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
+      if constexpr (NHB == 2) {
+        const RecPtr nxt = rec_ptr(cache, num_slots, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
+        stage2<true>(&sm.v[0][0][0], A, nxt, st, sacc, w, lane);
+      } else {
+        stage_chunk<NHB>(&sm.v[0][0][0], A, st, sacc, w, l16, g);
+        load_raw_slot(A, cache, num_slots, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
+      }
       float s[NHB][4], psum[NHB];
       softmax_local<NHB>(sm.p[0], sm.red[0], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
       __syncthreads();
