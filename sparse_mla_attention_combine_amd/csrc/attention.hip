@@ -10,23 +10,27 @@
 //   The head groups of a token get block ids with the same value mod 8, so they run on
 //   the same XCD and the three later gathers of each slot hit that XCD's L2.
 //   The listed slots are consumed in chunks of 64; wave w owns rows 16w..16w+15.
-// Per chunk:
-//   1. every lane holds its slot's 128 nope bytes, 32 rope bytes and 8 scale bytes in
-//      registers (requested two chunks ahead, as soon as the buffer is consumed; the
-//      token's index row is staged in LDS first and every load is branch-free, so the
-//      wait before a chunk covers exactly that chunk), converts them with gfx950's scaled
-//      FP8->bf16 instruction (exact: a power-of-two scale) into MFMA A-fragments, and
-//      stages the 512 value dims as bf16 rows in an XOR-swizzled LDS tile;
-//   2. S^T = K Q^T on bf16 MFMA 16x16x32 (Q^T fragments live in registers for the whole
-//      kernel);
-//   3. online softmax in the log2 domain: per-wave maxima through lane swaps
-//      (permlane16/32), the chunk maximum across the 4 waves through LDS; the reference
-//      maximum only moves (and O is rescaled) when a chunk beats it by more than 2^8;
-//      probabilities are rounded to bf16 into LDS;
-//   4. O^T += V^T P^T on bf16 MFMA 16x16x32: wave w owns output dims 128w..128w+127 for
-//      all NH heads; V^T fragments come from the row-major LDS tile through gfx950's
-//      transposing LDS read (ds_read_b64_tr_b16), P^T fragments are plain 16 B reads.
-//   LDS buffers are double-buffered so chunk i+1's staging overlaps chunk i's P.V.
+// Per chunk of 64 listed slots (a software pipeline: chunk i's P.V runs in the same step
+// as chunk i+1's staging, with one workgroup barrier per chunk):
+//   1. every lane holds its slot's 128 code bytes, 32 rope bytes and 8 scale bytes in
+//      registers (the token's index row is staged in LDS, every load is branch-free, and
+//      each piece is re-requested for the chunk two ahead right after it is converted, so
+//      the loads leave one by one instead of as a burst that would stall in-order issue),
+//      converts them with gfx950's scaled FP8->bf16 instruction (exact: a power-of-two
+//      scale) into MFMA fragments, and stages the 512 value dims as bf16 rows in an
+//      XOR-swizzled, double-buffered LDS tile;
+//   2. S^T = K Q^T on bf16 MFMA 16x16x32 (Q^T fragments live in registers);
+//   3. softmax in the log2 domain against a per-head reference maximum that all waves
+//      share: probabilities exp2(s - ref) (up to 2^20) are rounded to bf16 into LDS and
+//      each wave's chunk maxima (permlane16/32 swaps) go to LDS; after the barrier the
+//      maxima are compared with the reference, and only when a chunk beats it by more
+//      than 2^20 (always for the first chunk with a valid row) does the workgroup move
+//      the reference, rescale O and the denominator, and rewrite that chunk's
+//      probabilities behind one more barrier;
+//   4. O^T += V^T P^T on bf16 MFMA 32x32x16: wave w owns output dims 128mb + 32w (mb =
+//      0..3) for all NH heads; V^T fragments come from the row-major LDS tile through
+//      gfx950's transposing LDS read (ds_read_b64_tr_b16), P^T fragments are plain 16 B
+//      reads; these MFMAs are issued after the softmax and run across the barrier.
 // Numerics: bf16 operands, fp32 accumulation and softmax, P rounded to bf16 for P.V;
 // the per-head sink enters only the final denominator.
 #include "device.hpp"
