@@ -74,6 +74,12 @@ def parse():
     ap.add_argument("--instances", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--batch", type=int, default=64,
+                    help="decode batch: the first B requests of the workload (default 64, the "
+                         "headline configuration; smaller batches exercise --splits)")
+    ap.add_argument("--splits", type=int, default=1,
+                    help="pieces per index row for dsv4_sparse_mla_decode_split (1 = the "
+                         "one-workgroup-per-(token, head group) decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device-to-device copy 3 times (the known-size "
                          "kernel that scales FETCH_SIZE / WRITE_SIZE counter readings)")
@@ -104,6 +110,15 @@ def main():
     torch.cuda.set_device(dev)
     t0 = time.time()
     wl = attention_workload(2, seed=args.seed, instances=args.instances)
+    if not 1 <= args.batch <= wl["T"]:
+        print(f"bench.py: --batch must be in 1..{wl['T']}", file=sys.stderr)
+        sys.exit(2)
+    if args.batch < wl["T"]:  # the first B requests (one query token each)
+        B = args.batch
+        wl["qsl"], wl["seq_lens"] = wl["qsl"][:B + 1], wl["seq_lens"][:B]
+        wl["block_table"], wl["B"], wl["T"] = wl["block_table"][:B], B, B
+        for it in wl["instances"]:
+            it["q"], it["topk"], it["topk_lens"] = it["q"][:B], it["topk"][:B], it["topk_lens"][:B]
     T, H, W = wl["T"], wl["H"], wl["W"]
     npg = wl["num_pages"]
     log(f"[bench] workload generated in {time.time() - t0:.1f}s: T={T} H={H} W={W} "
@@ -142,6 +157,9 @@ def main():
     torch.cuda.synchronize()
 
     lib = dsv4.library()
+    splits = args.splits
+    ws_bytes = lib.dsv4_sparse_mla_split_workspace_bytes(T, H, splits) if splits > 1 else 0
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     P = ctypes.c_void_p
@@ -158,12 +176,16 @@ def main():
                 P(d["comb"].data_ptr()), W, P(d["lens"].data_ptr()), sp)
         dec = (P(d["q"].data_ptr()), P(cache.data_ptr()), npg, 64, P(d["comb"].data_ptr()), W,
                P(d["lens"].data_ptr()), P(d["sinks"].data_ptr()),
-               ctypes.c_float(wl["softmax_scale"]), P(d["out"].data_ptr()), None, T, H, sp)
+               ctypes.c_float(wl["softmax_scale"]), P(d["out"].data_ptr()), None, T, H)
+        dec = dec + ((splits, P(workspace.data_ptr()), ctypes.c_size_t(ws_bytes), sp) if splits > 1
+                     else (sp,))
         calls.append((ins, comb, dec))
 
     def check(st):
         if st != 0:
             raise RuntimeError(lib.dsv4_last_error().decode())
+
+    decode_fn = lib.dsv4_sparse_mla_decode_split if splits > 1 else lib.dsv4_sparse_mla_decode
 
     def with_stream(args_tuple, stream_ptr):
         return args_tuple[:-1] + (stream_ptr,)
@@ -189,7 +211,7 @@ def main():
         if timed_idx is None:
             check(lib.dsv4_kv_insert(*ins))
             check(lib.dsv4_combine_indices(*comb))
-            check(lib.dsv4_sparse_mla_decode(*dec))
+            check(decode_fn(*dec))
             return
         e = ev[6 * timed_idx:6 * timed_idx + 6]
         e[0].record(stream)
@@ -199,7 +221,7 @@ def main():
         check(lib.dsv4_combine_indices(*comb))
         e[3].record(stream)
         e[4].record(stream)
-        check(lib.dsv4_sparse_mla_decode(*dec))
+        check(decode_fn(*dec))
         e[5].record(stream)
 
     for i in range(args.warmup):
@@ -215,7 +237,7 @@ def main():
             csp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
             check(lib.dsv4_kv_insert(*with_stream(ins, csp)))
             check(lib.dsv4_combine_indices(*with_stream(comb, csp)))
-            check(lib.dsv4_sparse_mla_decode(*with_stream(dec, csp)))
+            check(decode_fn(*with_stream(dec, csp)))
         graphs.append(g)
     torch.cuda.synchronize()
     for i in range(args.warmup):
@@ -280,6 +302,7 @@ def main():
             "window": wl["window"], "combined_width": W, "context": int(wl["seq_lens"][0]),
             "page_size": 64, "latent_dim": LATENT, "value_dim": NOPE, "sinks": True,
             "instances_rotated": n_inst, "cache": "FP8 e4m3 nope + UE8M0 scales + bf16 rope",
+            **({"decode_splits": splits} if splits > 1 else {}),
         },
         "roofline": {
             "bound": bound,
@@ -288,8 +311,9 @@ def main():
             "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
             "frac": round((achieved_tflops / PEAK_BF16_TFLOPS) if bound == "mfma"
                           else (achieved_gbs / PEAK_HBM_GBS), 4),
-            "traffic": measured_traffic(),
-            "kernel": "sparse_mla_kernel<2> (dsv4_sparse_mla_decode)",
+            "traffic": measured_traffic() if (splits == 1 and T == 64) else None,
+            "kernel": ("sparse_mla_kernel<2> + split_merge_kernel (dsv4_sparse_mla_decode_split)"
+                       if splits > 1 else "sparse_mla_kernel<2> (dsv4_sparse_mla_decode)"),
             "launch_us": round(dec_s * 1e6, 2),
             "alg_flops": flops, "alg_bytes": bytes_alg,
             "hbm_frac": round(achieved_gbs / PEAK_HBM_GBS, 4),

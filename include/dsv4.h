@@ -69,6 +69,7 @@ typedef enum {
   DSV4_ERR_SHAPE = 2,       /* a size or stride is negative or inconsistent       */
   DSV4_ERR_ALIGN = 3,       /* a pointer is not aligned as documented             */
   DSV4_ERR_UNSUPPORTED = 4, /* a valid but unsupported configuration (H, P, ...)  */
+  DSV4_ERR_WORKSPACE = 5,   /* the caller's workspace is missing or too small     */
   DSV4_ERR_HIP = 6          /* the HIP runtime reported an error at launch        */
 } dsv4_status;
 
@@ -181,6 +182,40 @@ int dsv4_sparse_mla_prefill(const void* q, const uint8_t* kv_cache, int num_page
                             int page_size, const int32_t* indices, int idx_stride,
                             const int32_t* lens, const float* sinks, float softmax_scale,
                             void* out, float* lse, int T, int H, void* stream);
+
+/*
+ * dsv4_sparse_mla_split_workspace_bytes — bytes of device workspace that
+ * dsv4_sparse_mla_decode_split needs for T query tokens, H heads and `splits` pieces per
+ * row: T * splits * H * 514 * 4 (fp32 partial outputs, maxima and denominators).
+ * Returns 0 for a negative argument.
+ */
+size_t dsv4_sparse_mla_split_workspace_bytes(int T, int H, int splits);
+
+/*
+ * dsv4_sparse_mla_decode_split — the result of dsv4_sparse_mla_decode for batches too
+ * small to fill the GPU, where one workgroup per (token, head group) leaves most compute
+ * units idle [p4 forward_mqa: decode returns (output, None) where an lse would go; the
+ * lse output makes the pieces mergeable].  Each token's row is cut into `splits`
+ * contiguous pieces of a multiple of 64 entries; every (token, head group, piece) runs as
+ * its own workgroup and leaves, per head, the unnormalised output, its reference maximum
+ * and its denominator in `workspace`; a merge pass then forms
+ *   M = max(z, max_s m_s),  den = e^(z-M) + sum_s l_s e^(m_s-M),
+ *   out = sum_s O_s e^(m_s-M) / den,  lse = M + ln(den),
+ * which is the same result as the unsplit call up to rounding order.
+ *   Arguments as dsv4_sparse_mla_decode, plus
+ *   splits     1..64 (1 runs the unsplit path and needs no workspace);
+ *   workspace  caller-owned device memory of at least
+ *              dsv4_sparse_mla_split_workspace_bytes(T, H, splits) bytes, 16-byte
+ *              aligned; overwritten by the call; calls that share one workspace on
+ *              different streams race.
+ * Errors: DSV4_ERR_SHAPE for splits outside 1..64, DSV4_ERR_WORKSPACE for a NULL,
+ * misaligned or too small workspace, and everything dsv4_sparse_mla_decode checks.
+ */
+int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num_pages,
+                                 int page_size, const int32_t* indices, int idx_stride,
+                                 const int32_t* lens, const float* sinks, float softmax_scale,
+                                 void* out, float* lse, int T, int H, int splits,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dsv4_gather_dequant — gather + dequantise slots into bf16 rows [p2 Key source

@@ -37,13 +37,17 @@ _attn_args = [_vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _i32, _
 _lib.dsv4_sparse_mla_decode.argtypes = _attn_args
 _lib.dsv4_sparse_mla_prefill.argtypes = _attn_args
 _lib.dsv4_gather_dequant.argtypes = [_vp, _i32, _i32, _vp, _i32, _vp, _vp]
+_lib.dsv4_sparse_mla_split_workspace_bytes.argtypes = [_i32, _i32, _i32]
+_lib.dsv4_sparse_mla_split_workspace_bytes.restype = ctypes.c_size_t
+_lib.dsv4_sparse_mla_decode_split.argtypes = _attn_args[:-1] + [_i32, _vp, ctypes.c_size_t, _vp]
 for _f in (_lib.dsv4_kv_insert, _lib.dsv4_combine_indices, _lib.dsv4_sparse_mla_decode,
-           _lib.dsv4_sparse_mla_prefill, _lib.dsv4_gather_dequant):
+           _lib.dsv4_sparse_mla_prefill, _lib.dsv4_gather_dequant, _lib.dsv4_sparse_mla_decode_split):
     _f.restype = _i32
 
 EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4_kv_insert",
             "dsv4_combine_indices", "dsv4_sparse_mla_decode", "dsv4_sparse_mla_prefill",
-            "dsv4_gather_dequant"]
+            "dsv4_gather_dequant", "dsv4_sparse_mla_split_workspace_bytes",
+            "dsv4_sparse_mla_decode_split"]
 
 
 class Dsv4Error(RuntimeError):
@@ -153,6 +157,30 @@ def dsv4_sparse_mla_prefill(q, kv_cache, indices, lens, sinks, softmax_scale, ou
     """Same contract as dsv4_sparse_mla_decode, scheduled for many query tokens."""
     return _attention(_lib.dsv4_sparse_mla_prefill, q, kv_cache, indices, lens, sinks,
                       softmax_scale, out, lse, page_size, stream)
+
+
+def split_workspace_bytes(T, H, splits):
+    """Device workspace bytes dsv4_sparse_mla_decode_split needs."""
+    return int(_lib.dsv4_sparse_mla_split_workspace_bytes(T, H, splits))
+
+
+def dsv4_sparse_mla_decode_split(q, kv_cache, indices, lens, sinks, softmax_scale, out, splits,
+                                 workspace, lse=None, page_size=64, stream=None):
+    """dsv4_sparse_mla_decode with each token's row cut into `splits` pieces merged by
+    their lse; workspace: a caller-owned device tensor of at least
+    split_workspace_bytes(T, H, splits) bytes (16-byte aligned)."""
+    _want(q, torch.bfloat16, "q"), _want(kv_cache, torch.uint8, "kv_cache")
+    _want(indices, torch.int32, "indices"), _want(lens, torch.int32, "lens")
+    _want(sinks, torch.float32, "sinks"), _want(out, torch.bfloat16, "out")
+    _want(lse, torch.float32, "lse")
+    T, H = q.shape[0], q.shape[1]
+    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.dsv4_sparse_mla_decode_split(
+        _ptr(q), _ptr(kv_cache), num_pages, page_size, _ptr(indices), indices.shape[1], _ptr(lens),
+        _ptr(sinks), float(softmax_scale), _ptr(out), _ptr(lse), T, H, int(splits), _ptr(workspace),
+        ws_bytes, _stream(stream)))
+    return out
 
 
 def dsv4_gather_dequant(kv_cache, slots, out, page_size=64, stream=None):

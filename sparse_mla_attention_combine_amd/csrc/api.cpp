@@ -77,6 +77,7 @@ const char* dsv4_status_str(int status) {
     case DSV4_ERR_SHAPE: return "DSV4_ERR_SHAPE";
     case DSV4_ERR_ALIGN: return "DSV4_ERR_ALIGN";
     case DSV4_ERR_UNSUPPORTED: return "DSV4_ERR_UNSUPPORTED";
+    case DSV4_ERR_WORKSPACE: return "DSV4_ERR_WORKSPACE";
     case DSV4_ERR_HIP: return "DSV4_ERR_HIP";
     default: return "DSV4_UNKNOWN_STATUS";
   }
@@ -152,6 +153,39 @@ int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages
   return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, indices, idx_stride, lens, sinks,
                                            softmax_scale, out, lse, T, H, false,
                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t dsv4_sparse_mla_split_workspace_bytes(int T, int H, int splits) {
+  if (T < 0 || H < 0 || splits < 0) return 0;
+  return dsv4::split_workspace_bytes(T, H, splits);
+}
+
+int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num_pages,
+                                 int page_size, const int32_t* indices, int idx_stride,
+                                 const int32_t* lens, const float* sinks, float softmax_scale,
+                                 void* out, float* lse, int T, int H, int splits,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "dsv4_sparse_mla_decode_split";
+  int st = check_attention(fn, q, kv_cache, num_pages, page_size, indices, idx_stride, lens, sinks,
+                           softmax_scale, out, T, H);
+  if (st) return st;
+  if (splits < 1 || splits > 64) return fail(DSV4_ERR_SHAPE, "%s: splits %d not in 1..64", fn, splits);
+  if (T == 0) return ok();
+  if (splits == 1)
+    return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, indices, idx_stride, lens,
+                                             sinks, softmax_scale, out, lse, T, H, false,
+                                             static_cast<hipStream_t>(stream)),
+                      fn);
+  if ((int64_t)T * splits >= ((int64_t)1 << 31) / 8)
+    return fail(DSV4_ERR_SHAPE, "%s: T * splits = %lld too large", fn, (long long)T * splits);
+  const size_t need = dsv4::split_workspace_bytes(T, H, splits);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
+    return fail(DSV4_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned and hold %zu bytes (got %zu%s)",
+                fn, need, workspace_bytes, workspace ? "" : ", NULL");
+  return hip_status(dsv4::launch_attention_split(q, kv_cache, num_pages, indices, idx_stride, lens,
+                                                 sinks, softmax_scale, out, lse, T, H, splits,
+                                                 workspace, static_cast<hipStream_t>(stream)),
                     fn);
 }
 

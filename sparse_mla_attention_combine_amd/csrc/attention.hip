@@ -482,19 +482,22 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int64_t num_slots,
     const int32_t* __restrict__ indices, int idx_stride, const int32_t* __restrict__ lens,
     const float* __restrict__ sinks, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int T, int H, int groups) {
+    float* __restrict__ lse, int T, int H, int groups, int splits, int split_len,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ AttnSmem<NHB> sm;
 
-  int t, hg;
+  // work item vt = (query token, split); with one split it is the query token
+  int vt, hg;
   if (groups == 1) {
-    t = blockIdx.x;
+    vt = blockIdx.x;
     hg = 0;
   } else {
     const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
     hg = k % groups;
-    t = (k / groups) * 8 + x;
+    vt = (k / groups) * 8 + x;
   }
-  if (t >= T) return;
+  if (vt >= T * splits) return;
+  const int t = vt / splits, sp = vt - t * splits;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -503,6 +506,9 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   n = n < idx_stride ? n : idx_stride;
   n = n > 0 ? n : 0;
   const int32_t* idx_row = indices + (int64_t)t * idx_stride;
+  // this work item's entries [beg, end) of the row
+  const int beg = min(n, sp * split_len);
+  const int end = min(n, beg + split_len);
 
   AttnState<NHB> st;
   // Q^T fragments: lane (head l16 of block hb, k-group g); k-step s pairs with the
@@ -531,8 +537,8 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   // in register buffer c&1 and LDS tiles c&1; a buffer is refilled with chunk c+2 as
   // soon as staging has consumed it, so two chunks of records are always in flight.
   const int row = 16 * w + l16;
-  for (int blk0 = 0; blk0 < n; blk0 += kIdxBlock) {
-    const int n_blk = min(n - blk0, kIdxBlock);
+  for (int blk0 = beg; blk0 < end; blk0 += kIdxBlock) {
+    const int n_blk = min(end - blk0, kIdxBlock);
     __syncthreads();  // the previous block's entries and tiles are no longer read
 #pragma unroll 4
     for (int i = tid; i < n_blk; i += 256) sm.idx[i] = idx_row[blk0 + i];
@@ -584,6 +590,31 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   const int h = h0 + hl;
   const float lt = sm.lsum[0][hl] + sm.lsum[1][hl] + sm.lsum[2][hl] + sm.lsum[3][hl];
   const float mr = (NHB == 2 && (g & 1)) ? st.m_run[NHB - 1] : st.m_run[0];
+  if (part_o) {
+    // one split of a row: the unnormalised O (relative to the reference mr), mr and the
+    // denominator go to the workspace; the merge pass adds the sink and normalises
+    float* po = part_o + ((int64_t)vt * H + h) * kNope;
+    if constexpr (NHB == 2) {
+      const int hi = lane >> 5;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x16& o = st.o32[mb];
+          *reinterpret_cast<float4*>(po + 128 * mb + 32 * w + 8 * qd + 4 * hi) =
+              make_float4(o[4 * qd], o[4 * qd + 1], o[4 * qd + 2], o[4 * qd + 3]);
+        }
+      if (w == 0 && hi == 0) *reinterpret_cast<float2*>(part_ml + ((int64_t)vt * H + h) * 2) = make_float2(mr, lt);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const f32x4 o = st.o16[mb];
+        *reinterpret_cast<float4*>(po + 128 * w + 16 * mb + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+      if (w == 0 && g == 0) *reinterpret_cast<float2*>(part_ml + ((int64_t)vt * H + h) * 2) = make_float2(mr, lt);
+    }
+    return;
+  }
   const float z2 = sinks ? sinks[h] * kLog2e : -INFINITY;
   const float M = fmaxf(mr, z2);
   const float f = exp2f(mr - M);
@@ -615,25 +646,99 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   }
 }
 
+// Merge of the split partials of a row (LSE merge): with per-split reference maxima m_s
+// (log2 domain), denominators l_s and unnormalised outputs O_s, and the sink z,
+//   M = max(z, max_s m_s),  den = 2^(z-M) + sum_s l_s 2^(m_s-M),
+//   out = sum_s O_s 2^(m_s-M) / den,  lse = (M + log2 den) ln 2.
+// One wave per (token, head); lane l owns output dims 8l..8l+7.
+__global__ void __launch_bounds__(256) split_merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const float* __restrict__ sinks, uint16_t* __restrict__ out, float* __restrict__ lse, int T,
+    int H, int splits) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * H + h
+  if (row >= (int64_t)T * H) return;
+  const int t = (int)(row / H), h = (int)(row - (int64_t)t * H);
+  const float z2 = sinks ? sinks[h] * kLog2e : -INFINITY;
+  float M = z2;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(((int64_t)t * splits + s) * H + h) * 2]);
+  float den = (z2 == -INFINITY) ? 0.f : exp2f(z2 - M);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < splits; ++s) {
+    const int64_t pr = ((int64_t)t * splits + s) * H + h;
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + pr * 2);
+    const float wgt = exp2f(ml.x - M);
+    den += ml.y * wgt;
+    const float4 a = *reinterpret_cast<const float4*>(part_o + pr * kNope + 8 * lane);
+    const float4 b = *reinterpret_cast<const float4*>(part_o + pr * kNope + 8 * lane + 4);
+    acc[0] += a.x * wgt; acc[1] += a.y * wgt; acc[2] += a.z * wgt; acc[3] += a.w * wgt;
+    acc[4] += b.x * wgt; acc[5] += b.y * wgt; acc[6] += b.z * wgt; acc[7] += b.w * wgt;
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  uint4 v;
+  v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  v.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  v.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *reinterpret_cast<uint4*>(out + row * kNope + 8 * lane) = v;
+  if (lse && lane == 0) lse[row] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+}
+
+size_t split_workspace_bytes(int T, int H, int splits) {
+  return (size_t)T * splits * H * (kNope + 2) * sizeof(float);
+}
+
+static hipError_t launch_items(const void* q, const uint8_t* cache, int num_pages,
+                               const int32_t* indices, int idx_stride, const int32_t* lens,
+                               const float* sinks, float softmax_scale, void* out, float* lse,
+                               int T, int H, int splits, int split_len, float* part_o,
+                               float* part_ml, hipStream_t stream) {
+  const int64_t num_slots = (int64_t)num_pages * kPage;
+  const float scale_log2 = softmax_scale * kLog2e;
+  const int items = T * splits;
+  if (H == 16) {
+    hipLaunchKernelGGL(sparse_mla_kernel<1>, dim3(items), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), cache, num_slots, indices, idx_stride, lens,
+                       sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, 1, splits,
+                       split_len, part_o, part_ml);
+  } else {
+    const int groups = H / 32;
+    const int grid = groups == 1 ? items : 8 * groups * ((items + 7) / 8);
+    hipLaunchKernelGGL(sparse_mla_kernel<2>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), cache, num_slots, indices, idx_stride, lens,
+                       sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, groups, splits,
+                       split_len, part_o, part_ml);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages,
                             const int32_t* indices, int idx_stride, const int32_t* lens,
                             const float* sinks, float softmax_scale, void* out, float* lse, int T,
                             int H, bool prefill, hipStream_t stream) {
   (void)prefill;  // one schedule serves both entry points for now
   if (T == 0) return hipSuccess;
-  const int64_t num_slots = (int64_t)num_pages * kPage;
-  const float scale_log2 = softmax_scale * kLog2e;
-  if (H == 16) {
-    hipLaunchKernelGGL(sparse_mla_kernel<1>, dim3(T), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), cache, num_slots, indices, idx_stride, lens,
-                       sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, 1);
-  } else {
-    const int groups = H / 32;
-    const int grid = groups == 1 ? T : 8 * groups * ((T + 7) / 8);
-    hipLaunchKernelGGL(sparse_mla_kernel<2>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), cache, num_slots, indices, idx_stride, lens,
-                       sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, groups);
-  }
+  const int whole = idx_stride > 0 ? idx_stride : 1;
+  return launch_items(q, cache, num_pages, indices, idx_stride, lens, sinks, softmax_scale, out,
+                      lse, T, H, 1, whole, nullptr, nullptr, stream);
+}
+
+hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_pages,
+                                  const int32_t* indices, int idx_stride, const int32_t* lens,
+                                  const float* sinks, float softmax_scale, void* out, float* lse,
+                                  int T, int H, int splits, void* workspace, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  // 64-entry-aligned pieces of the row; trailing pieces may be empty
+  const int per = (idx_stride + splits - 1) / splits;
+  const int split_len = per > 0 ? ((per + kChunk - 1) / kChunk) * kChunk : kChunk;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_ml = part_o + (size_t)T * splits * H * kNope;
+  hipError_t e = launch_items(q, cache, num_pages, indices, idx_stride, lens, sinks, softmax_scale,
+                              out, lse, T, H, splits, split_len, part_o, part_ml, stream);
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)T * H;
+  hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                     part_o, part_ml, sinks, static_cast<uint16_t*>(out), lse, T, H, splits);
   return hipGetLastError();
 }
 

@@ -25,4 +25,12 @@ hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages,
                             const float* sinks, float softmax_scale, void* out, float* lse,
                             int T, int H, bool prefill, hipStream_t stream);
 
+// Split-slot decode: the row of each token is cut into `splits` 64-aligned pieces whose
+// partials go to `workspace` (split_workspace_bytes(T, H, splits) bytes) and are merged.
+hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_pages,
+                                  const int32_t* indices, int idx_stride, const int32_t* lens,
+                                  const float* sinks, float softmax_scale, void* out, float* lse,
+                                  int T, int H, int splits, void* workspace, hipStream_t stream);
+size_t split_workspace_bytes(int T, int H, int splits);
+
 }  // namespace dsv4

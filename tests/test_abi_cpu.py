@@ -62,6 +62,33 @@ def test_attention_validation(dsv4):
         assert call(fn, T=0, q=None) == 0 and lib.dsv4_last_error() == b""
 
 
+def test_split_decode_validation(dsv4):
+    lib = dsv4.library()
+    keep, p = _fake()
+    need = lib.dsv4_sparse_mla_split_workspace_bytes(2, 16, 4)
+    assert need == 2 * 4 * 16 * 514 * 4
+    assert lib.dsv4_sparse_mla_split_workspace_bytes(-1, 16, 4) == 0
+
+    def call(**kw):
+        a = dict(q=p, cache=p, num_pages=4, page_size=64, idx=p, stride=128, lens=p, sinks=None,
+                 scale=0.04, out=p, lse=None, T=2, H=16, splits=4, ws=p, wsb=need)
+        a.update(kw)
+        return lib.dsv4_sparse_mla_decode_split(a["q"], a["cache"], a["num_pages"], a["page_size"],
+                                                a["idx"], a["stride"], a["lens"], a["sinks"],
+                                                a["scale"], a["out"], a["lse"], a["T"], a["H"],
+                                                a["splits"], a["ws"], a["wsb"], None)
+
+    assert call(splits=0) == 2 and b"splits 0" in lib.dsv4_last_error()
+    assert call(splits=65) == 2
+    assert call(ws=None) == 5 and b"workspace" in lib.dsv4_last_error()
+    assert call(wsb=need - 4) == 5
+    assert call(ws=ctypes.c_void_p(p.value + 4)) == 5
+    assert call(H=24) == 4
+    assert call(q=None) == 1
+    assert call(T=0, q=None) == 0
+    assert lib.dsv4_status_str(5) == b"DSV4_ERR_WORKSPACE"
+
+
 def test_combine_validation(dsv4):
     lib = dsv4.library()
     keep, p = _fake()
