@@ -86,6 +86,20 @@ __device__ __forceinline__ int64_t idx_at(const int32_t* idx_lds, int jj, int n_
   return jj < n_blk ? (int64_t)idx_lds[jj] : -1;
 }
 
+// Copies entries [0, n_win) of an index block into LDS with every load in flight before
+// the first wait: one memory latency per block instead of one per 256 entries.
+__device__ __forceinline__ void stage_idx(int32_t* dst, const int32_t* __restrict__ src, int n_win,
+                                          int tid) {
+  constexpr int kPer = kIdxBlock / 256;
+  int32_t v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    if (256 * k < n_win) v[k] = src[min(tid + 256 * k, n_win - 1)];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    if (tid + 256 * k < n_win) dst[tid + 256 * k] = v[k];
+}
+
 // Where this lane's pieces of a slot's record live (the zero page for an invalid slot).
 struct RecPtr {
   const uint8_t* np;  // value codes, already offset by 16g
@@ -502,13 +516,15 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int h0 = hg * 16 * NHB;
-  int n = lens[t];
-  n = n < idx_stride ? n : idx_stride;
-  n = n > 0 ? n : 0;
+  // The row length is read as a vector load issued next to the Q and index loads (the
+  // address is moved to VGPRs), so that its latency overlaps theirs.
+  uint64_t len_addr = reinterpret_cast<uint64_t>(lens + t);
+  asm volatile("" : "+v"(len_addr));
+  const int n_lens_v = *reinterpret_cast<const __attribute__((address_space(1))) int32_t*>(len_addr);
   const int32_t* idx_row = indices + (int64_t)t * idx_stride;
-  // this work item's entries [beg, end) of the row
-  const int beg = min(n, sp * split_len);
-  const int end = min(n, beg + split_len);
+  // this work item's piece [beg, lim) of the row, known before its length arrives
+  const int beg = (int64_t)sp * split_len < idx_stride ? sp * split_len : idx_stride;
+  const int lim = beg + min(split_len, idx_stride - beg);
 
   AttnState<NHB> st;
   // Q^T fragments: lane (head l16 of block hb, k-group g); k-step s pairs with the
@@ -536,13 +552,19 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   // Index blocks of up to 4096 entries are staged in LDS.  Inside a block chunk c lives
   // in register buffer c&1 and LDS tiles c&1; a buffer is refilled with chunk c+2 as
   // soon as staging has consumed it, so two chunks of records are always in flight.
+  // The first block is requested together with Q and the row length (entries past the
+  // length are staged but never used), so the prologue waits for memory only once.
+  stage_idx(sm.idx, idx_row + beg, min(lim - beg, kIdxBlock), tid);
+  __syncthreads();
+  const int end = min(max(__builtin_amdgcn_readfirstlane(n_lens_v), 0), lim);
   const int row = 16 * w + l16;
   for (int blk0 = beg; blk0 < end; blk0 += kIdxBlock) {
     const int n_blk = min(end - blk0, kIdxBlock);
-    __syncthreads();  // the previous block's entries and tiles are no longer read
-#pragma unroll 4
-    for (int i = tid; i < n_blk; i += 256) sm.idx[i] = idx_row[blk0 + i];
-    __syncthreads();
+    if (blk0 != beg) {
+      __syncthreads();  // the previous block's entries and tiles are no longer read
+      for (int i = tid; i < n_blk; i += 256) sm.idx[i] = idx_row[blk0 + i];
+      __syncthreads();
+    }
     const int nch = (n_blk + kChunk - 1) / kChunk;
     RawSlot A, B;
     load_raw_slot(A, cache, num_slots, idx_at(sm.idx, row, n_blk), g);
