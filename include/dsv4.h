@@ -21,7 +21,8 @@
  * KV cache byte layout (this library's own specification; the pages name the content
  * of a record but give no byte order, and disagree across architectures [p2 Motivation
  * vs p4 get_kv_cache_shape]).  The cache is an array of pages of P slots each
- * (P = page_size, only 64 is accepted).  Page p starts at byte p * P * 648 and holds
+ * (P = page_size: 32, 64 or 256 [p4 get_supported_kernel_block_sizes: 32 and 64 for one
+ * backend, 256 for the other]).  Page p starts at byte p * P * 648 and holds
  *     +0          nope codes  uint8 [P][512]   FP8 OCP E4M3 ("e4m3fn", max 448)
  *     +P*512      rope values bf16  [P][64]    stored already rotated
  *     +P*640      scale bytes uint8 [P][8]     UE8M0, one per 64 nope dims
@@ -107,7 +108,7 @@ size_t dsv4_cache_page_bytes(int page_size);
  *                  Duplicate slots: one of the writers wins (unspecified which).
  *   q_norm_weight bf16 [576], shared by all heads.
  *   kv_cache     uint8, num_pages pages in the layout above (16-byte aligned).
- * Supported: page_size == 64, H in 1..128, T >= 0 (T == 0 is a no-op).
+ * Supported: page_size in {32, 64, 256}, H in 1..128, T >= 0 (T == 0 is a no-op).
  * Alignment: q, kv, kv_cache 16-byte aligned.
  */
 int dsv4_kv_insert(void* q, const void* kv, const int64_t* positions,
@@ -164,7 +165,7 @@ int dsv4_combine_indices(const int32_t* topk, int topk_stride, int topk_width,
  *   q        bf16 [T][H][576];  out bf16 [T][H][512];  lse fp32 [T][H] or NULL
  *   indices  int32 [T][idx_stride];  lens int32 [T];  sinks fp32 [H] or NULL
  * Arithmetic: bf16 operands, fp32 accumulation, probabilities rounded to bf16 for the
- * value product.  Supported: H in {16, 32, 64, 128}, page_size == 64.
+ * value product.  Supported: H in {16, 32, 64, 128}, page_size in {32, 64, 256}.
  * Alignment: q, out, kv_cache 16-byte aligned; indices 4-byte aligned.
  */
 int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages,

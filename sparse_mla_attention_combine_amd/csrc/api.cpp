@@ -38,8 +38,8 @@ int hip_status(hipError_t e, const char* what) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int check_page(const char* fn, int page_size, int num_pages) {
-  if (page_size != 64)
-    return fail(DSV4_ERR_UNSUPPORTED, "%s: page_size %d not supported (only 64)", fn, page_size);
+  if (dsv4::page_shift_of(page_size) < 0)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: page_size %d not supported (32, 64 or 256)", fn, page_size);
   if (num_pages < 0) return fail(DSV4_ERR_SHAPE, "%s: num_pages %d < 0", fn, num_pages);
   if ((int64_t)num_pages * page_size >= ((int64_t)1 << 31))
     return fail(DSV4_ERR_SHAPE, "%s: num_pages * page_size exceeds the int32 slot range", fn);
@@ -107,7 +107,8 @@ int dsv4_kv_insert(void* q, const void* kv, const int64_t* positions, const int6
       !aligned(slot_mapping, 8))
     return fail(DSV4_ERR_ALIGN, "%s: q, kv, q_norm_weight, cos_sin, kv_cache must be 16-byte aligned; positions, slot_mapping 8-byte", fn);
   return hip_status(dsv4::launch_insert(q, kv, positions, slot_mapping, cos_sin, max_pos,
-                                        q_norm_weight, eps, kv_cache, num_pages, T, H,
+                                        q_norm_weight, eps, kv_cache, num_pages,
+                                        dsv4::page_shift_of(page_size), T, H,
                                         static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -122,7 +123,8 @@ int dsv4_combine_indices(const int32_t* topk, int topk_stride, int topk_width,
   if (B < 0 || T < 0 || top_k < 0 || window < 0 || topk_width < 0 || topk_stride < topk_width ||
       block_table_stride < 0)
     return fail(DSV4_ERR_SHAPE, "%s: negative size or topk_stride < topk_width", fn);
-  if (page_size != 64) return fail(DSV4_ERR_UNSUPPORTED, "%s: page_size %d not supported (only 64)", fn, page_size);
+  if (dsv4::page_shift_of(page_size) < 0)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: page_size %d not supported (32, 64 or 256)", fn, page_size);
   if (top_k > topk_width) return fail(DSV4_ERR_SHAPE, "%s: top_k %d > topk_width %d", fn, top_k, topk_width);
   const int64_t need = ((int64_t)top_k + window + DSV4_COMBINE_ALIGN - 1) / DSV4_COMBINE_ALIGN * DSV4_COMBINE_ALIGN;
   if (combined_stride < need)
@@ -136,7 +138,8 @@ int dsv4_combine_indices(const int32_t* topk, int topk_stride, int topk_width,
     return fail(DSV4_ERR_ALIGN, "%s: int32 arrays must be 4-byte aligned", fn);
   return hip_status(dsv4::launch_combine(topk, topk_stride, topk_width, topk_lens, query_start_loc,
                                          seq_lens, block_table, block_table_stride, B, T, top_k,
-                                         window, combined, combined_stride, combined_lens,
+                                         window, dsv4::page_shift_of(page_size), combined,
+                                         combined_stride, combined_lens,
                                          static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -150,7 +153,7 @@ int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages
                            softmax_scale, out, T, H);
   if (st) return st;
   if (T == 0) return ok();
-  return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, indices, idx_stride, lens, sinks,
+  return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size), indices, idx_stride, lens, sinks,
                                            softmax_scale, out, lse, T, H, false,
                                            static_cast<hipStream_t>(stream)),
                     fn);
@@ -173,7 +176,7 @@ int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num
   if (splits < 1 || splits > 64) return fail(DSV4_ERR_SHAPE, "%s: splits %d not in 1..64", fn, splits);
   if (T == 0) return ok();
   if (splits == 1)
-    return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, indices, idx_stride, lens,
+    return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size), indices, idx_stride, lens,
                                              sinks, softmax_scale, out, lse, T, H, false,
                                              static_cast<hipStream_t>(stream)),
                       fn);
@@ -183,7 +186,7 @@ int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num
   if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
     return fail(DSV4_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned and hold %zu bytes (got %zu%s)",
                 fn, need, workspace_bytes, workspace ? "" : ", NULL");
-  return hip_status(dsv4::launch_attention_split(q, kv_cache, num_pages, indices, idx_stride, lens,
+  return hip_status(dsv4::launch_attention_split(q, kv_cache, num_pages, dsv4::page_shift_of(page_size), indices, idx_stride, lens,
                                                  sinks, softmax_scale, out, lse, T, H, splits,
                                                  workspace, static_cast<hipStream_t>(stream)),
                     fn);
@@ -198,7 +201,7 @@ int dsv4_sparse_mla_prefill(const void* q, const uint8_t* kv_cache, int num_page
                            softmax_scale, out, T, H);
   if (st) return st;
   if (T == 0) return ok();
-  return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, indices, idx_stride, lens, sinks,
+  return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size), indices, idx_stride, lens, sinks,
                                            softmax_scale, out, lse, T, H, true,
                                            static_cast<hipStream_t>(stream)),
                     fn);
@@ -215,7 +218,7 @@ int dsv4_gather_dequant(const uint8_t* kv_cache, int num_pages, int page_size, c
     return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
   if (!aligned(out, 16) || (kv_cache && !aligned(kv_cache, 16)) || !aligned(slots, 4))
     return fail(DSV4_ERR_ALIGN, "%s: out and kv_cache must be 16-byte aligned, slots 4-byte", fn);
-  return hip_status(dsv4::launch_gather(kv_cache, num_pages, slots, n, out,
+  return hip_status(dsv4::launch_gather(kv_cache, num_pages, dsv4::page_shift_of(page_size), slots, n, out,
                                         static_cast<hipStream_t>(stream)),
                     fn);
 }

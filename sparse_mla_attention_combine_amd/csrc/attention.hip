@@ -58,7 +58,14 @@ struct AttnSmem {
 // Source of the (all-zero) record read for an invalid or absent slot, so that every
 // lane issues the same loads every chunk: branch-free loads let the compiler wait for
 // exactly the chunk it is about to use while later chunks stay in flight.
-__device__ __attribute__((aligned(64))) uint8_t g_zero_page[kPage * kRecord];
+__device__ __attribute__((aligned(64))) uint8_t g_zero_page[kMaxPage * kRecord];
+
+// The cache as the kernels see it: base pointer, number of slots, log2 of the page size.
+struct CacheRef {
+  const uint8_t* base;
+  int64_t num_slots;
+  int ps;
+};
 
 struct RawSlot {
   uint4 nope[8];  // 128 codes: dims 64u + 16g .. 64u + 16g + 15 for u = 0..7
@@ -67,18 +74,17 @@ struct RawSlot {
   int valid;
 };
 
-__device__ __forceinline__ void load_raw_slot(RawSlot& r, const uint8_t* __restrict__ cache,
-                                              int64_t num_slots, int64_t slot, int g) {
-  r.valid = (slot >= 0 && slot < num_slots) ? 1 : 0;
-  const uint8_t* base = r.valid ? cache + page_base(slot >> 6) : g_zero_page;
-  const int off = r.valid ? (int)(slot & (kPage - 1)) : 0;
+__device__ __forceinline__ void load_raw_slot(RawSlot& r, const CacheRef& c, int64_t slot, int g) {
+  r.valid = (slot >= 0 && slot < c.num_slots) ? 1 : 0;
+  const uint8_t* base = r.valid ? c.base + page_base(slot >> c.ps, c.ps) : g_zero_page;
+  const int off = r.valid ? (int)(slot & ((1 << c.ps) - 1)) : 0;
   const uint8_t* np = base + nope_off(off) + 16 * g;
 #pragma unroll
   for (int u = 0; u < 8; ++u) r.nope[u] = *reinterpret_cast<const uint4*>(np + 64 * u);
-  const uint8_t* rp = base + rope_off(off) + 16 * g;
+  const uint8_t* rp = base + rope_off(off, c.ps) + 16 * g;
   r.rope[0] = *reinterpret_cast<const uint4*>(rp);
   r.rope[1] = *reinterpret_cast<const uint4*>(rp + 64);
-  r.sc = *reinterpret_cast<const uint2*>(base + scale_off(off));
+  r.sc = *reinterpret_cast<const uint2*>(base + scale_off(off, c.ps));
 }
 
 // Entry jj of the staged index block (-1 past its end).
@@ -107,15 +113,14 @@ struct RecPtr {
   const uint8_t* sp;  // scale bytes
   int valid;
 };
-__device__ __forceinline__ RecPtr rec_ptr(const uint8_t* __restrict__ cache, int64_t num_slots,
-                                          int64_t slot, int g) {
+__device__ __forceinline__ RecPtr rec_ptr(const CacheRef& c, int64_t slot, int g) {
   RecPtr p;
-  p.valid = (slot >= 0 && slot < num_slots) ? 1 : 0;
-  const uint8_t* base = p.valid ? cache + page_base(slot >> 6) : g_zero_page;
-  const int off = p.valid ? (int)(slot & (kPage - 1)) : 0;
+  p.valid = (slot >= 0 && slot < c.num_slots) ? 1 : 0;
+  const uint8_t* base = p.valid ? c.base + page_base(slot >> c.ps, c.ps) : g_zero_page;
+  const int off = p.valid ? (int)(slot & ((1 << c.ps) - 1)) : 0;
   p.np = base + nope_off(off) + 16 * g;
-  p.rp = base + rope_off(off) + 16 * g;
-  p.sp = base + scale_off(off);
+  p.rp = base + rope_off(off, c.ps) + 16 * g;
+  p.sp = base + scale_off(off, c.ps);
   return p;
 }
 
@@ -449,8 +454,7 @@ __device__ __forceinline__ void resolve_chunk(__bf16 (*__restrict__ ptile)[kPStr
 template <int NHB>
 __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnState<NHB>& st,
                                                RawSlot& raw, int pf_jj, int n_blk,
-                                               const uint8_t* __restrict__ cache,
-                                               int64_t num_slots, int w, int lane,
+                                               const CacheRef& cr, int w, int lane,
                                                float scale_log2) {
   const int l16 = lane & 15, g = lane >> 4;
   const int nb = cb ^ 1;
@@ -461,7 +465,7 @@ __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnSt
     // staging + S first, so the scores are ready by the softmax; the P.V operands are
     // requested next and consumed last, so their MFMAs run across the barrier.
     const uint64_t vmask = __ballot(raw.valid);  // bit j (j < 16) = row 16w + j valid
-    const RecPtr nxt = rec_ptr(cache, num_slots, next_slot, g);
+    const RecPtr nxt = rec_ptr(cr, next_slot, g);
     stage2<true>(&sm.v[nb][0][0], raw, nxt, st, sacc, w, lane);
     PvFrags f;
     pv_reads2(&sm.v[cb][0][0], sm.p[cb], f, w, lane);
@@ -471,7 +475,7 @@ __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnSt
     stage_chunk<NHB>(&sm.v[nb][0][0], raw, st, sacc, w, l16, g);
     pv_chunk<NHB>(&sm.v[cb][0][0], sm.p[cb], st, w, lane);
     const uint64_t vmask = __ballot(raw.valid);
-    load_raw_slot(raw, cache, num_slots, next_slot, g);
+    load_raw_slot(raw, cr, next_slot, g);
     softmax_local<NHB>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
   }
   __syncthreads();
@@ -493,7 +497,7 @@ __device__ __forceinline__ void pv_last(AttnSmem<NHB>& sm, int cb, AttnState<NHB
 
 template <int NHB>
 __global__ void __launch_bounds__(256) sparse_mla_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int64_t num_slots,
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int64_t num_slots, int ps,
     const int32_t* __restrict__ indices, int idx_stride, const int32_t* __restrict__ lens,
     const float* __restrict__ sinks, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, int T, int H, int groups, int splits, int split_len,
@@ -558,6 +562,7 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   __syncthreads();
   const int end = min(max(__builtin_amdgcn_readfirstlane(n_lens_v), 0), lim);
   const int row = 16 * w + l16;
+  const CacheRef cr{cache, num_slots, ps};
   for (int blk0 = beg; blk0 < end; blk0 += kIdxBlock) {
     const int n_blk = min(end - blk0, kIdxBlock);
     if (blk0 != beg) {
@@ -567,17 +572,17 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     }
     const int nch = (n_blk + kChunk - 1) / kChunk;
     RawSlot A, B;
-    load_raw_slot(A, cache, num_slots, idx_at(sm.idx, row, n_blk), g);
-    load_raw_slot(B, cache, num_slots, idx_at(sm.idx, kChunk + row, n_blk), g);
+    load_raw_slot(A, cr, idx_at(sm.idx, row, n_blk), g);
+    load_raw_slot(B, cr, idx_at(sm.idx, kChunk + row, n_blk), g);
     {  // prologue: stage chunk 0 and settle its probabilities
       f32x4 sacc[NHB];
       const uint64_t vmask = __ballot(A.valid);
       if constexpr (NHB == 2) {
-        const RecPtr nxt = rec_ptr(cache, num_slots, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
+        const RecPtr nxt = rec_ptr(cr, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
         stage2<true>(&sm.v[0][0][0], A, nxt, st, sacc, w, lane);
       } else {
         stage_chunk<NHB>(&sm.v[0][0][0], A, st, sacc, w, l16, g);
-        load_raw_slot(A, cache, num_slots, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
+        load_raw_slot(A, cr, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
       }
       float s[NHB][4], psum[NHB];
       softmax_local<NHB>(sm.p[0], sm.red[0], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
@@ -586,13 +591,13 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     }
     int i = 0;
     for (; i + 2 < nch; i += 2) {
-      pipelined_step<NHB>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cache, num_slots, w, lane,
+      pipelined_step<NHB>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cr, w, lane,
                           scale_log2);
-      pipelined_step<NHB>(sm, 1, st, A, (i + 4) * kChunk + row, n_blk, cache, num_slots, w, lane,
+      pipelined_step<NHB>(sm, 1, st, A, (i + 4) * kChunk + row, n_blk, cr, w, lane,
                           scale_log2);
     }
     if (i + 1 < nch) {
-      pipelined_step<NHB>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cache, num_slots, w, lane,
+      pipelined_step<NHB>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cr, w, lane,
                           scale_log2);
       pv_last<NHB>(sm, 1, st, w, lane);
     } else {
@@ -710,43 +715,43 @@ size_t split_workspace_bytes(int T, int H, int splits) {
   return (size_t)T * splits * H * (kNope + 2) * sizeof(float);
 }
 
-static hipError_t launch_items(const void* q, const uint8_t* cache, int num_pages,
+static hipError_t launch_items(const void* q, const uint8_t* cache, int num_pages, int ps,
                                const int32_t* indices, int idx_stride, const int32_t* lens,
                                const float* sinks, float softmax_scale, void* out, float* lse,
                                int T, int H, int splits, int split_len, float* part_o,
                                float* part_ml, hipStream_t stream) {
-  const int64_t num_slots = (int64_t)num_pages * kPage;
+  const int64_t num_slots = (int64_t)num_pages << ps;
   const float scale_log2 = softmax_scale * kLog2e;
   const int items = T * splits;
   if (H == 16) {
     hipLaunchKernelGGL(sparse_mla_kernel<1>, dim3(items), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), cache, num_slots, indices, idx_stride, lens,
+                       static_cast<const uint16_t*>(q), cache, num_slots, ps, indices, idx_stride, lens,
                        sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, 1, splits,
                        split_len, part_o, part_ml);
   } else {
     const int groups = H / 32;
     const int grid = groups == 1 ? items : 8 * groups * ((items + 7) / 8);
     hipLaunchKernelGGL(sparse_mla_kernel<2>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), cache, num_slots, indices, idx_stride, lens,
+                       static_cast<const uint16_t*>(q), cache, num_slots, ps, indices, idx_stride, lens,
                        sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, groups, splits,
                        split_len, part_o, part_ml);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages,
+hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, int page_shift,
                             const int32_t* indices, int idx_stride, const int32_t* lens,
                             const float* sinks, float softmax_scale, void* out, float* lse, int T,
                             int H, bool prefill, hipStream_t stream) {
   (void)prefill;  // one schedule serves both entry points for now
   if (T == 0) return hipSuccess;
   const int whole = idx_stride > 0 ? idx_stride : 1;
-  return launch_items(q, cache, num_pages, indices, idx_stride, lens, sinks, softmax_scale, out,
-                      lse, T, H, 1, whole, nullptr, nullptr, stream);
+  return launch_items(q, cache, num_pages, page_shift, indices, idx_stride, lens, sinks,
+                      softmax_scale, out, lse, T, H, 1, whole, nullptr, nullptr, stream);
 }
 
 hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_pages,
-                                  const int32_t* indices, int idx_stride, const int32_t* lens,
+                                  int page_shift, const int32_t* indices, int idx_stride, const int32_t* lens,
                                   const float* sinks, float softmax_scale, void* out, float* lse,
                                   int T, int H, int splits, void* workspace, hipStream_t stream) {
   if (T == 0) return hipSuccess;
@@ -755,8 +760,9 @@ hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_p
   const int split_len = per > 0 ? ((per + kChunk - 1) / kChunk) * kChunk : kChunk;
   float* part_o = static_cast<float*>(workspace);
   float* part_ml = part_o + (size_t)T * splits * H * kNope;
-  hipError_t e = launch_items(q, cache, num_pages, indices, idx_stride, lens, sinks, softmax_scale,
-                              out, lse, T, H, splits, split_len, part_o, part_ml, stream);
+  hipError_t e = launch_items(q, cache, num_pages, page_shift, indices, idx_stride, lens, sinks,
+                              softmax_scale, out, lse, T, H, splits, split_len, part_o, part_ml,
+                              stream);
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)T * H;
   hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,

@@ -14,19 +14,21 @@ namespace dsv4 {
 
 constexpr int kColsPerThread = 9;  // 2304 columns per pass covers the 2176-wide rows
 
+// Logical position x of a request -> physical slot through its block-table row (pages
+// of 2^ps slots); -1 for a position without a page.
 __device__ __forceinline__ int32_t phys_slot(const int32_t* __restrict__ bt_row, int bt_stride,
-                                             int64_t x) {
-  int64_t lp = x >> 6;  // logical page (page size 64)
+                                             int64_t x, int ps) {
+  int64_t lp = x >> ps;  // logical page
   if (x < 0 || lp >= bt_stride) return -1;
   int32_t page = bt_row[lp];
-  return page < 0 ? -1 : (int32_t)((int64_t)page * kPage + (x & (kPage - 1)));
+  return page < 0 ? -1 : (int32_t)(((int64_t)page << ps) + (x & ((1 << ps) - 1)));
 }
 
 __global__ void __launch_bounds__(256) combine_kernel(
     const int32_t* __restrict__ topk, int topk_stride, int topk_width,
     const int32_t* __restrict__ topk_lens, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table, int bt_stride,
-    int T, int top_k, int window, int32_t* __restrict__ combined, int combined_stride,
+    int T, int top_k, int window, int ps, int32_t* __restrict__ combined, int combined_stride,
     int32_t* __restrict__ combined_lens) {
   const int b = blockIdx.x;
   const int base = qsl[0];
@@ -60,7 +62,7 @@ __global__ void __launch_bounds__(256) combine_kernel(
       }
       int32_t v[kColsPerThread];
 #pragma unroll
-      for (int k = 0; k < kColsPerThread; ++k) v[k] = x[k] >= 0 ? phys_slot(bt_row, bt_stride, x[k]) : -1;
+      for (int k = 0; k < kColsPerThread; ++k) v[k] = x[k] >= 0 ? phys_slot(bt_row, bt_stride, x[k], ps) : -1;
 #pragma unroll
       for (int k = 0; k < kColsPerThread; ++k) {
         const int j = jb + threadIdx.x + 256 * k;
@@ -74,7 +76,7 @@ __global__ void __launch_bounds__(256) combine_kernel(
 hipError_t launch_combine(const int32_t* topk, int topk_stride, int topk_width,
                           const int32_t* topk_lens, const int32_t* qsl, const int32_t* seq_lens,
                           const int32_t* block_table, int bt_stride, int B, int T, int top_k,
-                          int window, int32_t* combined, int combined_stride,
+                          int window, int page_shift, int32_t* combined, int combined_stride,
                           int32_t* combined_lens, hipStream_t stream) {
   if (B == 0 || T == 0) return hipSuccess;
   // tokens per request are device data; size the second grid axis from the average
@@ -82,7 +84,7 @@ hipError_t launch_combine(const int32_t* topk, int topk_stride, int topk_width,
   int Y = per_req < 1 ? 1 : (per_req > 2048 ? 2048 : per_req);
   hipLaunchKernelGGL(combine_kernel, dim3(B, Y), dim3(256), 0, stream, topk, topk_stride,
                      topk_width, topk_lens, qsl, seq_lens, block_table, bt_stride, T, top_k,
-                     window, combined, combined_stride, combined_lens);
+                     window, page_shift, combined, combined_stride, combined_lens);
   return hipGetLastError();
 }
 

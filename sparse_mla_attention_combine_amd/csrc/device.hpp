@@ -18,13 +18,15 @@ constexpr int kNope = 512;
 constexpr int kRope = 64;
 constexpr int kBlocks = 8;
 constexpr int kRecord = 648;
-constexpr int kPage = 64;  // the only page size the launchers accept
+constexpr int kMaxPage = 256;  // page sizes accepted by the launchers: 32, 64 and 256 slots
 
-// Byte offsets of the three fields of slot `off` inside a page of kPage slots.
-__device__ __forceinline__ int64_t page_base(int64_t page) { return page * (int64_t)kPage * kRecord; }
+// A page of P = 2^ps slots holds the E4M3 codes [P][512] at byte 0, the bf16 rope rows
+// [P][64] at P*512 and the UE8M0 scales [P][8] at P*640.  Byte offsets of a page and of
+// the three fields of its slot `off`:
+__device__ __forceinline__ int64_t page_base(int64_t page, int ps) { return (page * (int64_t)kRecord) << ps; }
 __device__ __forceinline__ int nope_off(int off) { return off * kNope; }
-__device__ __forceinline__ int rope_off(int off) { return kPage * kNope + off * kRope * 2; }
-__device__ __forceinline__ int scale_off(int off) { return kPage * (kNope + 2 * kRope) + off * kBlocks; }
+__device__ __forceinline__ int rope_off(int off, int ps) { return (kNope << ps) + off * kRope * 2; }
+__device__ __forceinline__ int scale_off(int off, int ps) { return ((kNope + 2 * kRope) << ps) + off * kBlocks; }
 
 // UE8M0 byte -> an fp32 whose exponent field is that byte.  gfx950's scaled FP8
 // conversions read only the exponent field of the scale operand as an E8M0 value

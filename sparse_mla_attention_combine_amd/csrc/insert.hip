@@ -90,16 +90,16 @@ __device__ __forceinline__ void q_norm_rope(
 __device__ __forceinline__ void kv_quant_insert(
     const uint16_t* __restrict__ kv, const int64_t* __restrict__ positions,
     const int64_t* __restrict__ slot_mapping, const float* __restrict__ cos_sin, int max_pos,
-    uint8_t* __restrict__ cache, int64_t num_slots, int T, int block) {
+    uint8_t* __restrict__ cache, int64_t num_slots, int ps, int T, int block) {
   const int lane = threadIdx.x & 63;
   const int64_t t = ((int64_t)block * blockDim.x + threadIdx.x) >> 6;
   if (t >= T) return;
   const int64_t p = positions[t];
   const int64_t slot = slot_mapping[t];
   if (p < 0 || p >= max_pos || slot < 0 || slot >= num_slots) return;
-  const int64_t page = slot >> 6;
-  const int off = (int)(slot & (kPage - 1));
-  uint8_t* base = cache + page_base(page);
+  const int64_t page = slot >> ps;
+  const int off = (int)(slot & ((1 << ps) - 1));
+  uint8_t* base = cache + page_base(page, ps);
   const uint16_t* kr = kv + t * kLatent;
 
   // nope dims 8*lane .. 8*lane+7, block lane/8
@@ -136,7 +136,7 @@ __device__ __forceinline__ void kv_quant_insert(
     codes[h] = (uint32_t)c;
   }
   *reinterpret_cast<uint2*>(base + nope_off(off) + 8 * lane) = make_uint2(codes[0], codes[1]);
-  if ((lane & 7) == 0) base[scale_off(off) + (lane >> 3)] = (uint8_t)(e + 127);
+  if ((lane & 7) == 0) base[scale_off(off, ps) + (lane >> 3)] = (uint8_t)(e + 127);
 
   // rope dims 512 + 8*lane .. +7 for lanes 0..7, stored rotated (bf16)
   if (lane < 8) {
@@ -152,7 +152,7 @@ __device__ __forceinline__ void kv_quant_insert(
       const float a = bf16_bits_to_f32(ru[e2] & 0xFFFF), b = bf16_bits_to_f32(ru[e2] >> 16);
       o[e2] = pack_bf16x2(a * cc[e2] - b * sn[e2], a * sn[e2] + b * cc[e2]);
     }
-    *reinterpret_cast<uint4*>(base + rope_off(off) + 16 * lane) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(base + rope_off(off, ps) + 16 * lane) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -162,18 +162,18 @@ __global__ void __launch_bounds__(256) insert_kernel(
     uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int64_t* __restrict__ positions,
     const int64_t* __restrict__ slot_mapping, const float* __restrict__ cos_sin, int max_pos,
     const uint16_t* __restrict__ weight, float eps, uint8_t* __restrict__ cache, int64_t num_slots,
-    int T, int H, int qblocks) {
+    int ps, int T, int H, int qblocks) {
   if ((int)blockIdx.x < qblocks)
     q_norm_rope(q, positions, cos_sin, max_pos, weight, eps, (int64_t)T * H, H, qblocks);
   else
-    kv_quant_insert(kv, positions, slot_mapping, cos_sin, max_pos, cache, num_slots, T,
+    kv_quant_insert(kv, positions, slot_mapping, cos_sin, max_pos, cache, num_slots, ps, T,
                     (int)blockIdx.x - qblocks);
 }
 
 hipError_t launch_insert(void* q, const void* kv, const int64_t* positions,
                          const int64_t* slot_mapping, const float* cos_sin, int max_pos,
-                         const void* weight, float eps, uint8_t* cache, int num_pages, int T,
-                         int H, hipStream_t stream) {
+                         const void* weight, float eps, uint8_t* cache, int num_pages,
+                         int page_shift, int T, int H, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int64_t rows = (int64_t)T * H;
   const int64_t groups = (rows + 31) / 32;  // 32 q rows per 256-thread block per pass
@@ -182,7 +182,7 @@ hipError_t launch_insert(void* q, const void* kv, const int64_t* positions,
   hipLaunchKernelGGL(insert_kernel, dim3(qblocks + kvblocks), dim3(256), 0, stream,
                      static_cast<uint16_t*>(q), static_cast<const uint16_t*>(kv), positions,
                      slot_mapping, cos_sin, max_pos, static_cast<const uint16_t*>(weight), eps,
-                     cache, (int64_t)num_pages * kPage, T, H, qblocks);
+                     cache, (int64_t)num_pages << page_shift, page_shift, T, H, qblocks);
   return hipGetLastError();
 }
 

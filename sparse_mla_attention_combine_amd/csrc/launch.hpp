@@ -6,21 +6,26 @@
 
 namespace dsv4 {
 
+// log2 of a supported page size (32, 64 or 256 slots), -1 for any other.
+inline int page_shift_of(int page_size) {
+  return page_size == 32 ? 5 : page_size == 64 ? 6 : page_size == 256 ? 8 : -1;
+}
+
 hipError_t launch_combine(const int32_t* topk, int topk_stride, int topk_width,
                           const int32_t* topk_lens, const int32_t* qsl, const int32_t* seq_lens,
                           const int32_t* block_table, int bt_stride, int B, int T, int top_k,
-                          int window, int32_t* combined, int combined_stride,
+                          int window, int page_shift, int32_t* combined, int combined_stride,
                           int32_t* combined_lens, hipStream_t stream);
 
 hipError_t launch_insert(void* q, const void* kv, const int64_t* positions,
                          const int64_t* slot_mapping, const float* cos_sin, int max_pos,
-                         const void* weight, float eps, uint8_t* cache, int num_pages, int T,
-                         int H, hipStream_t stream);
+                         const void* weight, float eps, uint8_t* cache, int num_pages,
+                         int page_shift, int T, int H, hipStream_t stream);
 
-hipError_t launch_gather(const uint8_t* cache, int num_pages, const int32_t* slots, int n,
-                         void* out, hipStream_t stream);
+hipError_t launch_gather(const uint8_t* cache, int num_pages, int page_shift, const int32_t* slots,
+                         int n, void* out, hipStream_t stream);
 
-hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages,
+hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, int page_shift,
                             const int32_t* indices, int idx_stride, const int32_t* lens,
                             const float* sinks, float softmax_scale, void* out, float* lse,
                             int T, int H, bool prefill, hipStream_t stream);
@@ -28,7 +33,7 @@ hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages,
 // Split-slot decode: the row of each token is cut into `splits` 64-aligned pieces whose
 // partials go to `workspace` (split_workspace_bytes(T, H, splits) bytes) and are merged.
 hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_pages,
-                                  const int32_t* indices, int idx_stride, const int32_t* lens,
+                                  int page_shift, const int32_t* indices, int idx_stride, const int32_t* lens,
                                   const float* sinks, float softmax_scale, void* out, float* lse,
                                   int T, int H, int splits, void* workspace, hipStream_t stream);
 size_t split_workspace_bytes(int T, int H, int splits);

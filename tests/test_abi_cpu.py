@@ -53,7 +53,8 @@ def test_attention_validation(dsv4):
 
     for fn in (lib.dsv4_sparse_mla_decode, lib.dsv4_sparse_mla_prefill):
         assert call(fn, H=24) == 4 and b"H = 24" in lib.dsv4_last_error()
-        assert call(fn, page_size=32) == 4
+        for bad in (16, 48, 128, 0, -64):
+            assert call(fn, page_size=bad) == 4
         assert call(fn, q=None) == 1
         assert call(fn, lens=None) == 1
         assert call(fn, T=-1) == 2
