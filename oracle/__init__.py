@@ -50,11 +50,15 @@ def lib() -> ctypes.CDLL:
         L.oracle_gather_dequant.argtypes = [vp, i32, i32, vp, i32, vp]
         L.oracle_combine.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      vp, i32, vp]
+        L.oracle_combine_compressed.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                i32, i32, i32, vp, i32, vp]
+        L.oracle_gather_workspace.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, i32, vp, vp, i32,
+                                              i32, i32, i32, vp, i32]
         L.oracle_kv_insert.argtypes = [vp, vp, vp, vp, vp, i32, vp, dbl, vp, i32, i32, i32, i32]
         L.oracle_sparse_mla.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, dbl, vp, vp, i32, i32,
                                         i32]
-        for f in (L.oracle_gather_dequant, L.oracle_combine, L.oracle_kv_insert,
-                  L.oracle_sparse_mla):
+        for f in (L.oracle_gather_dequant, L.oracle_combine, L.oracle_combine_compressed,
+                  L.oracle_gather_workspace, L.oracle_kv_insert, L.oracle_sparse_mla):
             f.restype = None
         _lib = L
     return _lib
@@ -122,6 +126,37 @@ def combine(topk, topk_lens, qsl, seq_lens, block_table, T, top_k, window, page_
                          _ptr(bt), bt.shape[1], B, T, top_k, window, page_size, _ptr(out),
                          combined_stride, _ptr(lens))
     return out, lens
+
+
+def combine_compressed(topk, topk_lens, qsl, seq_lens, gather_lens, T, top_k, ratio, window, M, N,
+                       combined_stride, topk_width=None, fill=-7):
+    """Combined rows ``[T, combined_stride]`` and lengths ``[T]`` in the workspace index
+    space of the compressed-cache form (request b owns rows ``M*b .. M*b+M-1``)."""
+    topk = _c(topk, np.int32)
+    tl = _c(topk_lens, np.int32)
+    qsl, seq_lens, gl = _c(qsl, np.int32), _c(seq_lens, np.int32), _c(gather_lens, np.int32)
+    B = seq_lens.shape[0]
+    out = np.full((T, combined_stride), fill, np.int32)
+    lens = np.full((T,), fill, np.int32)
+    width = topk.shape[1] if topk_width is None else topk_width
+    lib().oracle_combine_compressed(_ptr(topk), topk.shape[1], width, _ptr(tl), _ptr(qsl),
+                                    _ptr(seq_lens), _ptr(gl), B, T, top_k, ratio, window, M, N,
+                                    _ptr(out), combined_stride, _ptr(lens))
+    return out, lens
+
+
+def gather_workspace(comp_cache, comp_num_pages, comp_bt, swa_cache, swa_num_pages, swa_bt,
+                     page_size, seq_lens, gather_lens, ratio, M, N, ws_num_pages, ws=None):
+    """The workspace cache (``ws_num_pages`` pages) those indices address."""
+    comp_bt, swa_bt = _c(comp_bt, np.int32), _c(swa_bt, np.int32)
+    seq_lens, gl = _c(seq_lens, np.int32), _c(gather_lens, np.int32)
+    out = (np.full(ws_num_pages * page_size * RECORD, 0xA5, np.uint8) if ws is None
+           else np.array(ws, np.uint8, copy=True))
+    lib().oracle_gather_workspace(_ptr(_c(comp_cache, np.uint8)), comp_num_pages, _ptr(comp_bt),
+                                  comp_bt.shape[1], _ptr(_c(swa_cache, np.uint8)), swa_num_pages,
+                                  _ptr(swa_bt), swa_bt.shape[1], page_size, _ptr(seq_lens),
+                                  _ptr(gl), seq_lens.shape[0], ratio, M, N, _ptr(out), ws_num_pages)
+    return out
 
 
 def kv_insert(q_bits, kv_bits, positions, slot_mapping, cos_sin, weight_bits, eps, cache,

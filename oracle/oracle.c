@@ -224,6 +224,114 @@ void oracle_combine(const int32_t* topk, int topk_stride, int topk_width, const 
 }
 
 /* ------------------------------------------------------------------------------- */
+/* Step 1, compressed-cache form [p3 Key source excerpts: the same combine kernel with */
+/* COMPRESS_RATIO, M, N and gather_lens].  The indices address the rows of a per-      */
+/* request workspace of M rows: request b owns rows M*b .. M*b+M-1; its first N rows   */
+/* hold compressed entries 0..N-1, the next ones the last gather_lens[b] raw tokens of  */
+/* the sequence, starting at position gather_start = seq_len - gather_len.  Per token  */
+/* at position pos (request b):                                                         */
+/*   tk = min((pos+1) / ratio, top_k[, topk_lens[t]]) (floor; at least 0),              */
+/*   sw = min(pos+1, window),                                                           */
+/*   row[j]    = M*b + e for j < tk, e = topk[t][j], if 0 <= e < N, else -1,            */
+/*   row[tk+r] = M*b + N + (pos-sw+1+r - gather_start) for r < sw,                      */
+/*   lens[t]   = tk + sw, the rest of the row -1.                                       */
+/* Readings: no dedup between the two parts (they are different index spaces); a      */
+/* window row outside the gathered tokens or beyond the request's M rows is -1 (the    */
+/* page writes it unchecked; the two agree whenever gather_len covers the window and   */
+/* N + gather_len <= M); topk_lens is optional (NULL: the page's kernel exactly).      */
+/* ------------------------------------------------------------------------------- */
+
+void oracle_combine_compressed(const int32_t* topk, int topk_stride, int topk_width,
+                               const int32_t* topk_lens, const int32_t* qsl,
+                               const int32_t* seq_lens, const int32_t* gather_lens, int B, int T,
+                               int top_k, int ratio, int window, int M, int N, int32_t* combined,
+                               int combined_stride, int32_t* combined_lens) {
+  for (int b = 0; b < B; ++b) {
+    int qlen = qsl[b + 1] - qsl[b];
+    int64_t gather_start = (int64_t)seq_lens[b] - gather_lens[b];
+    for (int i = 0; i < qlen; ++i) {
+      int64_t t = (int64_t)qsl[b] - qsl[0] + i;
+      if (t < 0 || t >= T) continue;
+      int64_t pos = (int64_t)seq_lens[b] - qlen + i;
+      int64_t tk = pos + 1 >= 0 ? (pos + 1) / ratio : 0;
+      if (tk > top_k) tk = top_k;
+      if (topk_lens && topk_lens[t] < tk) tk = topk_lens[t];
+      if (tk < 0) tk = 0;
+      int64_t sw = pos + 1 < window ? pos + 1 : window;
+      if (sw < 0) sw = 0;
+      int32_t* row = combined + t * combined_stride;
+      for (int64_t j = 0; j < tk; ++j) {
+        int64_t e = j < topk_width ? topk[t * topk_stride + j] : -1;
+        row[j] = (e >= 0 && e < N) ? (int32_t)((int64_t)M * b + e) : -1;
+      }
+      for (int64_t r = 0; r < sw; ++r) {
+        int64_t k = pos - sw + 1 + r - gather_start; /* row among the gathered tokens */
+        int ok = k >= 0 && k < gather_lens[b] && N + k < M;
+        row[tk + r] = ok ? (int32_t)((int64_t)M * b + N + k) : -1;
+      }
+      for (int64_t j = tk + sw; j < combined_stride; ++j) row[j] = -1;
+      combined_lens[t] = (int32_t)(tk + sw);
+    }
+  }
+}
+
+/* The workspace those indices address, as a cache of its own (pages of P slots, slot */
+/* M*b + e): row e < N of request b is a copy of compressed entry e (the entries       */
+/* seq_len / ratio ... N-1 do not exist yet and are zero), row N + k (k < gather_len)  */
+/* a copy of the raw token at position gather_start + k; rows without a source are     */
+/* zero.  Compressed entry e lives in comp_cache at comp_bt[b][e / P] * P + e % P, raw */
+/* position x in swa_cache at swa_bt[b][x / P] * P + x % P (a negative page or one     */
+/* past the table also gives a zero row).  Readings: the page shows the indices, not   */
+/* the step that fills the workspace; this is the plainest filling they imply.         */
+static void copy_record(uint8_t* dst, int Pd, int64_t ds, const uint8_t* src, int Ps, int64_t ss) {
+  uint8_t* dn = dst + (ds / Pd) * (int64_t)Pd * RECORD + (ds % Pd) * NOPE;
+  uint8_t* dr = dst + (ds / Pd) * (int64_t)Pd * RECORD + (int64_t)Pd * NOPE + (ds % Pd) * ROPE * 2;
+  uint8_t* dc = dst + (ds / Pd) * (int64_t)Pd * RECORD + (int64_t)Pd * (NOPE + ROPE * 2) + (ds % Pd) * NBLOCKS;
+  if (!src) {
+    memset(dn, 0, NOPE);
+    memset(dr, 0, ROPE * 2);
+    memset(dc, 0, NBLOCKS);
+    return;
+  }
+  memcpy(dn, rec_nope(src, Ps, ss), NOPE);
+  memcpy(dr, rec_rope(src, Ps, ss), ROPE * 2);
+  memcpy(dc, rec_scale(src, Ps, ss), NBLOCKS);
+}
+
+void oracle_gather_workspace(const uint8_t* comp_cache, int comp_num_pages, const int32_t* comp_bt,
+                             int comp_bt_stride, const uint8_t* swa_cache, int swa_num_pages,
+                             const int32_t* swa_bt, int swa_bt_stride, int P,
+                             const int32_t* seq_lens, const int32_t* gather_lens, int B, int ratio,
+                             int M, int N, uint8_t* ws, int ws_num_pages) {
+  for (int b = 0; b < B; ++b) {
+    int64_t n_comp = seq_lens[b] / ratio;
+    int64_t gather_start = (int64_t)seq_lens[b] - gather_lens[b];
+    for (int64_t e = 0; e < M; ++e) {
+      int64_t ds = (int64_t)M * b + e;
+      if (ds >= (int64_t)ws_num_pages * P) continue;
+      const uint8_t* src = NULL;
+      int64_t ss = -1;
+      if (e < N) {
+        if (e < n_comp) {
+          ss = phys_slot(comp_bt, comp_bt_stride, b, e, P);
+          if (ss >= (int64_t)comp_num_pages * P) ss = -1;
+          src = ss >= 0 ? comp_cache : NULL;
+        }
+      } else {
+        int64_t k = e - N;
+        int64_t x = gather_start + k;
+        if (k < gather_lens[b] && x >= 0 && x < seq_lens[b]) {
+          ss = phys_slot(swa_bt, swa_bt_stride, b, x, P);
+          if (ss >= (int64_t)swa_num_pages * P) ss = -1;
+          src = ss >= 0 ? swa_cache : NULL;
+        }
+      }
+      copy_record(ws, P, ds, src, P, ss);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------- */
 /* Step 4 (fused insert) [p2 Implementation breakdown item 4: per-head q RMSNorm,      */
 /* GPT-J RoPE, FP8 UE8M0 KV insert; Key source excerpts: xpu_sparse.py calls it with   */
 /* (q, kv, kv_cache, slot_mapping, positions); p1 item 2 "RMSNorm+Rope+Quant"].        */
