@@ -150,6 +150,61 @@ int dsv4_combine_indices(const int32_t* topk, int topk_stride, int topk_width,
                          int32_t* combined_lens, void* stream);
 
 /*
+ * dsv4_combine_indices_compressed — the combine step for a compressed KV cache, where
+ * top-k picks compressed entries and the window picks raw tokens: two index spaces
+ * [p3 Key source excerpts: rocm.py combine kernel with COMPRESS_RATIO, M, N and
+ * gather_lens].  The output indexes a per-request workspace of M rows (request b owns
+ * rows M*b .. M*b+M-1: N compressed entries, then the last gather_lens[b] raw tokens of
+ * the sequence, from position gather_start = seq_lens[b] - gather_lens[b]); see
+ * dsv4_gather_workspace.  For request b's i-th token, at pos = seq_lens[b]-qlen+i:
+ *   tk = max(0, min((pos+1) / compress_ratio, top_k, topk_lens[t] if topk_lens)),
+ *   sw = max(0, min(pos+1, window)),
+ *   combined[t][j]    = M*b + e for j < tk, e = topk[t][j], if 0 <= e < N, else -1;
+ *   combined[t][tk+r] = M*b + N + k for r < sw, k = pos-sw+1+r - gather_start, or -1
+ *                       when k < 0, k >= gather_lens[b] or N + k >= M;
+ *   combined[t][j]    = -1 past tk+sw;  combined_lens[t] = tk + sw.
+ * No dedup between the parts (different index spaces).  Arrays as for
+ * dsv4_combine_indices, plus gather_lens int32 [B].  Requires compress_ratio >= 1,
+ * 0 <= N <= M, B*M < 2^31, top_k <= topk_width, combined_stride >= round_up(top_k +
+ * window, 128); errors otherwise as for dsv4_combine_indices.
+ */
+int dsv4_combine_indices_compressed(const int32_t* topk, int topk_stride, int topk_width,
+                                    const int32_t* topk_lens, const int32_t* query_start_loc,
+                                    const int32_t* seq_lens, const int32_t* gather_lens, int B,
+                                    int T, int top_k, int compress_ratio, int window, int M, int N,
+                                    int32_t* combined, int combined_stride, int32_t* combined_lens,
+                                    void* stream);
+
+/*
+ * dsv4_gather_workspace — fills the workspace the compressed-form indices address, as a
+ * cache of its own (ws_num_pages pages of page_size slots, the layout above; slot M*b+e
+ * for row e of request b), so that dsv4_sparse_mla_prefill / _decode run over it with
+ * those indices as slots [p3 Key source excerpts: the workspace rows M*b + ... of the
+ * combine kernel; the page shows the indices, the filling is their plain reading]:
+ *   e < N:      compressed entry e of request b, read from comp_cache at slot
+ *               comp_block_table[b][e/P]*P + e%P, if e < seq_lens[b] / compress_ratio
+ *               (the entries that exist), else a zero record;
+ *   e = N + k:  the raw token at x = seq_lens[b] - gather_lens[b] + k, read from
+ *               swa_cache at swa_block_table[b][x/P]*P + x%P, for k < gather_lens[b]
+ *               and 0 <= x < seq_lens[b], else a zero record.
+ * A negative page, a page index past the table's stride or a slot past the source
+ * cache also give a zero record.  Records are copied exactly (codes, scales, rope).
+ * Workspace slots >= B*M, and all of ws_cache past ws_num_pages pages, are untouched.
+ *   comp_cache / swa_cache  caches of comp_num_pages / swa_num_pages pages (may be the
+ *                           same buffer); block tables int32 [B][stride]
+ *   seq_lens, gather_lens   int32 [B]
+ * Requires page_size in {32, 64, 256} (all three caches), compress_ratio >= 1,
+ * 0 <= N <= M, B*M < 2^31, 16-byte aligned caches.
+ */
+int dsv4_gather_workspace(const uint8_t* comp_cache, int comp_num_pages,
+                          const int32_t* comp_block_table, int comp_bt_stride,
+                          const uint8_t* swa_cache, int swa_num_pages,
+                          const int32_t* swa_block_table, int swa_bt_stride, int page_size,
+                          const int32_t* seq_lens, const int32_t* gather_lens, int B,
+                          int compress_ratio, int M, int N, uint8_t* ws_cache, int ws_num_pages,
+                          void* stream);
+
+/*
  * dsv4_sparse_mla_decode — sparse MQA-form MLA attention of every head over the
  * listed cache slots [p2 Key source excerpts xpu_sparse_decode_fp8: dequantise the
  * gathered FP8 slots, then bf16 sparse MLA with topk_lens; p4 forward_mqa: output

@@ -40,14 +40,20 @@ _lib.dsv4_gather_dequant.argtypes = [_vp, _i32, _i32, _vp, _i32, _vp, _vp]
 _lib.dsv4_sparse_mla_split_workspace_bytes.argtypes = [_i32, _i32, _i32]
 _lib.dsv4_sparse_mla_split_workspace_bytes.restype = ctypes.c_size_t
 _lib.dsv4_sparse_mla_decode_split.argtypes = _attn_args[:-1] + [_i32, _vp, ctypes.c_size_t, _vp]
+_lib.dsv4_combine_indices_compressed.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
+                                                 _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]
+_lib.dsv4_gather_workspace.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp,
+                                       _i32, _i32, _i32, _i32, _vp, _i32, _vp]
 for _f in (_lib.dsv4_kv_insert, _lib.dsv4_combine_indices, _lib.dsv4_sparse_mla_decode,
-           _lib.dsv4_sparse_mla_prefill, _lib.dsv4_gather_dequant, _lib.dsv4_sparse_mla_decode_split):
+           _lib.dsv4_sparse_mla_prefill, _lib.dsv4_gather_dequant, _lib.dsv4_sparse_mla_decode_split,
+           _lib.dsv4_combine_indices_compressed, _lib.dsv4_gather_workspace):
     _f.restype = _i32
 
 EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4_kv_insert",
             "dsv4_combine_indices", "dsv4_sparse_mla_decode", "dsv4_sparse_mla_prefill",
             "dsv4_gather_dequant", "dsv4_sparse_mla_split_workspace_bytes",
-            "dsv4_sparse_mla_decode_split"]
+            "dsv4_sparse_mla_decode_split", "dsv4_combine_indices_compressed",
+            "dsv4_gather_workspace"]
 
 
 class Dsv4Error(RuntimeError):
@@ -129,6 +135,43 @@ def dsv4_combine_indices(topk, topk_lens, query_start_loc, seq_lens, block_table
                                      block_table.shape[1], B, T, top_k, window, page_size,
                                      _ptr(combined), combined.shape[1], _ptr(combined_lens),
                                      _stream(stream)))
+
+
+def dsv4_combine_indices_compressed(topk, topk_lens, query_start_loc, seq_lens, gather_lens,
+                                    top_k, compress_ratio, window, M, N, combined, combined_lens,
+                                    topk_width=None, stream=None):
+    """Compressed-cache form of the combine: writes combined int32 [T, stride] (indices
+    into a per-request workspace of M rows: N compressed entries, then gathered raw
+    tokens) and combined_lens int32 [T]."""
+    for t, n in ((topk, "topk"), (topk_lens, "topk_lens"), (query_start_loc, "query_start_loc"),
+                 (seq_lens, "seq_lens"), (gather_lens, "gather_lens"), (combined, "combined"),
+                 (combined_lens, "combined_lens")):
+        _want(t, torch.int32, n)
+    T, B = combined.shape[0], seq_lens.shape[0]
+    width = topk.shape[1] if topk_width is None else topk_width
+    _check(_lib.dsv4_combine_indices_compressed(
+        _ptr(topk), topk.shape[1], width, _ptr(topk_lens), _ptr(query_start_loc), _ptr(seq_lens),
+        _ptr(gather_lens), B, T, top_k, compress_ratio, window, M, N, _ptr(combined),
+        combined.shape[1], _ptr(combined_lens), _stream(stream)))
+
+
+def dsv4_gather_workspace(comp_cache, comp_block_table, swa_cache, swa_block_table, seq_lens,
+                          gather_lens, compress_ratio, M, N, ws_cache, page_size=64, stream=None):
+    """Fills ws_cache (uint8 pages) with the workspace rows the compressed-form indices
+    address: compressed entries through comp_block_table, raw tokens through
+    swa_block_table (int32 [B, stride] each)."""
+    for t, n in ((comp_cache, "comp_cache"), (swa_cache, "swa_cache"), (ws_cache, "ws_cache")):
+        _want(t, torch.uint8, n)
+    for t, n in ((comp_block_table, "comp_block_table"), (swa_block_table, "swa_block_table"),
+                 (seq_lens, "seq_lens"), (gather_lens, "gather_lens")):
+        _want(t, torch.int32, n)
+    pb = cache_page_bytes(page_size)
+    _check(_lib.dsv4_gather_workspace(
+        _ptr(comp_cache), comp_cache.numel() // pb, _ptr(comp_block_table), comp_block_table.shape[1],
+        _ptr(swa_cache), swa_cache.numel() // pb, _ptr(swa_block_table), swa_block_table.shape[1],
+        page_size, _ptr(seq_lens), _ptr(gather_lens), seq_lens.shape[0], compress_ratio, M, N,
+        _ptr(ws_cache), ws_cache.numel() // pb, _stream(stream)))
+    return ws_cache
 
 
 def _attention(fn, q, kv_cache, indices, lens, sinks, softmax_scale, out, lse, page_size, stream):

@@ -144,6 +144,73 @@ int dsv4_combine_indices(const int32_t* topk, int topk_stride, int topk_width,
                     fn);
 }
 
+int dsv4_combine_indices_compressed(const int32_t* topk, int topk_stride, int topk_width,
+                                    const int32_t* topk_lens, const int32_t* query_start_loc,
+                                    const int32_t* seq_lens, const int32_t* gather_lens, int B,
+                                    int T, int top_k, int compress_ratio, int window, int M, int N,
+                                    int32_t* combined, int combined_stride, int32_t* combined_lens,
+                                    void* stream) {
+  const char* fn = "dsv4_combine_indices_compressed";
+  if (B < 0 || T < 0 || top_k < 0 || window < 0 || topk_width < 0 || topk_stride < topk_width)
+    return fail(DSV4_ERR_SHAPE, "%s: negative size or topk_stride < topk_width", fn);
+  if (compress_ratio < 1) return fail(DSV4_ERR_SHAPE, "%s: compress_ratio %d < 1", fn, compress_ratio);
+  if (N < 0 || M < N) return fail(DSV4_ERR_SHAPE, "%s: need 0 <= N <= M (N %d, M %d)", fn, N, M);
+  if ((int64_t)B * M >= ((int64_t)1 << 31))
+    return fail(DSV4_ERR_SHAPE, "%s: B * M exceeds the int32 index range", fn);
+  if (top_k > topk_width) return fail(DSV4_ERR_SHAPE, "%s: top_k %d > topk_width %d", fn, top_k, topk_width);
+  const int64_t need = ((int64_t)top_k + window + DSV4_COMBINE_ALIGN - 1) / DSV4_COMBINE_ALIGN * DSV4_COMBINE_ALIGN;
+  if (combined_stride < need)
+    return fail(DSV4_ERR_SHAPE, "%s: combined_stride %d < round_up(top_k + window, 128) = %lld", fn,
+                combined_stride, (long long)need);
+  if (B == 0 || T == 0) return ok();
+  if (!query_start_loc || !seq_lens || !gather_lens || !combined || !combined_lens ||
+      (!topk && topk_width > 0))
+    return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(combined, 4) || !aligned(combined_lens, 4) || (topk && !aligned(topk, 4)))
+    return fail(DSV4_ERR_ALIGN, "%s: int32 arrays must be 4-byte aligned", fn);
+  return hip_status(dsv4::launch_combine_compressed(topk, topk_stride, topk_width, topk_lens,
+                                                    query_start_loc, seq_lens, gather_lens, B, T,
+                                                    top_k, compress_ratio, window, M, N, combined,
+                                                    combined_stride, combined_lens,
+                                                    static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int dsv4_gather_workspace(const uint8_t* comp_cache, int comp_num_pages,
+                          const int32_t* comp_block_table, int comp_bt_stride,
+                          const uint8_t* swa_cache, int swa_num_pages,
+                          const int32_t* swa_block_table, int swa_bt_stride, int page_size,
+                          const int32_t* seq_lens, const int32_t* gather_lens, int B,
+                          int compress_ratio, int M, int N, uint8_t* ws_cache, int ws_num_pages,
+                          void* stream) {
+  const char* fn = "dsv4_gather_workspace";
+  int st = check_page(fn, page_size, comp_num_pages);
+  if (!st) st = check_page(fn, page_size, swa_num_pages);
+  if (!st) st = check_page(fn, page_size, ws_num_pages);
+  if (st) return st;
+  if (B < 0 || comp_bt_stride < 0 || swa_bt_stride < 0)
+    return fail(DSV4_ERR_SHAPE, "%s: negative size", fn);
+  if (compress_ratio < 1) return fail(DSV4_ERR_SHAPE, "%s: compress_ratio %d < 1", fn, compress_ratio);
+  if (N < 0 || M < N) return fail(DSV4_ERR_SHAPE, "%s: need 0 <= N <= M (N %d, M %d)", fn, N, M);
+  if ((int64_t)B * M >= ((int64_t)1 << 31))
+    return fail(DSV4_ERR_SHAPE, "%s: B * M exceeds the int32 index range", fn);
+  if (B == 0 || M == 0 || ws_num_pages == 0) return ok();
+  if (!seq_lens || !gather_lens || !ws_cache || (!comp_cache && comp_num_pages > 0) ||
+      (!swa_cache && swa_num_pages > 0) || (!comp_block_table && comp_bt_stride > 0) ||
+      (!swa_block_table && swa_bt_stride > 0))
+    return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(ws_cache, 16) || (comp_cache && !aligned(comp_cache, 16)) ||
+      (swa_cache && !aligned(swa_cache, 16)))
+    return fail(DSV4_ERR_ALIGN, "%s: caches must be 16-byte aligned", fn);
+  return hip_status(dsv4::launch_gather_workspace(comp_cache, comp_num_pages, comp_block_table,
+                                                  comp_bt_stride, swa_cache, swa_num_pages,
+                                                  swa_block_table, swa_bt_stride,
+                                                  dsv4::page_shift_of(page_size), seq_lens,
+                                                  gather_lens, B, compress_ratio, M, N, ws_cache,
+                                                  ws_num_pages, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
                            const int32_t* indices, int idx_stride, const int32_t* lens,
                            const float* sinks, float softmax_scale, void* out, float* lse, int T,

@@ -73,6 +73,77 @@ __global__ void __launch_bounds__(256) combine_kernel(
   }
 }
 
+// Compressed-cache form (PR #43385, the same combine kernel with COMPRESS_RATIO, M, N
+// and gather_lens): the indices address a per-request workspace of M rows, the first N
+// holding compressed entries, the next the last gather_len raw tokens of the sequence.
+// Per token at position pos: tk = min((pos+1) / ratio, top_k[, topk_lens[t]]) top-k
+// entries e -> M*b + e (0 <= e < N, else -1), then sw = min(pos+1, window) window rows
+// M*b + N + (pos-sw+1+r - gather_start), -1 when outside the gathered tokens or past the
+// request's M rows; no dedup (two index spaces).  Integer only: bit-exact by design.
+__global__ void __launch_bounds__(256) combine_compressed_kernel(
+    const int32_t* __restrict__ topk, int topk_stride, int topk_width,
+    const int32_t* __restrict__ topk_lens, const int32_t* __restrict__ qsl,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ gather_lens, int T,
+    int top_k, int ratio, int window, int M, int N, int32_t* __restrict__ combined,
+    int combined_stride, int32_t* __restrict__ combined_lens) {
+  const int b = blockIdx.x;
+  const int base = qsl[0];
+  const int q0 = qsl[b] - base;
+  const int qlen = qsl[b + 1] - qsl[b];
+  const int seq_len = seq_lens[b];
+  const int gl = gather_lens[b];
+  const int64_t gather_start = (int64_t)seq_len - gl;
+  const int64_t row0 = (int64_t)M * b;
+  for (int i = blockIdx.y; i < qlen; i += gridDim.y) {
+    const int64_t t = (int64_t)q0 + i;
+    if (t < 0 || t >= T) continue;
+    const int64_t pos = (int64_t)seq_len - qlen + i;
+    int64_t tk = pos + 1 >= 0 ? (pos + 1) / ratio : 0;
+    tk = min(tk, (int64_t)top_k);
+    if (topk_lens) tk = min(tk, (int64_t)topk_lens[t]);
+    tk = max(tk, (int64_t)0);
+    const int64_t sw = max(min(pos + 1, (int64_t)window), (int64_t)0);
+    const int64_t k0 = pos - sw + 1 - gather_start;  // gathered-token row of the first window entry
+    const int32_t* trow = topk + t * topk_stride;
+    int32_t* crow = combined + t * combined_stride;
+    for (int jb = 0; jb < combined_stride; jb += 256 * kColsPerThread) {
+      int32_t v[kColsPerThread];
+#pragma unroll
+      for (int k = 0; k < kColsPerThread; ++k) {
+        const int j = jb + threadIdx.x + 256 * k;
+        int64_t e = -1;
+        if (j < tk) e = j < topk_width ? (int64_t)trow[j] : -1;
+        v[k] = (j < tk && e >= 0 && e < N) ? (int32_t)(row0 + e) : -1;
+      }
+#pragma unroll
+      for (int k = 0; k < kColsPerThread; ++k) {
+        const int j = jb + threadIdx.x + 256 * k;
+        if (j >= tk && j < tk + sw) {
+          const int64_t kk = k0 + (j - tk);
+          v[k] = (kk >= 0 && kk < gl && N + kk < M) ? (int32_t)(row0 + N + kk) : -1;
+        }
+        if (j < combined_stride) crow[j] = v[k];
+      }
+    }
+    if (threadIdx.x == 0) combined_lens[t] = (int32_t)(tk + sw);
+  }
+}
+
+hipError_t launch_combine_compressed(const int32_t* topk, int topk_stride, int topk_width,
+                                     const int32_t* topk_lens, const int32_t* qsl,
+                                     const int32_t* seq_lens, const int32_t* gather_lens, int B,
+                                     int T, int top_k, int ratio, int window, int M, int N,
+                                     int32_t* combined, int combined_stride,
+                                     int32_t* combined_lens, hipStream_t stream) {
+  if (B == 0 || T == 0) return hipSuccess;
+  int per_req = (T + B - 1) / B;
+  int Y = per_req < 1 ? 1 : (per_req > 2048 ? 2048 : per_req);
+  hipLaunchKernelGGL(combine_compressed_kernel, dim3(B, Y), dim3(256), 0, stream, topk,
+                     topk_stride, topk_width, topk_lens, qsl, seq_lens, gather_lens, T, top_k,
+                     ratio, window, M, N, combined, combined_stride, combined_lens);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const int32_t* topk, int topk_stride, int topk_width,
                           const int32_t* topk_lens, const int32_t* qsl, const int32_t* seq_lens,
                           const int32_t* block_table, int bt_stride, int B, int T, int top_k,

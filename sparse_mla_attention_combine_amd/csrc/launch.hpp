@@ -17,6 +17,23 @@ hipError_t launch_combine(const int32_t* topk, int topk_stride, int topk_width,
                           int window, int page_shift, int32_t* combined, int combined_stride,
                           int32_t* combined_lens, hipStream_t stream);
 
+// Compressed-cache form of the combine: indices into a per-request workspace of M rows.
+hipError_t launch_combine_compressed(const int32_t* topk, int topk_stride, int topk_width,
+                                     const int32_t* topk_lens, const int32_t* qsl,
+                                     const int32_t* seq_lens, const int32_t* gather_lens, int B,
+                                     int T, int top_k, int ratio, int window, int M, int N,
+                                     int32_t* combined, int combined_stride,
+                                     int32_t* combined_lens, hipStream_t stream);
+
+// Fills that workspace (a cache of ws_num_pages pages) from the compressed and raw caches.
+hipError_t launch_gather_workspace(const uint8_t* comp_cache, int comp_num_pages,
+                                   const int32_t* comp_bt, int comp_bt_stride,
+                                   const uint8_t* swa_cache, int swa_num_pages,
+                                   const int32_t* swa_bt, int swa_bt_stride, int page_shift,
+                                   const int32_t* seq_lens, const int32_t* gather_lens, int B,
+                                   int ratio, int M, int N, uint8_t* ws, int ws_num_pages,
+                                   hipStream_t stream);
+
 hipError_t launch_insert(void* q, const void* kv, const int64_t* positions,
                          const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                          const void* weight, float eps, uint8_t* cache, int num_pages,

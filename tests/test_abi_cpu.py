@@ -110,6 +110,46 @@ def test_combine_validation(dsv4):
     assert call(T=0) == 0
 
 
+def test_compressed_combine_and_workspace_validation(dsv4):
+    lib = dsv4.library()
+    keep, p = _fake()
+
+    def comb(**kw):
+        a = dict(topk=p, ts=512, tw=512, tl=None, qsl=p, sl=p, gl=p, B=4, T=4, top_k=512, r=4,
+                 window=128, M=4096, N=2048, comb=p, cs=640, cl=p)
+        a.update(kw)
+        return lib.dsv4_combine_indices_compressed(
+            a["topk"], a["ts"], a["tw"], a["tl"], a["qsl"], a["sl"], a["gl"], a["B"], a["T"],
+            a["top_k"], a["r"], a["window"], a["M"], a["N"], a["comb"], a["cs"], a["cl"], None)
+
+    assert comb(r=0) == 2 and b"compress_ratio" in lib.dsv4_last_error()
+    assert comb(N=5000) == 2
+    assert comb(N=-1) == 2
+    assert comb(B=1 << 20, M=1 << 12) == 2
+    assert comb(cs=600) == 2
+    assert comb(top_k=600) == 2
+    assert comb(gl=None) == 1
+    assert comb(comb=ctypes.c_void_p(p.value + 2)) == 3
+    assert comb(T=0) == 0
+
+    def ws(**kw):
+        a = dict(cc=p, cn=4, cbt=p, cbs=8, sc=p, sn=4, sbt=p, sbs=8, P=64, sl=p, gl=p, B=2, r=4,
+                 M=300, N=100, ws=p, wn=10)
+        a.update(kw)
+        return lib.dsv4_gather_workspace(a["cc"], a["cn"], a["cbt"], a["cbs"], a["sc"], a["sn"],
+                                         a["sbt"], a["sbs"], a["P"], a["sl"], a["gl"], a["B"], a["r"],
+                                         a["M"], a["N"], a["ws"], a["wn"], None)
+
+    assert ws(P=128) == 4
+    assert ws(r=0) == 2
+    assert ws(N=301) == 2
+    assert ws(cn=-1) == 2
+    assert ws(sl=None) == 1
+    assert ws(ws=None) == 1
+    assert ws(ws=ctypes.c_void_p(p.value + 8)) == 3
+    assert ws(B=0) == 0 and ws(wn=0) == 0
+
+
 def test_insert_and_gather_validation(dsv4):
     lib = dsv4.library()
     keep, p = _fake()
