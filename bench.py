@@ -80,6 +80,10 @@ def parse():
     ap.add_argument("--splits", type=int, default=1,
                     help="pieces per index row for dsv4_sparse_mla_decode_split (1 = the "
                          "one-workgroup-per-(token, head group) decode)")
+    ap.add_argument("--workload", choices=["decode", "compressed-prefill"], default="decode",
+                    help="decode (default: the headline decode step) or compressed-prefill (one "
+                         "8192-token sequence over a 4x compressed cache: insert + compressed "
+                         "combine + workspace fill + prefill attention)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device-to-device copy 3 times (the known-size "
                          "kernel that scales FETCH_SIZE / WRITE_SIZE counter readings)")
@@ -105,6 +109,8 @@ def main():
         return
     import sparse_mla_attention_combine_amd as dsv4
     from synth_inputs import attention_workload, bf16_normal
+    if args.workload == "compressed-prefill":
+        return bench_compressed_prefill(args, torch, dsv4)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -325,6 +331,129 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inst[0], calls, H, T, W)
+    print(json.dumps(result), flush=True)
+
+
+def bench_compressed_prefill(args, torch, dsv4):
+    """One 8192-token prefill over a compressed cache (ratio 4: 2048 compressed entries)
+    plus the raw window cache, H = 64, top-k 2048, window 128.  A step: dsv4_kv_insert
+    (q norm/RoPE in place + the 8192 raw rows into the window cache),
+    dsv4_combine_indices_compressed, dsv4_gather_workspace (M = 10240 rows),
+    dsv4_sparse_mla_prefill over the workspace; captured once into a HIP graph and
+    replayed; per-kernel times from a separate eager pass with HIP events."""
+    from synth_inputs import compressed_prefill_workload
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    wl = compressed_prefill_workload(seed=args.seed)
+    L, H, P, M, N, W = wl["L"], wl["H"], wl["P"], wl["M"], wl["N"], wl["W"]
+    log(f"[bench] compressed prefill workload in {time.time() - t0:.1f}s: L={L} H={H} ratio={wl['ratio']} "
+        f"N={N} M={M} W={W}")
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def dv(a, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).to(dev)
+
+    comp = dsv4.new_cache(wl["comp_pages"], page_size=P)
+    swa = dsv4.new_cache(wl["swa_pages"], page_size=P)
+    ws_pages = (M + P - 1) // P
+    ws = dsv4.new_cache(ws_pages, page_size=P)
+    cos_sin = dv(wl["cos_sin"], np.float32)
+    dsv4.dsv4_kv_insert(None, bf(wl["comp_kv"]), dv(wl["comp_positions"], np.int64),
+                        dv(wl["comp_slots"], np.int64), cos_sin, None, wl["eps"], comp, page_size=P)
+    q, kv = bf(wl["q"]), bf(wl["kv"])
+    positions, swa_slots = dv(wl["positions"], np.int64), dv(wl["swa_slots"], np.int64)
+    weight = bf(wl["q_norm_weight"])
+    topk = dv(wl["topk"], np.int32)
+    qsl, seq_lens, gl = dv(wl["qsl"], np.int32), dv(wl["seq_lens"], np.int32), dv(wl["gather_lens"], np.int32)
+    comp_bt, swa_bt = dv(wl["comp_bt"], np.int32), dv(wl["swa_bt"], np.int32)
+    sinks = dv(wl["sinks"], np.float32)
+    comb = torch.empty(L, W, dtype=torch.int32, device=dev)
+    lens = torch.empty(L, dtype=torch.int32, device=dev)
+    out = torch.empty(L, H, NOPE, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def run(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(torch.cuda.current_stream())
+        mark(0)
+        dsv4.dsv4_kv_insert(q, kv, positions, swa_slots, cos_sin, weight, wl["eps"], swa, page_size=P)
+        mark(1)
+        dsv4.dsv4_combine_indices_compressed(topk, None, qsl, seq_lens, gl, wl["top_k"], wl["ratio"],
+                                             wl["window"], M, N, comb, lens)
+        mark(2)
+        dsv4.dsv4_gather_workspace(comp, comp_bt, swa, swa_bt, seq_lens, gl, wl["ratio"], M, N, ws,
+                                   page_size=P)
+        mark(3)
+        dsv4.dsv4_sparse_mla_prefill(q, ws, comb, lens, sinks, wl["softmax_scale"], out, page_size=P)
+        mark(4)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        run()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        run(evs[k])
+    torch.cuda.synchronize()
+    kt = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs]) * 1e3  # us
+
+    c = comb.cpu().numpy()
+    ln = lens.cpu().numpy()
+    valid = (np.arange(W)[None, :] < ln[:, None]) & (c >= 0) & (c < ws_pages * P)
+    nv = int(valid.sum())
+    rows = int(np.unique(c[valid]).size)
+    attn_s = float(kt[:, 3].mean()) * 1e-6
+    flops = 2.0 * H * (LATENT + NOPE) * nv
+    bytes_alg = RECORD * rows + L * H * (LATENT + NOPE) * 2 + 4.0 * float(ln.sum()) + 4.0 * L + 4.0 * H
+    tflops, gbs = flops / attn_s / 1e12, bytes_alg / attn_s / 1e9
+    bound = "mfma" if flops / (PEAK_BF16_TFLOPS * 1e12) >= bytes_alg / (PEAK_HBM_GBS * 1e9) else "hbm"
+    ws_bytes = 2.0 * RECORD * M
+    log(f"[bench] {args.steps} steps (graph replays) in {elapsed * 1e3:.1f} ms -> {elapsed / args.steps * 1e3:.3f} ms/step; "
+        f"kernel means: insert {kt[:, 0].mean():.1f} us, combine {kt[:, 1].mean():.1f} us, "
+        f"workspace {kt[:, 2].mean():.1f} us ({ws_bytes / (kt[:, 2].mean() * 1e-6) / 1e9:.0f} GB/s), "
+        f"attention {kt[:, 3].mean():.1f} us")
+    log(f"[bench] attention: {nv} slot visits, {rows} distinct rows, {flops / 1e12:.3f} TFLOP -> "
+        f"{tflops:.0f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS * 100:.1f}% of bf16 MFMA)")
+    result = {
+        "metric": "sparse MLA compressed-cache prefill query-tokens/s + % of MFMA roofline "
+                  "(L=8192, H=64, ratio 4, k=2048)",
+        "value": round(L * args.steps / elapsed, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "compressed-cache sparse MLA prefill: fused q-norm/RoPE/FP8 insert + "
+                               "compressed top-k/window index combine + workspace fill + sparse "
+                               "MLA over the workspace",
+                   "tokens": L, "heads": H, "compress_ratio": wl["ratio"], "top_k": wl["top_k"],
+                   "window": wl["window"], "N": N, "M": M, "page_size": P, "sinks": True},
+        "roofline": {"bound": bound,
+                     "achieved": round(tflops if bound == "mfma" else gbs, 2),
+                     "peak": PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS,
+                     "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None,
+                     "kernel": "sparse_mla_kernel<2> (dsv4_sparse_mla_prefill over the workspace)",
+                     "launch_us": round(attn_s * 1e6, 2), "alg_flops": flops, "alg_bytes": bytes_alg},
+        "kernels_us": {"kv_insert": round(float(kt[:, 0].mean()), 2),
+                       "combine_indices_compressed": round(float(kt[:, 1].mean()), 2),
+                       "gather_workspace": round(float(kt[:, 2].mean()), 2),
+                       "sparse_mla_prefill": round(float(kt[:, 3].mean()), 2)},
+    }
     print(json.dumps(result), flush=True)
 
 

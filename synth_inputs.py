@@ -203,3 +203,40 @@ def insert_workload(seed: int = 1, T: int = 4096, H: int = 128, requests: int = 
     return dict(T=T, H=H, requests=requests, num_pages=num_pages, page_size=PAGE, q=q, kv=kv,
                 positions=positions, slot_mapping=slots, q_norm_weight=weight, eps=1e-6,
                 cos_sin=rope_table(max_pos))
+
+
+def compressed_prefill_workload(seed: int = 5, L: int = 8192, H: int = 64, ratio: int = 4,
+                                top_k: int = 2048, window: int = 128, P: int = PAGE):
+    """One sequence of L query tokens over a compressed KV cache (every `ratio` tokens
+    summarised into one entry) plus the raw window cache: top-k min((pos+1)//ratio, top_k)
+    distinct uniform compressed entries in [0, (pos+1)//ratio) per token (causal), window
+    `window`, every raw token gathered (gather_len = L), sinks ~ N(0,1).  The compressed
+    rows are N(0,1) stand-ins for a compressor's output (which needs trained weights);
+    each is inserted at position e*ratio + ratio - 1, the last token it covers.  Two
+    caches, each with its own seeded random page order."""
+    r = _streams(seed)
+    N = L // ratio
+    q = bf16_normal(r["q"], (L, H, LATENT))
+    kv = bf16_normal(r["kv"], (L, LATENT))
+    comp_kv = bf16_normal(r["kv"], (N, LATENT))
+    topk = np.full((L, top_k), -1, np.int32)
+    for pos in range(L):
+        hi = (pos + 1) // ratio
+        n = min(hi, top_k)
+        topk[pos, :n] = _distinct(r["topk"], hi, n)
+    sinks = r["sinks"].standard_normal(H).astype(np.float32)
+    comp_bt, comp_pages = _block_table(r["perm"], [N], P)
+    swa_bt, swa_pages = _block_table(r["perm"], [L], P)
+    pos = np.arange(L, dtype=np.int64)
+    swa_slots = swa_bt[0, pos // P].astype(np.int64) * P + pos % P
+    e = np.arange(N, dtype=np.int64)
+    comp_slots = comp_bt[0, e // P].astype(np.int64) * P + e % P
+    weight = bf16_normal(r["weight"], (LATENT,), mean=1.0, std=0.1)
+    return dict(L=L, H=H, ratio=ratio, top_k=top_k, window=window, P=P, N=N, M=N + L,
+                W=round_up(top_k + window, ALIGN), q=q, kv=kv, comp_kv=comp_kv, topk=topk,
+                sinks=sinks, comp_bt=comp_bt, comp_pages=comp_pages, swa_bt=swa_bt,
+                swa_pages=swa_pages, positions=pos, swa_slots=swa_slots,
+                comp_positions=e * ratio + ratio - 1, comp_slots=comp_slots, q_norm_weight=weight,
+                eps=1e-6, cos_sin=rope_table(L), qsl=np.array([0, L], np.int32),
+                seq_lens=np.array([L], np.int32), gather_lens=np.array([L], np.int32),
+                softmax_scale=1.0 / math.sqrt(LATENT))
