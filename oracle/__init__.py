@@ -54,11 +54,13 @@ def lib() -> ctypes.CDLL:
                                                 i32, i32, i32, vp, i32, vp]
         L.oracle_gather_workspace.argtypes = [vp, i32, vp, i32, vp, i32, vp, i32, i32, vp, vp, i32,
                                               i32, i32, i32, vp, i32]
+        L.oracle_indexer_topk.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp]
         L.oracle_kv_insert.argtypes = [vp, vp, vp, vp, vp, i32, vp, dbl, vp, i32, i32, i32, i32]
         L.oracle_sparse_mla.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, dbl, vp, vp, i32, i32,
                                         i32]
         for f in (L.oracle_gather_dequant, L.oracle_combine, L.oracle_combine_compressed,
-                  L.oracle_gather_workspace, L.oracle_kv_insert, L.oracle_sparse_mla):
+                  L.oracle_gather_workspace, L.oracle_indexer_topk, L.oracle_kv_insert,
+                  L.oracle_sparse_mla):
             f.restype = None
         _lib = L
     return _lib
@@ -157,6 +159,19 @@ def gather_workspace(comp_cache, comp_num_pages, comp_bt, swa_cache, swa_num_pag
                                   _ptr(swa_bt), swa_bt.shape[1], page_size, _ptr(seq_lens),
                                   _ptr(gl), seq_lens.shape[0], ratio, M, N, _ptr(out), ws_num_pages)
     return out
+
+
+def indexer_topk(logits, qsl, seq_lens, T, ratio, top_k, topk_stride, fill=-7):
+    """Top-k candidate ids ``[T, topk_stride]`` (ascending, -1 padded) and their counts
+    ``[T]`` from per-token indexer logits ``[T, n]`` (fp32); rows of tokens no request
+    covers keep ``fill``."""
+    lg = _c(logits, np.float32)
+    qsl, seq_lens = _c(qsl, np.int32), _c(seq_lens, np.int32)
+    out = np.full((T, topk_stride), fill, np.int32)
+    lens = np.full((T,), fill, np.int32)
+    lib().oracle_indexer_topk(_ptr(lg), lg.shape[1], _ptr(qsl), _ptr(seq_lens), seq_lens.shape[0],
+                              T, ratio, top_k, _ptr(out), topk_stride, _ptr(lens))
+    return out, lens
 
 
 def kv_insert(q_bits, kv_bits, positions, slot_mapping, cos_sin, weight_bits, eps, cache,

@@ -332,6 +332,65 @@ void oracle_gather_workspace(const uint8_t* comp_cache, int comp_num_pages, cons
 }
 
 /* ------------------------------------------------------------------------------- */
+/* Before step 1: the indexer's top-k selection [p1 item 2 and Key files: the MLA      */
+/* layer integrates an Indexer whose top-k picks feed the sparse backend; p3 combine   */
+/* kernel: top-k entries are compressed-entry ids below (pos+1) / COMPRESS_RATIO].     */
+/* Per token at position pos: the candidates are ids 0 .. n-1, n = min((pos+1) /      */
+/* ratio, logits_stride); the result is the set of the min(n, top_k) candidates with   */
+/* the largest logits, ties going to the smaller id, listed in ascending id order,     */
+/* then -1 up to topk_stride; topk_lens[t] = min(n, top_k).  Readings: the pages name  */
+/* the step but not its tie rule or output order; ascending ids make the result unique */
+/* (and the later gathers ordered); a NaN logit counts as -inf.                        */
+/* ------------------------------------------------------------------------------- */
+
+typedef struct {
+  float v;
+  int32_t id;
+} scored;
+
+static int by_score(const void* a, const void* b) {
+  const scored* x = (const scored*)a;
+  const scored* y = (const scored*)b;
+  if (x->v > y->v) return -1;
+  if (x->v < y->v) return 1;
+  return x->id < y->id ? -1 : (x->id > y->id ? 1 : 0);
+}
+
+static int by_id(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+void oracle_indexer_topk(const float* logits, int logits_stride, const int32_t* qsl,
+                         const int32_t* seq_lens, int B, int T, int ratio, int top_k,
+                         int32_t* topk, int topk_stride, int32_t* topk_lens) {
+  scored* buf = (scored*)malloc(sizeof(scored) * (size_t)(logits_stride > 0 ? logits_stride : 1));
+  for (int b = 0; b < B; ++b) {
+    int qlen = qsl[b + 1] - qsl[b];
+    for (int i = 0; i < qlen; ++i) {
+      int64_t t = (int64_t)qsl[b] - qsl[0] + i;
+      if (t < 0 || t >= T) continue;
+      int64_t pos = (int64_t)seq_lens[b] - qlen + i;
+      int64_t n = pos + 1 > 0 ? (pos + 1) / ratio : 0;
+      if (n > logits_stride) n = logits_stride;
+      for (int64_t c = 0; c < n; ++c) {
+        float v = logits[t * (int64_t)logits_stride + c];
+        buf[c].v = isnan(v) ? -INFINITY : v;
+        buf[c].id = (int32_t)c;
+      }
+      qsort(buf, (size_t)n, sizeof(scored), by_score);
+      int64_t k = n < top_k ? n : top_k;
+      int32_t* row = topk + t * (int64_t)topk_stride;
+      for (int64_t j = 0; j < k; ++j) row[j] = buf[j].id;
+      qsort(row, (size_t)k, sizeof(int32_t), by_id);
+      for (int64_t j = k; j < topk_stride; ++j) row[j] = -1;
+      topk_lens[t] = (int32_t)k;
+    }
+  }
+  free(buf);
+}
+
+/* ------------------------------------------------------------------------------- */
 /* Step 4 (fused insert) [p2 Implementation breakdown item 4: per-head q RMSNorm,      */
 /* GPT-J RoPE, FP8 UE8M0 KV insert; Key source excerpts: xpu_sparse.py calls it with   */
 /* (q, kv, kv_cache, slot_mapping, positions); p1 item 2 "RMSNorm+Rope+Quant"].        */
