@@ -150,6 +150,28 @@ int dsv4_combine_indices(const int32_t* topk, int topk_stride, int topk_width,
                          int32_t* combined_lens, void* stream);
 
 /*
+ * dsv4_indexer_topk — the indexer's top-k selection that feeds the combine step
+ * [p1 Implementation breakdown item 2 and Key files: the MLA layer integrates an Indexer
+ * whose picks feed the sparse backend; p3 combine kernel: top-k ids are compressed
+ * entries below (pos+1) / COMPRESS_RATIO].  For request b's i-th token t, at
+ * pos = seq_lens[b]-qlen+i, the candidates are ids 0..n-1 with
+ * n = min((pos+1) / compress_ratio, logits_stride) (floor; 0 when pos < 0):
+ *   topk[t][0..k)   = the k = min(n, top_k) ids with the largest logits[t][id], ties
+ *                     to the smaller id, a NaN counting as -inf, in ascending id order;
+ *   topk[t][k..)    = -1 up to topk_stride;   topk_lens[t] = k.
+ * (The pages name the step, not its tie rule or order: ascending ids make the result
+ * unique.)  Tokens of no request are not written.  The output is the topk / topk_lens
+ * input of dsv4_combine_indices (compress_ratio 1: ids are positions) and of
+ * dsv4_combine_indices_compressed.
+ *   logits int32-aligned fp32 [T][logits_stride]; topk int32 [T][topk_stride];
+ *   topk_lens int32 [T]; query_start_loc int32 [B+1]; seq_lens int32 [B]
+ * Requires compress_ratio >= 1, topk_stride >= top_k >= 0.
+ */
+int dsv4_indexer_topk(const float* logits, int logits_stride, const int32_t* query_start_loc,
+                      const int32_t* seq_lens, int B, int T, int compress_ratio, int top_k,
+                      int32_t* topk, int topk_stride, int32_t* topk_lens, void* stream);
+
+/*
  * dsv4_combine_indices_compressed — the combine step for a compressed KV cache, where
  * top-k picks compressed entries and the window picks raw tokens: two index spaces
  * [p3 Key source excerpts: rocm.py combine kernel with COMPRESS_RATIO, M, N and

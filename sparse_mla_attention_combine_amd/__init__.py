@@ -5,7 +5,7 @@ has the C entry point's name, takes torch tensors that already live on the GPU, 
 their device pointers and the current HIP stream, and raises on a non-zero status.
 Every step of the path runs in the library's HIP kernels; there is no fallback.  If
 the library has not been built the import fails (run
-``python -m sparse_mla_attention_combine_amd.build``).
+``python sparse_mla_attention_combine_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -21,7 +21,7 @@ LATENT_DIM, NOPE_DIM, ROPE_DIM, RECORD_BYTES, COMBINE_ALIGN = 576, 512, 64, 648,
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m sparse_mla_attention_combine_amd.build`")
+                      "`python sparse_mla_attention_combine_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i32, _f32, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
@@ -42,18 +42,21 @@ _lib.dsv4_sparse_mla_split_workspace_bytes.restype = ctypes.c_size_t
 _lib.dsv4_sparse_mla_decode_split.argtypes = _attn_args[:-1] + [_i32, _vp, ctypes.c_size_t, _vp]
 _lib.dsv4_combine_indices_compressed.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]
+_lib.dsv4_indexer_topk.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp,
+                                   _vp]
 _lib.dsv4_gather_workspace.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp,
                                        _i32, _i32, _i32, _i32, _vp, _i32, _vp]
 for _f in (_lib.dsv4_kv_insert, _lib.dsv4_combine_indices, _lib.dsv4_sparse_mla_decode,
            _lib.dsv4_sparse_mla_prefill, _lib.dsv4_gather_dequant, _lib.dsv4_sparse_mla_decode_split,
-           _lib.dsv4_combine_indices_compressed, _lib.dsv4_gather_workspace):
+           _lib.dsv4_combine_indices_compressed, _lib.dsv4_gather_workspace,
+           _lib.dsv4_indexer_topk):
     _f.restype = _i32
 
 EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4_kv_insert",
             "dsv4_combine_indices", "dsv4_sparse_mla_decode", "dsv4_sparse_mla_prefill",
             "dsv4_gather_dequant", "dsv4_sparse_mla_split_workspace_bytes",
             "dsv4_sparse_mla_decode_split", "dsv4_combine_indices_compressed",
-            "dsv4_gather_workspace"]
+            "dsv4_gather_workspace", "dsv4_indexer_topk"]
 
 
 class Dsv4Error(RuntimeError):
@@ -153,6 +156,20 @@ def dsv4_combine_indices_compressed(topk, topk_lens, query_start_loc, seq_lens, 
         _ptr(topk), topk.shape[1], width, _ptr(topk_lens), _ptr(query_start_loc), _ptr(seq_lens),
         _ptr(gather_lens), B, T, top_k, compress_ratio, window, M, N, _ptr(combined),
         combined.shape[1], _ptr(combined_lens), _stream(stream)))
+
+
+def dsv4_indexer_topk(logits, query_start_loc, seq_lens, top_k, topk, topk_lens, compress_ratio=1,
+                      stream=None):
+    """logits fp32 [T, n] per-token indexer scores -> topk int32 [T, stride] (the top_k
+    largest causal candidates, ascending ids, -1 padded) and topk_lens int32 [T]."""
+    _want(logits, torch.float32, "logits")
+    for t, n in ((query_start_loc, "query_start_loc"), (seq_lens, "seq_lens"), (topk, "topk"),
+                 (topk_lens, "topk_lens")):
+        _want(t, torch.int32, n)
+    _check(_lib.dsv4_indexer_topk(_ptr(logits), logits.shape[1], _ptr(query_start_loc),
+                                  _ptr(seq_lens), seq_lens.shape[0], topk.shape[0], compress_ratio,
+                                  top_k, _ptr(topk), topk.shape[1], _ptr(topk_lens),
+                                  _stream(stream)))
 
 
 def dsv4_gather_workspace(comp_cache, comp_block_table, swa_cache, swa_block_table, seq_lens,

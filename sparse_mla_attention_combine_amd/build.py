@@ -1,6 +1,6 @@
 """Build libdsv4.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-    python -m sparse_mla_attention_combine_amd.build [--verbose]
+    python sparse_mla_attention_combine_amd/build.py [--verbose]
 
 Every source is compiled to an object in parallel, then linked into
 ``sparse_mla_attention_combine_amd/_lib/libdsv4.so``.  hipcc cross-compiles, so this
@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libdsv4.so")
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "combine.hip", "insert.hip", "gather.hip", "attention.hip", "workspace.hip"]
+SOURCES = ["api.cpp", "combine.hip", "insert.hip", "gather.hip", "attention.hip", "workspace.hip",
+           "indexer.hip"]
 # Packed FP32 instructions are disabled for all device code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Wno-unused-result", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -176,6 +176,26 @@ int dsv4_combine_indices_compressed(const int32_t* topk, int topk_stride, int to
                     fn);
 }
 
+int dsv4_indexer_topk(const float* logits, int logits_stride, const int32_t* query_start_loc,
+                      const int32_t* seq_lens, int B, int T, int compress_ratio, int top_k,
+                      int32_t* topk, int topk_stride, int32_t* topk_lens, void* stream) {
+  const char* fn = "dsv4_indexer_topk";
+  if (B < 0 || T < 0 || top_k < 0 || logits_stride < 0)
+    return fail(DSV4_ERR_SHAPE, "%s: negative size", fn);
+  if (compress_ratio < 1) return fail(DSV4_ERR_SHAPE, "%s: compress_ratio %d < 1", fn, compress_ratio);
+  if (topk_stride < top_k)
+    return fail(DSV4_ERR_SHAPE, "%s: topk_stride %d < top_k %d", fn, topk_stride, top_k);
+  if (B == 0 || T == 0) return ok();
+  if (!query_start_loc || !seq_lens || !topk || !topk_lens || (!logits && logits_stride > 0))
+    return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if ((logits && !aligned(logits, 4)) || !aligned(topk, 4) || !aligned(topk_lens, 4))
+    return fail(DSV4_ERR_ALIGN, "%s: arrays must be 4-byte aligned", fn);
+  return hip_status(dsv4::launch_indexer_topk(logits, logits_stride, query_start_loc, seq_lens, B,
+                                              T, compress_ratio, top_k, topk, topk_stride,
+                                              topk_lens, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int dsv4_gather_workspace(const uint8_t* comp_cache, int comp_num_pages,
                           const int32_t* comp_block_table, int comp_bt_stride,
                           const uint8_t* swa_cache, int swa_num_pages,

@@ -34,6 +34,12 @@ hipError_t launch_gather_workspace(const uint8_t* comp_cache, int comp_num_pages
                                    int ratio, int M, int N, uint8_t* ws, int ws_num_pages,
                                    hipStream_t stream);
 
+// Indexer top-k: the top_k largest-logit causal candidates per token, ascending ids.
+hipError_t launch_indexer_topk(const float* logits, int logits_stride, const int32_t* qsl,
+                               const int32_t* seq_lens, int B, int T, int ratio, int top_k,
+                               int32_t* topk, int topk_stride, int32_t* topk_lens,
+                               hipStream_t stream);
+
 hipError_t launch_insert(void* q, const void* kv, const int64_t* positions,
                          const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                          const void* weight, float eps, uint8_t* cache, int num_pages,

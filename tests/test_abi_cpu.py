@@ -150,6 +150,25 @@ def test_compressed_combine_and_workspace_validation(dsv4):
     assert ws(B=0) == 0 and ws(wn=0) == 0
 
 
+def test_indexer_topk_validation(dsv4):
+    lib = dsv4.library()
+    keep, p = _fake()
+
+    def call(**kw):
+        a = dict(lg=p, ls=4096, qsl=p, sl=p, B=2, T=2, r=1, k=2048, out=p, os=2048, ol=p)
+        a.update(kw)
+        return lib.dsv4_indexer_topk(a["lg"], a["ls"], a["qsl"], a["sl"], a["B"], a["T"], a["r"],
+                                     a["k"], a["out"], a["os"], a["ol"], None)
+
+    assert call(r=0) == 2
+    assert call(os=100) == 2 and b"topk_stride" in lib.dsv4_last_error()
+    assert call(k=-1) == 2
+    assert call(qsl=None) == 1
+    assert call(lg=None) == 1
+    assert call(out=ctypes.c_void_p(p.value + 2)) == 3
+    assert call(T=0) == 0
+
+
 def test_insert_and_gather_validation(dsv4):
     lib = dsv4.library()
     keep, p = _fake()
