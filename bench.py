@@ -80,10 +80,14 @@ def parse():
     ap.add_argument("--splits", type=int, default=1,
                     help="pieces per index row for dsv4_sparse_mla_decode_split (1 = the "
                          "one-workgroup-per-(token, head group) decode)")
-    ap.add_argument("--workload", choices=["decode", "compressed-prefill"], default="decode",
+    ap.add_argument("--page-size", type=int, default=64, choices=[32, 64, 256],
+                    help="cache page size of the decode workload (default 64)")
+    ap.add_argument("--workload", choices=["decode", "compressed-prefill", "indexer"],
+                    default="decode",
                     help="decode (default: the headline decode step) or compressed-prefill (one "
                          "8192-token sequence over a 4x compressed cache: insert + compressed "
-                         "combine + workspace fill + prefill attention)")
+                         "combine + workspace fill + prefill attention) or indexer (the top-k "
+                         "selection over 64 x 32768 indexer logits, top-k 2048)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device-to-device copy 3 times (the known-size "
                          "kernel that scales FETCH_SIZE / WRITE_SIZE counter readings)")
@@ -111,11 +115,14 @@ def main():
     from synth_inputs import attention_workload, bf16_normal
     if args.workload == "compressed-prefill":
         return bench_compressed_prefill(args, torch, dsv4)
+    if args.workload == "indexer":
+        return bench_indexer(args, torch, dsv4)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
-    wl = attention_workload(2, seed=args.seed, instances=args.instances)
+    PS = args.page_size
+    wl = attention_workload(2, seed=args.seed, instances=args.instances, page_size=PS)
     if not 1 <= args.batch <= wl["T"]:
         print(f"bench.py: --batch must be in 1..{wl['T']}", file=sys.stderr)
         sys.exit(2)
@@ -137,16 +144,17 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).to(dev)
 
     # cache filled by the library's own insert (cache-only: no q heads)
-    cache = dsv4.new_cache(npg)
+    cache = dsv4.new_cache(npg, page_size=PS)
     cos_sin = to_dev(wl["cos_sin"], np.float32)
     weight = to_bf16(wl["q_norm_weight"])
     dsv4.dsv4_kv_insert(None, to_bf16(wl["ctx_kv"]), to_dev(wl["ctx_pos"], np.int64),
-                        to_dev(wl["ctx_slot"], np.int64), cos_sin, None, wl["eps"], cache)
+                        to_dev(wl["ctx_slot"], np.int64), cos_sin, None, wl["eps"], cache,
+                        page_size=PS)
     qsl = to_dev(wl["qsl"], np.int32)
     seq_lens = to_dev(wl["seq_lens"], np.int32)
     bt = to_dev(wl["block_table"], np.int32)
     pos_np = (wl["seq_lens"].astype(np.int64) - 1)
-    slot_np = wl["block_table"][np.arange(T), pos_np // 64].astype(np.int64) * 64 + pos_np % 64
+    slot_np = wl["block_table"][np.arange(T), pos_np // PS].astype(np.int64) * PS + pos_np % PS
     positions = to_dev(pos_np, np.int64)
     slot_mapping = to_dev(slot_np, np.int64)
     rng = np.random.default_rng(1000 + args.seed)
@@ -175,12 +183,12 @@ def main():
     for d in inst:
         ins = (P(d["q"].data_ptr()), P(d["kv"].data_ptr()), P(positions.data_ptr()),
                P(slot_mapping.data_ptr()), P(cos_sin.data_ptr()), cos_sin.shape[0],
-               P(weight.data_ptr()), ctypes.c_float(wl["eps"]), P(cache.data_ptr()), npg, 64, T, H, sp)
+               P(weight.data_ptr()), ctypes.c_float(wl["eps"]), P(cache.data_ptr()), npg, PS, T, H, sp)
         comb = (P(d["topk"].data_ptr()), d["topk"].shape[1], d["topk"].shape[1],
                 P(d["topk_lens"].data_ptr()), P(qsl.data_ptr()), P(seq_lens.data_ptr()),
-                P(bt.data_ptr()), bt.shape[1], wl["B"], T, wl["top_k"], wl["window"], 64,
+                P(bt.data_ptr()), bt.shape[1], wl["B"], T, wl["top_k"], wl["window"], PS,
                 P(d["comb"].data_ptr()), W, P(d["lens"].data_ptr()), sp)
-        dec = (P(d["q"].data_ptr()), P(cache.data_ptr()), npg, 64, P(d["comb"].data_ptr()), W,
+        dec = (P(d["q"].data_ptr()), P(cache.data_ptr()), npg, PS, P(d["comb"].data_ptr()), W,
                P(d["lens"].data_ptr()), P(d["sinks"].data_ptr()),
                ctypes.c_float(wl["softmax_scale"]), P(d["out"].data_ptr()), None, T, H)
         dec = dec + ((splits, P(workspace.data_ptr()), ctypes.c_size_t(ws_bytes), sp) if splits > 1
@@ -198,7 +206,7 @@ def main():
 
     # valid slots per instance (algorithmic work), from one combine per instance
     n_valid = []
-    num_slots = npg * 64
+    num_slots = npg * PS
     for (ins, comb, dec), d in zip(calls, inst):
         check(lib.dsv4_combine_indices(*comb))
     torch.cuda.synchronize()
@@ -306,7 +314,7 @@ def main():
                         "index combine + sparse MLA over an FP8/UE8M0 paged latent cache",
             "batch": T, "heads": H, "top_k": wl["top_k"], "topk_lens": "U{1024..2048}",
             "window": wl["window"], "combined_width": W, "context": int(wl["seq_lens"][0]),
-            "page_size": 64, "latent_dim": LATENT, "value_dim": NOPE, "sinks": True,
+            "page_size": PS, "latent_dim": LATENT, "value_dim": NOPE, "sinks": True,
             "instances_rotated": n_inst, "cache": "FP8 e4m3 nope + UE8M0 scales + bf16 rope",
             **({"decode_splits": splits} if splits > 1 else {}),
         },
@@ -317,7 +325,7 @@ def main():
             "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
             "frac": round((achieved_tflops / PEAK_BF16_TFLOPS) if bound == "mfma"
                           else (achieved_gbs / PEAK_HBM_GBS), 4),
-            "traffic": measured_traffic() if (splits == 1 and T == 64) else None,
+            "traffic": measured_traffic() if (splits == 1 and T == 64 and PS == 64) else None,
             "kernel": ("sparse_mla_kernel<2> + split_merge_kernel (dsv4_sparse_mla_decode_split)"
                        if splits > 1 else "sparse_mla_kernel<2> (dsv4_sparse_mla_decode)"),
             "launch_us": round(dec_s * 1e6, 2),
@@ -330,7 +338,73 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, inst[0], calls, H, T, W)
+        result["cpu_baseline"] = cpu_baseline(wl, inst[0], calls, H, T, W, PS)
+    print(json.dumps(result), flush=True)
+
+
+def bench_indexer(args, torch, dsv4):
+    """The indexer top-k selection at the decode shape: 64 query tokens, each with 32768
+    candidate positions (context 32768) of N(0,1) fp32 indexer logits, top-k 2048; 8
+    logit instances rotated.  Eager launches with HIP events around each; also logs the
+    prefill shape (one 8192-token sequence, causal candidates)."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, L, K = 64, 32768, 2048
+    rng = np.random.default_rng(args.seed)
+    logits = [torch.from_numpy(rng.standard_normal((T, L)).astype(np.float32)).to(dev)
+              for _ in range(8)]
+    qsl = torch.arange(T + 1, dtype=torch.int32, device=dev)
+    seq = torch.full((T,), L, dtype=torch.int32, device=dev)
+    out = torch.empty(T, K, dtype=torch.int32, device=dev)
+    lens = torch.empty(T, dtype=torch.int32, device=dev)
+    for i in range(args.warmup):
+        dsv4.dsv4_indexer_topk(logits[i % 8], qsl, seq, K, out, lens)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        ev[2 * k].record()
+        dsv4.dsv4_indexer_topk(logits[k % 8], qsl, seq, K, out, lens)
+        ev[2 * k + 1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    us = np.array([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps)]) * 1e3
+    bytes_alg = T * L * 4.0 + T * K * 4.0 + T * 4.0
+    gbs = bytes_alg / (us.mean() * 1e-6) / 1e9
+    # prefill shape: one 8192-token sequence, token i has i+1 candidates
+    Lp = 8192
+    lp = torch.from_numpy(rng.standard_normal((Lp, Lp)).astype(np.float32)).to(dev)
+    qp = torch.tensor([0, Lp], dtype=torch.int32, device=dev)
+    sp_ = torch.tensor([Lp], dtype=torch.int32, device=dev)
+    op = torch.empty(Lp, K, dtype=torch.int32, device=dev)
+    lnp = torch.empty(Lp, dtype=torch.int32, device=dev)
+    dsv4.dsv4_indexer_topk(lp, qp, sp_, K, op, lnp)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dsv4.dsv4_indexer_topk(lp, qp, sp_, K, op, lnp)
+    e1.record()
+    torch.cuda.synchronize()
+    pre_us = e0.elapsed_time(e1) / 5 * 1e3
+    pre_bytes = 4.0 * Lp * (Lp + 1) / 2 + 4.0 * Lp * K
+    log(f"[bench] indexer top-k {T} x {L} -> {K}: {us.mean():.1f} us mean (median {np.median(us):.1f}, "
+        f"min {us.min():.1f}) = {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS * 100:.1f}% of HBM); "
+        f"prefill shape {Lp} causal rows: {pre_us:.0f} us ({pre_bytes / (pre_us * 1e-6) / 1e9:.0f} GB/s)")
+    result = {
+        "metric": "indexer top-k query-tokens/s + % of HBM roofline (T=64, 32768 candidates, k=2048)",
+        "value": round(T / (us.mean() * 1e-6), 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(float(us.mean()) * 1e-3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "indexer top-k selection over N(0,1) fp32 logits", "tokens": T,
+                   "candidates": L, "top_k": K, "instances_rotated": 8},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "indexer_topk_kernel (dsv4_indexer_topk)",
+                     "launch_us": round(float(us.mean()), 2), "alg_bytes": bytes_alg},
+        "prefill_shape_us": round(pre_us, 1),
+    }
     print(json.dumps(result), flush=True)
 
 
@@ -457,7 +531,7 @@ def bench_compressed_prefill(args, torch, dsv4):
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(wl, d0, calls, H, T, W):
+def cpu_baseline(wl, d0, calls, H, T, W, PS=64):
     """The CPU oracle (fp64, as it stands) timed on this host on one full step of
     instance 0: insert + combine + attention for all 64 query tokens."""
     import oracle
@@ -468,23 +542,23 @@ def cpu_baseline(wl, d0, calls, H, T, W):
     npg = wl["num_pages"]
     # host cache holding the rows instance 0 references (built untimed)
     idx0, lens0 = oracle.combine(it["topk"], it["topk_lens"], wl["qsl"], wl["seq_lens"],
-                                 wl["block_table"], T, wl["top_k"], wl["window"], 64, W)
+                                 wl["block_table"], T, wl["top_k"], wl["window"], PS, W)
     need = np.unique(idx0[idx0 >= 0])
     sel = np.isin(wl["ctx_slot"], need)
-    cache = np.zeros(npg * 64 * RECORD, np.uint8)
+    cache = np.zeros(npg * PS * RECORD, np.uint8)
     oracle.kv_insert(np.zeros((int(sel.sum()), 0, LATENT), np.uint16), wl["ctx_kv"][sel],
                      wl["ctx_pos"][sel], wl["ctx_slot"][sel], wl["cos_sin"],
-                     np.zeros(LATENT, np.uint16), wl["eps"], cache, npg, 64, inplace=True)
+                     np.zeros(LATENT, np.uint16), wl["eps"], cache, npg, PS, inplace=True)
     q = np.array(it["q"], copy=True)
     kv_new = d0["kv"].cpu().view(__import__("torch").int16).numpy().view(np.uint16)
     pos = wl["seq_lens"].astype(np.int64) - 1
-    slots = wl["block_table"][np.arange(T), pos // 64].astype(np.int64) * 64 + pos % 64
+    slots = wl["block_table"][np.arange(T), pos // PS].astype(np.int64) * PS + pos % PS
     t0 = time.perf_counter()
     oracle.kv_insert(q, kv_new, pos, slots, wl["cos_sin"], wl["q_norm_weight"], wl["eps"], cache,
-                     npg, 64, inplace=True)
+                     npg, PS, inplace=True)
     idx, lens = oracle.combine(it["topk"], it["topk_lens"], wl["qsl"], wl["seq_lens"],
-                               wl["block_table"], T, wl["top_k"], wl["window"], 64, W)
-    oracle.sparse_mla(q, cache, npg, 64, idx, lens, it["sinks"], wl["softmax_scale"],
+                               wl["block_table"], T, wl["top_k"], wl["window"], PS, W)
+    oracle.sparse_mla(q, cache, npg, PS, idx, lens, it["sinks"], wl["softmax_scale"],
                       nthreads=cores, with_lse=False)
     el = time.perf_counter() - t0
     log(f"[bench] cpu oracle: one step ({T} query tokens) in {el:.2f} s on {cores} threads")

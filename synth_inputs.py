@@ -93,7 +93,7 @@ def _block_table(rng, seq_lens, P=PAGE):
 
 
 def attention_workload(cfg: int, seed: int | None = None, instances: int = 1,
-                       context_kv: str = "referenced", ctx_tokens=None):
+                       context_kv: str = "referenced", ctx_tokens=None, page_size: int = PAGE):
     """Inputs of the combine + attention steps for configs 0, 2, 3, 4.
 
     Returns a dict.  ``instances`` > 1 draws independent (q, topk, topk_lens, sinks)
@@ -101,7 +101,8 @@ def attention_workload(cfg: int, seed: int | None = None, instances: int = 1,
     ``ctx_*`` describe the context tokens whose latent rows must be inserted into the
     cache before attention: every position a top-k row or a window may touch
     ("referenced"), or every context position ("all").  ``ctx_tokens`` restricts the
-    referenced set to the rows of those query tokens (sampled parity checks)."""
+    referenced set to the rows of those query tokens (sampled parity checks).
+    ``page_size`` sets the slots per cache page (and so the block table)."""
     seed = cfg if seed is None else seed
     r = _streams(seed)
     if cfg == 0:
@@ -129,7 +130,7 @@ def attention_workload(cfg: int, seed: int | None = None, instances: int = 1,
     qsl = np.zeros(B + 1, np.int32)
     qsl[1:] = np.cumsum(qlens)
     T = int(qsl[-1])
-    block_table, num_pages = _block_table(r["perm"], seq_lens)
+    block_table, num_pages = _block_table(r["perm"], seq_lens, page_size)
     W = round_up(top_k + window, ALIGN)
 
     inst = []
@@ -180,10 +181,11 @@ def attention_workload(cfg: int, seed: int | None = None, instances: int = 1,
         ctx_x.append(xs)
     ctx_b = np.concatenate(ctx_b)
     ctx_x = np.concatenate(ctx_x)
-    ctx_slot = block_table[ctx_b, ctx_x // PAGE].astype(np.int64) * PAGE + ctx_x % PAGE
+    ctx_slot = (block_table[ctx_b, ctx_x // page_size].astype(np.int64) * page_size +
+                ctx_x % page_size)
     ctx_kv = bf16_normal(r["kv"], (ctx_x.size, LATENT))
     max_pos = int(seq_lens.max())
-    return dict(cfg=cfg, B=B, H=H, T=T, top_k=top_k, window=window, W=W, page_size=PAGE,
+    return dict(cfg=cfg, B=B, H=H, T=T, top_k=top_k, window=window, W=W, page_size=page_size,
                 softmax_scale=1.0 / math.sqrt(LATENT), seq_lens=seq_lens, qsl=qsl,
                 block_table=block_table, num_pages=num_pages, instances=inst,
                 ctx_kv=ctx_kv, ctx_pos=ctx_x, ctx_slot=ctx_slot,
