@@ -5,11 +5,13 @@
 // the result is the min(n, top_k) ids with the largest logits, ties to the smaller id
 // (a NaN logit counts as -inf), listed in ascending id order, -1 after them.
 //
-// One workgroup (4 waves) per token.  Logits map to order-preserving 32-bit keys; a
-// radix select (four 8-bit digits, most significant first, histograms in LDS) finds the
-// k-th largest key K and how many keys equal to K are taken (m); one ordered pass then
-// emits every id with key > K and the first m ids with key == K.  Each thread owns 8
-// consecutive candidates per pass, so a block-wide scan of its counts (packed into one
+// One workgroup (16 waves) per token.  Logits map to order-preserving 32-bit keys,
+// staged in LDS by the first pass for rows of up to 32768 candidates; a radix select
+// (digits of 11, 11 and 10 bits, most significant first, 2048-bin histograms in LDS:
+// wide enough that similar logits rarely collide on one bin) finds the k-th largest
+// key K and how many keys equal to K are taken (m); one ordered pass then emits every
+// id with key > K and the first m ids with key == K.  Each thread owns 8 consecutive
+// candidates per compaction pass, so a block-wide scan of its counts (packed into one
 // 32-bit value) gives every thread its output position.  Integer decisions on fp32
 // keys only: bit-exact with the oracle's fp32 comparisons.
 #include "device.hpp"
@@ -17,8 +19,9 @@
 
 namespace dsv4 {
 
-constexpr int kSelThreads = 256;
 constexpr int kSelItems = 8;
+constexpr int kStageMax = 32768;  // rows up to this many candidates keep their keys in LDS
+constexpr int kBins = 2048;       // radix digits of 11, 11 and 10 bits
 
 // Larger key <=> larger logit; -0 and +0 share a key (they compare equal), NaN takes the
 // key of -inf.
@@ -29,7 +32,8 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive scan over the 256 threads of the block (4 waves); `wsum` holds 4 ints.
+// Inclusive scan over the block of NT threads; `wsum` holds one int per wave.
+template <int NT>
 __device__ __forceinline__ int block_inclusive_scan(int x, int* wsum) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -41,17 +45,23 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int* wsum) {
   __syncthreads();
   int add = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) add += i < w ? wsum[i] : 0;
+  for (int i = 0; i < NT / 64; ++i) add += i < w ? wsum[i] : 0;
   __syncthreads();  // wsum may be reused by the next scan
   return x + add;
 }
 
-__global__ void __launch_bounds__(kSelThreads) indexer_topk_kernel(
+// NT threads per token; STAGE keeps the keys of rows up to kStageMax candidates in LDS
+// (few tokens, long rows: one large workgroup per CU), otherwise every pass rereads the
+// row from the caches (many tokens: several small workgroups per CU).
+template <int NT, bool STAGE>
+__global__ void __launch_bounds__(NT) indexer_topk_kernel(
     const float* __restrict__ logits, int logits_stride, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ seq_lens, int T, int ratio, int top_k, int32_t* __restrict__ topk,
     int topk_stride, int32_t* __restrict__ topk_lens) {
-  __shared__ uint32_t hist[256];
-  __shared__ int wsum[4];
+  constexpr int kSelThreads = NT;
+  __shared__ uint32_t keys[STAGE ? kStageMax : 1];
+  __shared__ uint32_t hist[kBins];
+  __shared__ int wsum[NT / 64];
   __shared__ uint32_t sh_digit, sh_above;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -71,29 +81,68 @@ __global__ void __launch_bounds__(kSelThreads) indexer_topk_kernel(
     if (k == n) {
       for (int j = tid; j < n; j += kSelThreads) out[j] = j;
     } else if (k > 0) {
-      // radix select of the k-th largest key
+      const bool staged = STAGE && n <= kStageMax;
+      // radix select of the k-th largest key (digits of 11, 11 and 10 bits, most
+      // significant first); the first pass also stages the keys
       uint32_t prefix = 0, mask = 0;
       int remaining = k;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[tid] = 0;
+#pragma unroll 1
+      for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+        for (int d = tid; d < kBins; d += kSelThreads) hist[d] = 0;
         __syncthreads();
-        for (int j = tid; j < n; j += kSelThreads) {
-          const uint32_t key = order_key(row[j]);
-          if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        if (pass == 0) {
+          for (int j0 = 0; j0 < n; j0 += kSelThreads * kSelItems) {
+            float v[kSelItems];
+#pragma unroll
+            for (int u = 0; u < kSelItems; ++u) {
+              const int j = j0 + u * kSelThreads + tid;
+              v[u] = j < n ? row[j] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kSelItems; ++u) {
+              const int j = j0 + u * kSelThreads + tid;
+              if (j < n) {
+                const uint32_t key = order_key(v[u]);
+                if (staged) keys[j] = key;
+                atomicAdd(&hist[key >> 21], 1u);
+              }
+            }
+          }
+        } else {
+          for (int j = tid; j < n; j += kSelThreads) {
+            const uint32_t key = staged ? keys[j] : order_key(row[j]);
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+          }
         }
         __syncthreads();
-        // thread d holds the count of digit 255-d; the inclusive scan gives, for digit
-        // 255-d, the number of matching keys with that digit or a larger one
-        const int c = (int)hist[255 - tid];
-        const int incl = block_inclusive_scan(c, wsum);
-        const int excl = incl - c;  // keys with a larger digit
-        if (excl < remaining && incl >= remaining) {
-          sh_digit = 255u - (uint32_t)tid;
-          sh_above = (uint32_t)excl;
+        // thread i owns the kBins/NT digits below dmask - (kBins/NT)*i (from the top);
+        // after the scan of its counts it knows how many matching keys have a larger
+        // digit than each of them, and the one whose range covers `remaining` is the digit
+        constexpr int kPer = kBins / NT;
+        int cnt[kPer];
+        int sum = 0;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+          const int d = (int)dmask - kPer * tid - r;
+          cnt[r] = d >= 0 ? (int)hist[d] : 0;
+          sum += cnt[r];
+        }
+        const int incl = block_inclusive_scan<NT>(sum, wsum);
+        int above = incl - sum;  // keys with a digit larger than this thread's first
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+          const int d = (int)dmask - kPer * tid - r;
+          if (d >= 0 && above < remaining && above + cnt[r] >= remaining) {
+            sh_digit = (uint32_t)d;
+            sh_above = (uint32_t)above;
+          }
+          above += cnt[r];
         }
         __syncthreads();
         prefix |= sh_digit << shift;
-        mask |= 255u << shift;
+        mask |= dmask << shift;
         remaining -= (int)sh_above;
         __syncthreads();  // sh_digit / sh_above / hist are rewritten next pass
       }
@@ -106,13 +155,13 @@ __global__ void __launch_bounds__(kSelThreads) indexer_topk_kernel(
         int cgt = 0, ceq = 0;
 #pragma unroll
         for (int j = 0; j < kSelItems; ++j) {
-          key[j] = first + j < n ? order_key(row[first + j]) : 0u;
+          key[j] = first + j < n ? (staged ? keys[first + j] : order_key(row[first + j])) : 0u;
           cgt += (first + j < n && key[j] > K) ? 1 : 0;
           ceq += (first + j < n && key[j] == K) ? 1 : 0;
         }
-        // counts of at most 2048 per pass: pack (gt, eq) into one scan
+        // at most 8192 of each per pass: pack (gt, eq) into one scan
         const int packed = cgt | (ceq << 16);
-        const int incl = block_inclusive_scan(packed, wsum);
+        const int incl = block_inclusive_scan<NT>(packed, wsum);
         const int excl = incl - packed;
         const int gt_before = gt_run + (excl & 0xFFFF);
         const int eq_before = eq_run + (excl >> 16);
@@ -150,8 +199,16 @@ hipError_t launch_indexer_topk(const float* logits, int logits_stride, const int
   if (B == 0 || T == 0) return hipSuccess;
   int per_req = (T + B - 1) / B;
   int Y = per_req < 1 ? 1 : (per_req > 4096 ? 4096 : per_req);
-  hipLaunchKernelGGL(indexer_topk_kernel, dim3(B, Y), dim3(kSelThreads), 0, stream, logits,
-                     logits_stride, qsl, seq_lens, T, ratio, top_k, topk, topk_stride, topk_lens);
+  // few tokens: one 16-wave workgroup per token with the row's keys in LDS; many tokens:
+  // 4-wave workgroups without staging, several per CU
+  if (T < 1024)
+    hipLaunchKernelGGL((indexer_topk_kernel<1024, true>), dim3(B, Y), dim3(1024), 0, stream,
+                       logits, logits_stride, qsl, seq_lens, T, ratio, top_k, topk, topk_stride,
+                       topk_lens);
+  else
+    hipLaunchKernelGGL((indexer_topk_kernel<256, false>), dim3(B, Y), dim3(256), 0, stream,
+                       logits, logits_stride, qsl, seq_lens, T, ratio, top_k, topk, topk_stride,
+                       topk_lens);
   return hipGetLastError();
 }
 

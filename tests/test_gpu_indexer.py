@@ -100,3 +100,32 @@ def test_indexer_combine_decode_chain(dsv4):
     torch.cuda.synchronize()
     assert np.array_equal(tk.cpu().numpy(), tk_r) and np.array_equal(comb.cpu().numpy(), comb_r)
     assert_attention_close(host_bits(out), ref, "indexer chain")
+
+
+def test_indexer_topk_many_tokens(dsv4):
+    """T >= 1024 takes the small-workgroup schedule (no LDS staging): a 1500-token
+    prefill, causal candidates, coarse logits with ties."""
+    rng = np.random.default_rng(1500)
+    L, top_k = 1500, 300
+    qsl = np.array([0, L], np.int32)
+    seq = np.array([L], np.int32)
+    logits = (np.round(rng.standard_normal((L, L)) * 8) / 8).astype(np.float32)
+    logits[rng.random((L, L)) < 0.01] = np.nan
+    log("indexer many tokens 1500 x 1500")
+    ref, rlen = oracle.indexer_topk(logits, qsl, seq, L, 1, top_k, top_k)
+    got, glen = _gpu_topk(dsv4, logits, qsl, seq, L, 1, top_k, top_k)
+    assert np.array_equal(glen, rlen) and np.array_equal(got, ref)
+
+
+def test_indexer_topk_rows_longer_than_the_lds_stage(dsv4):
+    """Few tokens with more than 32768 candidates: the large-workgroup schedule rereads
+    the row instead of staging it."""
+    rng = np.random.default_rng(1600)
+    T, L, top_k = 4, 50000, 2048
+    qsl = np.arange(T + 1, dtype=np.int32)
+    seq = np.array([50000, 32769, 32768, 40000], np.int32)
+    logits = rng.standard_normal((T, L)).astype(np.float32)
+    log("indexer long rows 4 x 50000")
+    ref, rlen = oracle.indexer_topk(logits, qsl, seq, T, 1, top_k, top_k)
+    got, glen = _gpu_topk(dsv4, logits, qsl, seq, T, 1, top_k, top_k)
+    assert np.array_equal(glen, rlen) and np.array_equal(got, ref)
