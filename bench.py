@@ -4,9 +4,10 @@
 A step is one pass of the whole path over one decode batch (B = 64 requests, one query
 token each, H = 128 heads, context 32768, top-k 2048 with lengths ~ U{1024..2048}, a
 128-token sliding window, per-head sinks):
-    dsv4_kv_insert        q RMSNorm + RoPE in place, new latent rows -> FP8 cache
-    dsv4_combine_indices  top-k + window -> one physical index row per token (width 2176)
-    dsv4_sparse_mla_decode
+    dsv4_kv_insert               q RMSNorm + RoPE in place, new latent rows -> FP8 cache
+    dsv4_sparse_mla_decode_topk  top-k + window -> one physical index row per token, built
+                                 in LDS, then sparse MLA over it (one launch)
+or, with --unfused, dsv4_kv_insert + dsv4_combine_indices + dsv4_sparse_mla_decode.
 Steps rotate over independent (q, top-k, lengths, sinks) instances so the gathered
 cache records (~69 MB per step, ~550 MB over 8 instances) cannot stay in the 256 MB
 Infinity Cache.  Inputs are resident in HBM before timing starts.  The three calls of a
@@ -45,12 +46,15 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def measured_traffic():
+def measured_traffic(which="fused"):
     """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     readings (each scaled by the reading of a 256 MiB copy), or None when the kernel's
-    sources have changed since the counters were taken."""
+    sources have changed since the counters were taken.  `which`: the fused combine +
+    decode launch or the plain decode launch."""
     import hashlib
-    path = os.path.join(HERE, "profiles", "sparse_mla_decode_b64_h128_traffic.json")
+    name = ("sparse_mla_decode_topk_b64_h128_traffic.json" if which == "fused"
+            else "sparse_mla_decode_b64_h128_traffic.json")
+    path = os.path.join(HERE, "profiles", name)
     try:
         with open(path) as f:
             d = json.load(f)
@@ -80,6 +84,9 @@ def parse():
     ap.add_argument("--splits", type=int, default=1,
                     help="pieces per index row for dsv4_sparse_mla_decode_split (1 = the "
                          "one-workgroup-per-(token, head group) decode)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the step as three launches (insert, combine, decode) instead of "
+                         "insert + the fused combine/decode")
     ap.add_argument("--page-size", type=int, default=64, choices=[32, 64, 256],
                     help="cache page size of the decode workload (default 64)")
     ap.add_argument("--workload", choices=["decode", "compressed-prefill", "indexer"],
@@ -193,13 +200,19 @@ def main():
                ctypes.c_float(wl["softmax_scale"]), P(d["out"].data_ptr()), None, T, H)
         dec = dec + ((splits, P(workspace.data_ptr()), ctypes.c_size_t(ws_bytes), sp) if splits > 1
                      else (sp,))
-        calls.append((ins, comb, dec))
+        fused = (P(d["q"].data_ptr()), P(cache.data_ptr()), npg, PS, P(d["topk"].data_ptr()),
+                 d["topk"].shape[1], d["topk"].shape[1], P(d["topk_lens"].data_ptr()),
+                 P(qsl.data_ptr()), P(seq_lens.data_ptr()), P(bt.data_ptr()), bt.shape[1], wl["B"],
+                 wl["top_k"], wl["window"], P(d["sinks"].data_ptr()),
+                 ctypes.c_float(wl["softmax_scale"]), P(d["out"].data_ptr()), None, T, H, sp)
+        calls.append((ins, comb, dec, fused))
 
     def check(st):
         if st != 0:
             raise RuntimeError(lib.dsv4_last_error().decode())
 
     decode_fn = lib.dsv4_sparse_mla_decode_split if splits > 1 else lib.dsv4_sparse_mla_decode
+    fused_step = not args.unfused and splits == 1
 
     def with_stream(args_tuple, stream_ptr):
         return args_tuple[:-1] + (stream_ptr,)
@@ -207,7 +220,7 @@ def main():
     # valid slots per instance (algorithmic work), from one combine per instance
     n_valid = []
     num_slots = npg * PS
-    for (ins, comb, dec), d in zip(calls, inst):
+    for (ins, comb, dec, fu), d in zip(calls, inst):
         check(lib.dsv4_combine_indices(*comb))
     torch.cuda.synchronize()
     for d in inst:
@@ -220,22 +233,31 @@ def main():
     n_inst = len(inst)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(6 * (args.steps))]
 
+    def run_step(ins, comb, dec, fu, stream_ptr=None):
+        def s_(a):
+            return a if stream_ptr is None else with_stream(a, stream_ptr)
+        check(lib.dsv4_kv_insert(*s_(ins)))
+        if fused_step:
+            check(lib.dsv4_sparse_mla_decode_topk(*s_(fu)))
+        else:
+            check(lib.dsv4_combine_indices(*s_(comb)))
+            check(decode_fn(*s_(dec)))
+
     def step(i, timed_idx=None):
-        ins, comb, dec = calls[i % n_inst]
+        ins, comb, dec, fu = calls[i % n_inst]
         if timed_idx is None:
-            check(lib.dsv4_kv_insert(*ins))
-            check(lib.dsv4_combine_indices(*comb))
-            check(decode_fn(*dec))
+            run_step(ins, comb, dec, fu)
             return
         e = ev[6 * timed_idx:6 * timed_idx + 6]
         e[0].record(stream)
         check(lib.dsv4_kv_insert(*ins))
         e[1].record(stream)
         e[2].record(stream)
-        check(lib.dsv4_combine_indices(*comb))
+        if not fused_step:
+            check(lib.dsv4_combine_indices(*comb))
         e[3].record(stream)
         e[4].record(stream)
-        check(decode_fn(*dec))
+        check(lib.dsv4_sparse_mla_decode_topk(*fu) if fused_step else decode_fn(*dec))
         e[5].record(stream)
 
     for i in range(args.warmup):
@@ -245,13 +267,10 @@ def main():
     # one HIP graph per instance holding its insert + combine + decode
     graphs = []
     cap = torch.cuda.Stream()
-    for ins, comb, dec in calls:
+    for ins, comb, dec, fu in calls:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            csp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-            check(lib.dsv4_kv_insert(*with_stream(ins, csp)))
-            check(lib.dsv4_combine_indices(*with_stream(comb, csp)))
-            check(decode_fn(*with_stream(dec, csp)))
+            run_step(ins, comb, dec, fu, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         graphs.append(g)
     torch.cuda.synchronize()
     for i in range(args.warmup):
@@ -288,9 +307,11 @@ def main():
     bound = "mfma" if t_mfma >= t_hbm else "hbm"
 
     value = T * args.steps / elapsed
+    dec_name = "combine+decode (fused)" if fused_step else "decode"
     log(f"[bench] {args.steps} steps (graph replays) in {elapsed * 1e3:.2f} ms -> {elapsed / args.steps * 1e6:.1f} us/step; "
-        f"kernel means: insert {ins_ms.mean() * 1e3:.1f} us, combine {comb_ms.mean() * 1e3:.1f} us, "
-        f"decode {dec_ms.mean() * 1e3:.1f} us (median {np.median(dec_ms) * 1e3:.1f}, "
+        f"kernel means: insert {ins_ms.mean() * 1e3:.1f} us, "
+        + ("" if fused_step else f"combine {comb_ms.mean() * 1e3:.1f} us, ")
+        + f"{dec_name} {dec_ms.mean() * 1e3:.1f} us (median {np.median(dec_ms) * 1e3:.1f}, "
         f"min {dec_ms.min() * 1e3:.1f})")
     log(f"[bench] decode: valid slots/launch {nv:.0f}, {flops / 1e9:.2f} GFLOP, {bytes_alg / 1e6:.1f} MB "
         f"-> {achieved_tflops:.0f} TFLOP/s ({achieved_tflops / PEAK_BF16_TFLOPS * 100:.1f}% of bf16 MFMA), "
@@ -312,6 +333,8 @@ def main():
         "config": {
             "workload": "sparse MLA decode step: fused q-norm/RoPE/FP8 insert + top-k/window "
                         "index combine + sparse MLA over an FP8/UE8M0 paged latent cache",
+            "launches": ("insert, combine+decode (fused)" if fused_step
+                         else "insert, combine, decode"),
             "batch": T, "heads": H, "top_k": wl["top_k"], "topk_lens": "U{1024..2048}",
             "window": wl["window"], "combined_width": W, "context": int(wl["seq_lens"][0]),
             "page_size": PS, "latent_dim": LATENT, "value_dim": NOPE, "sinks": True,
@@ -325,16 +348,22 @@ def main():
             "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
             "frac": round((achieved_tflops / PEAK_BF16_TFLOPS) if bound == "mfma"
                           else (achieved_gbs / PEAK_HBM_GBS), 4),
-            "traffic": measured_traffic() if (splits == 1 and T == 64 and PS == 64) else None,
+            "traffic": (measured_traffic("fused" if fused_step else "decode")
+                        if (splits == 1 and T == 64 and PS == 64) else None),
             "kernel": ("sparse_mla_kernel<2> + split_merge_kernel (dsv4_sparse_mla_decode_split)"
-                       if splits > 1 else "sparse_mla_kernel<2> (dsv4_sparse_mla_decode)"),
+                       if splits > 1 else
+                       "sparse_mla_kernel<2, fused combine> (dsv4_sparse_mla_decode_topk)"
+                       if fused_step else "sparse_mla_kernel<2> (dsv4_sparse_mla_decode)"),
             "launch_us": round(dec_s * 1e6, 2),
             "alg_flops": flops, "alg_bytes": bytes_alg,
             "hbm_frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
         },
-        "kernels_us": {"kv_insert": round(float(ins_ms.mean()) * 1e3, 2),
-                       "combine_indices": round(float(comb_ms.mean()) * 1e3, 2),
-                       "sparse_mla_decode": round(float(dec_ms.mean()) * 1e3, 2)},
+        "kernels_us": ({"kv_insert": round(float(ins_ms.mean()) * 1e3, 2),
+                        "sparse_mla_decode_topk": round(float(dec_ms.mean()) * 1e3, 2)}
+                       if fused_step else
+                       {"kv_insert": round(float(ins_ms.mean()) * 1e3, 2),
+                        "combine_indices": round(float(comb_ms.mean()) * 1e3, 2),
+                        "sparse_mla_decode": round(float(dec_ms.mean()) * 1e3, 2)}),
     }
 
     if not args.no_cpu_baseline:

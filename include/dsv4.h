@@ -251,6 +251,26 @@ int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages
                            void* out, float* lse, int T, int H, void* stream);
 
 /*
+ * dsv4_sparse_mla_decode_topk — dsv4_combine_indices followed by dsv4_sparse_mla_decode
+ * in one launch: each workgroup builds its token's combined index row in LDS from the
+ * combine step's inputs and attends over it, so the combined rows never go through
+ * memory [p3 combine kernel + p4 forward_mqa, the same two steps].  The result (out, lse)
+ * is the decode's on the rows dsv4_combine_indices would write; a token that belongs to
+ * no request gets an empty row (out 0; lse -inf, or the sink alone).  Arguments: those of the two entry
+ * points (the combine's topk / topk_lens / query_start_loc / seq_lens / block_table / B /
+ * top_k / window, the decode's q / cache / sinks / scale / out / lse / T / H); no
+ * combined_stride, since the row lives in LDS.  Requires top_k + window <= 4096
+ * (DSV4_ERR_UNSUPPORTED otherwise) and what both entry points require.
+ */
+int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
+                                const int32_t* topk, int topk_stride, int topk_width,
+                                const int32_t* topk_lens, const int32_t* query_start_loc,
+                                const int32_t* seq_lens, const int32_t* block_table,
+                                int block_table_stride, int B, int top_k, int window,
+                                const float* sinks, float softmax_scale, void* out, float* lse,
+                                int T, int H, void* stream);
+
+/*
  * dsv4_sparse_mla_prefill — the same result as dsv4_sparse_mla_decode, scheduled for
  * many query tokens per call (prefill: each token of a long sequence attends its own
  * combined index row) [p3 Motivation/Implementation breakdown: sparse prefill index

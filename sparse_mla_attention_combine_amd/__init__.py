@@ -42,6 +42,9 @@ _lib.dsv4_sparse_mla_split_workspace_bytes.restype = ctypes.c_size_t
 _lib.dsv4_sparse_mla_decode_split.argtypes = _attn_args[:-1] + [_i32, _vp, ctypes.c_size_t, _vp]
 _lib.dsv4_combine_indices_compressed.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]
+_lib.dsv4_sparse_mla_decode_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp,
+                                             _vp, _i32, _i32, _i32, _i32, _vp, _f32, _vp, _vp,
+                                             _i32, _i32, _vp]
 _lib.dsv4_indexer_topk.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp,
                                    _vp]
 _lib.dsv4_gather_workspace.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp,
@@ -49,14 +52,14 @@ _lib.dsv4_gather_workspace.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i3
 for _f in (_lib.dsv4_kv_insert, _lib.dsv4_combine_indices, _lib.dsv4_sparse_mla_decode,
            _lib.dsv4_sparse_mla_prefill, _lib.dsv4_gather_dequant, _lib.dsv4_sparse_mla_decode_split,
            _lib.dsv4_combine_indices_compressed, _lib.dsv4_gather_workspace,
-           _lib.dsv4_indexer_topk):
+           _lib.dsv4_indexer_topk, _lib.dsv4_sparse_mla_decode_topk):
     _f.restype = _i32
 
 EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4_kv_insert",
             "dsv4_combine_indices", "dsv4_sparse_mla_decode", "dsv4_sparse_mla_prefill",
             "dsv4_gather_dequant", "dsv4_sparse_mla_split_workspace_bytes",
             "dsv4_sparse_mla_decode_split", "dsv4_combine_indices_compressed",
-            "dsv4_gather_workspace", "dsv4_indexer_topk"]
+            "dsv4_gather_workspace", "dsv4_indexer_topk", "dsv4_sparse_mla_decode_topk"]
 
 
 class Dsv4Error(RuntimeError):
@@ -217,6 +220,30 @@ def dsv4_sparse_mla_prefill(q, kv_cache, indices, lens, sinks, softmax_scale, ou
     """Same contract as dsv4_sparse_mla_decode, scheduled for many query tokens."""
     return _attention(_lib.dsv4_sparse_mla_prefill, q, kv_cache, indices, lens, sinks,
                       softmax_scale, out, lse, page_size, stream)
+
+
+def dsv4_sparse_mla_decode_topk(q, kv_cache, topk, topk_lens, query_start_loc, seq_lens,
+                                block_table, top_k, window, sinks, softmax_scale, out, lse=None,
+                                page_size=64, topk_width=None, stream=None):
+    """dsv4_combine_indices + dsv4_sparse_mla_decode in one launch (the combined rows are
+    built in LDS): q bf16 [T, H, 576], topk int32 [T, width], topk_lens int32 [T] or None,
+    query_start_loc int32 [B+1], seq_lens int32 [B], block_table int32 [B, pages] ->
+    out bf16 [T, H, 512] (and lse fp32 [T, H] if given)."""
+    _want(q, torch.bfloat16, "q"), _want(kv_cache, torch.uint8, "kv_cache")
+    for t, n in ((topk, "topk"), (topk_lens, "topk_lens"), (query_start_loc, "query_start_loc"),
+                 (seq_lens, "seq_lens"), (block_table, "block_table")):
+        _want(t, torch.int32, n)
+    _want(sinks, torch.float32, "sinks"), _want(out, torch.bfloat16, "out")
+    _want(lse, torch.float32, "lse")
+    T, H = q.shape[0], q.shape[1]
+    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    width = topk.shape[1] if topk_width is None else topk_width
+    _check(_lib.dsv4_sparse_mla_decode_topk(
+        _ptr(q), _ptr(kv_cache), num_pages, page_size, _ptr(topk), topk.shape[1], width,
+        _ptr(topk_lens), _ptr(query_start_loc), _ptr(seq_lens), _ptr(block_table),
+        block_table.shape[1], seq_lens.shape[0], top_k, window, _ptr(sinks), float(softmax_scale),
+        _ptr(out), _ptr(lse), T, H, _stream(stream)))
+    return out
 
 
 def split_workspace_bytes(T, H, splits):

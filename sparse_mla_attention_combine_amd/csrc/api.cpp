@@ -279,6 +279,42 @@ int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num
                     fn);
 }
 
+int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
+                                const int32_t* topk, int topk_stride, int topk_width,
+                                const int32_t* topk_lens, const int32_t* query_start_loc,
+                                const int32_t* seq_lens, const int32_t* block_table,
+                                int block_table_stride, int B, int top_k, int window,
+                                const float* sinks, float softmax_scale, void* out, float* lse,
+                                int T, int H, void* stream) {
+  const char* fn = "dsv4_sparse_mla_decode_topk";
+  if (T < 0 || B < 0 || top_k < 0 || window < 0 || topk_width < 0 || topk_stride < topk_width ||
+      block_table_stride < 0)
+    return fail(DSV4_ERR_SHAPE, "%s: negative size or topk_stride < topk_width", fn);
+  if (H != 16 && H != 32 && H != 64 && H != 128)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: H = %d not in {16, 32, 64, 128}", fn, H);
+  int st = check_page(fn, page_size, num_pages);
+  if (st) return st;
+  if (top_k > topk_width) return fail(DSV4_ERR_SHAPE, "%s: top_k %d > topk_width %d", fn, top_k, topk_width);
+  if ((int64_t)top_k + window > 4096)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: top_k + window = %lld > 4096", fn, (long long)top_k + window);
+  if (!(softmax_scale == softmax_scale)) return fail(DSV4_ERR_SHAPE, "%s: softmax_scale is NaN", fn);
+  if (T == 0) return ok();
+  if (!q || !out || !query_start_loc || !seq_lens || (!topk && topk_width > 0) ||
+      (!block_table && block_table_stride > 0) || (!kv_cache && num_pages > 0))
+    return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(q, 16) || !aligned(out, 16) || (kv_cache && !aligned(kv_cache, 16)))
+    return fail(DSV4_ERR_ALIGN, "%s: q, out and kv_cache must be 16-byte aligned", fn);
+  if ((topk && !aligned(topk, 4)) || !aligned(query_start_loc, 4) || !aligned(seq_lens, 4))
+    return fail(DSV4_ERR_ALIGN, "%s: int32 arrays must be 4-byte aligned", fn);
+  return hip_status(dsv4::launch_attention_topk(q, kv_cache, num_pages, dsv4::page_shift_of(page_size),
+                                                topk, topk_stride, topk_width, topk_lens,
+                                                query_start_loc, seq_lens, block_table,
+                                                block_table_stride, B, top_k, window, sinks,
+                                                softmax_scale, out, lse, T, H,
+                                                static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int dsv4_sparse_mla_prefill(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
                             const int32_t* indices, int idx_stride, const int32_t* lens,
                             const float* sinks, float softmax_scale, void* out, float* lse, int T,

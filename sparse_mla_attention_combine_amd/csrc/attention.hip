@@ -53,6 +53,23 @@ struct AttnSmem {
   float red[2][4][16 * NHB];
   float lsum[4][16 * NHB];
   int32_t idx[kIdxBlock];
+  int req[4];  // fused combine: request of the token, its first token, its query count, its length
+};
+
+// Inputs of the combine step when the decode builds its index rows itself (the
+// arguments of dsv4_combine_indices; the page geometry comes with the cache).
+struct TopkIn {
+  const int32_t* topk;
+  int topk_stride;
+  int topk_width;
+  const int32_t* topk_lens;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int bt_stride;
+  int B;
+  int top_k;
+  int window;
 };
 
 // Source of the (all-zero) record read for an invalid or absent slot, so that every
@@ -104,6 +121,74 @@ __device__ __forceinline__ void stage_idx(int32_t* dst, const int32_t* __restric
 #pragma unroll
   for (int k = 0; k < kPer; ++k)
     if (tid + 256 * k < n_win) dst[tid + 256 * k] = v[k];
+}
+
+// The combine step for token t, written straight into the LDS index block (the rules of
+// combine_kernel: valid top-k entries outside the window, then the window ascending, each
+// mapped through the request's block table; -1 for the rest).  The top-k row is requested
+// before the token's request is known; returns the row length tk + sw (0 for a token of
+// no request), the same in every thread.  Contains barriers: call from all threads.
+// Every load is unconditional at a clamped, in-bounds address (only uniform conditions
+// skip one) and its value is selected afterwards: a load under a per-lane condition is
+// waited for on the spot, which would serialise them.
+template <int NHB>
+__device__ __forceinline__ int stage_combined(AttnSmem<NHB>& sm, const TopkIn& c, int64_t t, int ps,
+                                             int tid) {
+  constexpr int kPer = kIdxBlock / 256;
+  const int kmax = min(c.top_k, c.topk_width);
+  int32_t xv[kPer];
+  const int32_t* trow = c.topk + t * c.topk_stride;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    xv[u] = 256 * u < kmax ? trow[min(tid + 256 * u, kmax - 1)] : -1;
+  const int tl = c.topk_lens ? c.topk_lens[t] : c.top_k;
+  if (tid == 0) sm.req[0] = -1;
+  __syncthreads();
+  const int base = c.qsl[0];
+  // thread r tests request r and brings its length along, so the token's position is
+  // known right after one round of loads
+  for (int r = tid; r < c.B; r += 256) {
+    const int lo = c.qsl[r] - base, hi = c.qsl[r + 1] - base;
+    const int L = c.seq_lens[r];
+    if (t >= lo && t < hi) {  // at most one request holds the token
+      sm.req[0] = r;
+      sm.req[1] = lo;
+      sm.req[2] = hi - lo;
+      sm.req[3] = L;
+    }
+  }
+  __syncthreads();
+  const int b = sm.req[0];
+  if (b < 0) return 0;
+  const int64_t pos = (int64_t)sm.req[3] - sm.req[2] + (t - sm.req[1]);
+  int64_t tk = min(pos + 1, (int64_t)c.top_k);
+  tk = min(tk, (int64_t)tl);
+  tk = max(tk, (int64_t)0);
+  const int64_t sw = max(min(pos + 1, (int64_t)c.window), (int64_t)0);
+  const int64_t lo = pos - sw + 1;
+  const int32_t* bt_row = c.block_table + (int64_t)b * c.bt_stride;
+  const int n = (int)(tk + sw);
+  int64_t xs[kPer];
+  int32_t pg[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = tid + 256 * u;
+    int64_t x = j < tk ? (j < kmax ? (int64_t)xv[u] : -1) : lo + (j - tk);
+    if (j < tk && !(x >= 0 && x < lo)) x = -1;  // invalid, beyond pos, or in the window
+    if (j >= n) x = -1;
+    xs[u] = x;
+    const int64_t lp = x >> ps;
+    pg[u] = (256 * u < n && c.bt_stride > 0)
+                ? bt_row[lp < 0 ? 0 : (lp < c.bt_stride ? lp : c.bt_stride - 1)] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = tid + 256 * u;
+    const int64_t x = xs[u];
+    const bool ok = x >= 0 && (x >> ps) < c.bt_stride && pg[u] >= 0;
+    if (j < n) sm.idx[j] = ok ? (int32_t)(((int64_t)pg[u] << ps) + (x & ((1 << ps) - 1))) : -1;
+  }
+  return n;
 }
 
 // Where this lane's pieces of a slot's record live (the zero page for an invalid slot).
@@ -495,13 +580,15 @@ __device__ __forceinline__ void pv_last(AttnSmem<NHB>& sm, int cb, AttnState<NHB
   }
 }
 
-template <int NHB>
+// FUSED: the index rows are built in the prologue from the combine step's inputs (`tin`)
+// instead of read from `indices` / `lens` (one row per token, no pieces).
+template <int NHB, bool FUSED>
 __global__ void __launch_bounds__(256) sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int64_t num_slots, int ps,
     const int32_t* __restrict__ indices, int idx_stride, const int32_t* __restrict__ lens,
     const float* __restrict__ sinks, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, int T, int H, int groups, int splits, int split_len,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, TopkIn tin) {
   __shared__ AttnSmem<NHB> sm;
 
   // work item vt = (query token, split); with one split it is the query token
@@ -522,13 +609,16 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   const int h0 = hg * 16 * NHB;
   // The row length is read as a vector load issued next to the Q and index loads (the
   // address is moved to VGPRs), so that its latency overlaps theirs.
-  uint64_t len_addr = reinterpret_cast<uint64_t>(lens + t);
-  asm volatile("" : "+v"(len_addr));
-  const int n_lens_v = *reinterpret_cast<const __attribute__((address_space(1))) int32_t*>(len_addr);
+  int n_lens_v = 0;
+  if constexpr (!FUSED) {
+    uint64_t len_addr = reinterpret_cast<uint64_t>(lens + t);
+    asm volatile("" : "+v"(len_addr));
+    n_lens_v = *reinterpret_cast<const __attribute__((address_space(1))) int32_t*>(len_addr);
+  }
   const int32_t* idx_row = indices + (int64_t)t * idx_stride;
   // this work item's piece [beg, lim) of the row, known before its length arrives
-  const int beg = (int64_t)sp * split_len < idx_stride ? sp * split_len : idx_stride;
-  const int lim = beg + min(split_len, idx_stride - beg);
+  const int beg = FUSED ? 0 : ((int64_t)sp * split_len < idx_stride ? sp * split_len : idx_stride);
+  const int lim = FUSED ? kIdxBlock : beg + min(split_len, idx_stride - beg);
 
   AttnState<NHB> st;
   // Q^T fragments: lane (head l16 of block hb, k-group g); k-step s pairs with the
@@ -558,9 +648,14 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   // soon as staging has consumed it, so two chunks of records are always in flight.
   // The first block is requested together with Q and the row length (entries past the
   // length are staged but never used), so the prologue waits for memory only once.
-  stage_idx(sm.idx, idx_row + beg, min(lim - beg, kIdxBlock), tid);
+  int end;
+  if constexpr (FUSED) {
+    end = stage_combined<NHB>(sm, tin, t, ps, tid);
+  } else {
+    stage_idx(sm.idx, idx_row + beg, min(lim - beg, kIdxBlock), tid);
+    end = min(max(__builtin_amdgcn_readfirstlane(n_lens_v), 0), lim);
+  }
   __syncthreads();
-  const int end = min(max(__builtin_amdgcn_readfirstlane(n_lens_v), 0), lim);
   const int row = 16 * w + l16;
   const CacheRef cr{cache, num_slots, ps};
   for (int blk0 = beg; blk0 < end; blk0 += kIdxBlock) {
@@ -715,28 +810,44 @@ size_t split_workspace_bytes(int T, int H, int splits) {
   return (size_t)T * splits * H * (kNope + 2) * sizeof(float);
 }
 
+template <bool FUSED>
 static hipError_t launch_items(const void* q, const uint8_t* cache, int num_pages, int ps,
                                const int32_t* indices, int idx_stride, const int32_t* lens,
                                const float* sinks, float softmax_scale, void* out, float* lse,
                                int T, int H, int splits, int split_len, float* part_o,
-                               float* part_ml, hipStream_t stream) {
+                               float* part_ml, const TopkIn& tin, hipStream_t stream) {
   const int64_t num_slots = (int64_t)num_pages << ps;
   const float scale_log2 = softmax_scale * kLog2e;
   const int items = T * splits;
   if (H == 16) {
-    hipLaunchKernelGGL(sparse_mla_kernel<1>, dim3(items), dim3(256), 0, stream,
+    hipLaunchKernelGGL((sparse_mla_kernel<1, FUSED>), dim3(items), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), cache, num_slots, ps, indices, idx_stride, lens,
                        sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, 1, splits,
-                       split_len, part_o, part_ml);
+                       split_len, part_o, part_ml, tin);
   } else {
     const int groups = H / 32;
     const int grid = groups == 1 ? items : 8 * groups * ((items + 7) / 8);
-    hipLaunchKernelGGL(sparse_mla_kernel<2>, dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL((sparse_mla_kernel<2, FUSED>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), cache, num_slots, ps, indices, idx_stride, lens,
                        sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, groups, splits,
-                       split_len, part_o, part_ml);
+                       split_len, part_o, part_ml, tin);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attention_topk(const void* q, const uint8_t* cache, int num_pages,
+                                 int page_shift, const int32_t* topk, int topk_stride,
+                                 int topk_width, const int32_t* topk_lens, const int32_t* qsl,
+                                 const int32_t* seq_lens, const int32_t* block_table, int bt_stride,
+                                 int B, int top_k, int window, const float* sinks,
+                                 float softmax_scale, void* out, float* lse, int T, int H,
+                                 hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const TopkIn tin{topk, topk_stride, topk_width, topk_lens, qsl, seq_lens, block_table,
+                   bt_stride, B, top_k, window};
+  return launch_items<true>(q, cache, num_pages, page_shift, nullptr, 0, nullptr, sinks,
+                            softmax_scale, out, lse, T, H, 1, kIdxBlock, nullptr, nullptr, tin,
+                            stream);
 }
 
 hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, int page_shift,
@@ -746,8 +857,9 @@ hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, 
   (void)prefill;  // one schedule serves both entry points for now
   if (T == 0) return hipSuccess;
   const int whole = idx_stride > 0 ? idx_stride : 1;
-  return launch_items(q, cache, num_pages, page_shift, indices, idx_stride, lens, sinks,
-                      softmax_scale, out, lse, T, H, 1, whole, nullptr, nullptr, stream);
+  return launch_items<false>(q, cache, num_pages, page_shift, indices, idx_stride, lens, sinks,
+                             softmax_scale, out, lse, T, H, 1, whole, nullptr, nullptr, TopkIn{},
+                             stream);
 }
 
 hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_pages,
@@ -760,9 +872,9 @@ hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_p
   const int split_len = per > 0 ? ((per + kChunk - 1) / kChunk) * kChunk : kChunk;
   float* part_o = static_cast<float*>(workspace);
   float* part_ml = part_o + (size_t)T * splits * H * kNope;
-  hipError_t e = launch_items(q, cache, num_pages, page_shift, indices, idx_stride, lens, sinks,
-                              softmax_scale, out, lse, T, H, splits, split_len, part_o, part_ml,
-                              stream);
+  hipError_t e = launch_items<false>(q, cache, num_pages, page_shift, indices, idx_stride, lens,
+                                     sinks, softmax_scale, out, lse, T, H, splits, split_len,
+                                     part_o, part_ml, TopkIn{}, stream);
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)T * H;
   hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,

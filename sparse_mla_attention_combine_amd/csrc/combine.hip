@@ -14,16 +14,6 @@ namespace dsv4 {
 
 constexpr int kColsPerThread = 9;  // 2304 columns per pass covers the 2176-wide rows
 
-// Logical position x of a request -> physical slot through its block-table row (pages
-// of 2^ps slots); -1 for a position without a page.
-__device__ __forceinline__ int32_t phys_slot(const int32_t* __restrict__ bt_row, int bt_stride,
-                                             int64_t x, int ps) {
-  int64_t lp = x >> ps;  // logical page
-  if (x < 0 || lp >= bt_stride) return -1;
-  int32_t page = bt_row[lp];
-  return page < 0 ? -1 : (int32_t)(((int64_t)page << ps) + (x & ((1 << ps) - 1)));
-}
-
 __global__ void __launch_bounds__(256) combine_kernel(
     const int32_t* __restrict__ topk, int topk_stride, int topk_width,
     const int32_t* __restrict__ topk_lens, const int32_t* __restrict__ qsl,
@@ -48,21 +38,40 @@ __global__ void __launch_bounds__(256) combine_kernel(
     const int32_t* trow = topk + t * topk_stride;
     int32_t* crow = combined + t * combined_stride;
     // columns j = threadIdx.x + 256k: all top-k loads, then all block-table loads, are
-    // issued before any is consumed (one memory round trip each per row, not per column)
+    // issued before any is consumed (one memory round trip each per row, not per column).
+    // The loads are unconditional at clamped in-bounds addresses (only uniform conditions
+    // skip one) and their values selected afterwards: a load under a per-lane condition
+    // is waited for on the spot.
+    const int kmax = (int)min(tk, (int64_t)topk_width);  // top-k columns that are read
+    const int32_t* tsrc = kmax > 0 ? trow : qsl;          // any readable word when none is
     for (int jb = 0; jb < combined_stride; jb += 256 * kColsPerThread) {
+      int32_t tv[kColsPerThread];
+#pragma unroll
+      for (int k = 0; k < kColsPerThread; ++k)  // every load first, then their use
+        tv[k] = tsrc[kmax > 0 ? min(jb + (int)threadIdx.x + 256 * k, kmax - 1) : 0];
       int64_t x[kColsPerThread];
 #pragma unroll
       for (int k = 0; k < kColsPerThread; ++k) {
         const int j = jb + threadIdx.x + 256 * k;
-        x[k] = -1;
-        if (j < tk) x[k] = j < topk_width ? (int64_t)trow[j] : -1;
-        else if (j < tk + sw) x[k] = lo + (j - tk);
+        const int64_t from_topk = j < topk_width ? (int64_t)tv[k] : -1;
+        const int64_t from_window = j < tk + sw ? lo + (j - tk) : -1;
+        const int64_t xx = j < tk ? from_topk : from_window;
         // top-k entries that are invalid, beyond pos, or inside the window -> -1
-        if (j < tk && !(x[k] >= 0 && x[k] < lo)) x[k] = -1;
+        x[k] = (j < tk && !(xx >= 0 && xx < lo)) ? -1 : xx;
+      }
+      int32_t pg[kColsPerThread];
+#pragma unroll
+      for (int k = 0; k < kColsPerThread; ++k) {
+        const int64_t lp = x[k] >> ps;
+        pg[k] = (jb + 256 * k < tk + sw && bt_stride > 0)
+                    ? bt_row[lp < 0 ? 0 : (lp < bt_stride ? lp : bt_stride - 1)] : -1;
       }
       int32_t v[kColsPerThread];
 #pragma unroll
-      for (int k = 0; k < kColsPerThread; ++k) v[k] = x[k] >= 0 ? phys_slot(bt_row, bt_stride, x[k], ps) : -1;
+      for (int k = 0; k < kColsPerThread; ++k) {
+        const bool ok = x[k] >= 0 && (x[k] >> ps) < bt_stride && pg[k] >= 0;
+        v[k] = ok ? (int32_t)(((int64_t)pg[k] << ps) + (x[k] & ((1 << ps) - 1))) : -1;
+      }
 #pragma unroll
       for (int k = 0; k < kColsPerThread; ++k) {
         const int j = jb + threadIdx.x + 256 * k;
@@ -104,16 +113,19 @@ __global__ void __launch_bounds__(256) combine_compressed_kernel(
     tk = max(tk, (int64_t)0);
     const int64_t sw = max(min(pos + 1, (int64_t)window), (int64_t)0);
     const int64_t k0 = pos - sw + 1 - gather_start;  // gathered-token row of the first window entry
+    const int kmax = (int)min(tk, (int64_t)topk_width);
     const int32_t* trow = topk + t * topk_stride;
+    const int32_t* tsrc = kmax > 0 ? trow : qsl;  // any readable word when no column is
     int32_t* crow = combined + t * combined_stride;
     for (int jb = 0; jb < combined_stride; jb += 256 * kColsPerThread) {
       int32_t v[kColsPerThread];
 #pragma unroll
       for (int k = 0; k < kColsPerThread; ++k) {
         const int j = jb + threadIdx.x + 256 * k;
-        int64_t e = -1;
-        if (j < tk) e = j < topk_width ? (int64_t)trow[j] : -1;
-        v[k] = (j < tk && e >= 0 && e < N) ? (int32_t)(row0 + e) : -1;
+        // unconditional load at a clamped column (see combine_kernel), selected after
+        const int32_t tv = tsrc[kmax > 0 ? min(j, kmax - 1) : 0];
+        const int64_t e = (j < tk && j < topk_width) ? (int64_t)tv : -1;
+        v[k] = (e >= 0 && e < N) ? (int32_t)(row0 + e) : -1;
       }
 #pragma unroll
       for (int k = 0; k < kColsPerThread; ++k) {

@@ -97,8 +97,10 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(
             float v[kSelItems];
 #pragma unroll
             for (int u = 0; u < kSelItems; ++u) {
+              // unconditional load at a clamped index (a load under a per-lane condition
+              // is waited for on the spot); entries past n are ignored below
               const int j = j0 + u * kSelThreads + tid;
-              v[u] = j < n ? row[j] : 0.f;
+              v[u] = j0 + u * kSelThreads < n ? row[min(j, n - 1)] : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < kSelItems; ++u) {
@@ -110,10 +112,24 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(
               }
             }
           }
-        } else {
+        } else if (staged) {
           for (int j = tid; j < n; j += kSelThreads) {
-            const uint32_t key = staged ? keys[j] : order_key(row[j]);
+            const uint32_t key = keys[j];
             if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+          }
+        } else {
+          // eight loads per thread in flight at a time, at clamped indices
+          for (int j0 = 0; j0 < n; j0 += kSelThreads * kSelItems) {
+            float v[kSelItems];
+#pragma unroll
+            for (int u = 0; u < kSelItems; ++u)
+              v[u] = row[min(j0 + u * kSelThreads + tid, n - 1)];
+#pragma unroll
+            for (int u = 0; u < kSelItems; ++u) {
+              const uint32_t key = order_key(v[u]);
+              if (j0 + u * kSelThreads + tid < n && (key & mask) == prefix)
+                atomicAdd(&hist[(key >> shift) & dmask], 1u);
+            }
           }
         }
         __syncthreads();
@@ -153,9 +169,18 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(
         const int first = c0 + tid * kSelItems;
         uint32_t key[kSelItems];
         int cgt = 0, ceq = 0;
+        if (staged) {
+#pragma unroll
+          for (int j = 0; j < kSelItems; ++j) key[j] = first + j < n ? keys[first + j] : 0u;
+        } else {
+          float lv[kSelItems];  // every load first (clamped), then their use
+#pragma unroll
+          for (int j = 0; j < kSelItems; ++j) lv[j] = row[min(first + j, n - 1)];
+#pragma unroll
+          for (int j = 0; j < kSelItems; ++j) key[j] = first + j < n ? order_key(lv[j]) : 0u;
+        }
 #pragma unroll
         for (int j = 0; j < kSelItems; ++j) {
-          key[j] = first + j < n ? (staged ? keys[first + j] : order_key(row[first + j])) : 0u;
           cgt += (first + j < n && key[j] > K) ? 1 : 0;
           ceq += (first + j < n && key[j] == K) ? 1 : 0;
         }

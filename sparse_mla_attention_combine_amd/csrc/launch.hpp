@@ -61,4 +61,14 @@ hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_p
                                   int T, int H, int splits, void* workspace, hipStream_t stream);
 size_t split_workspace_bytes(int T, int H, int splits);
 
+// Decode that builds each token's combined index row itself from the combine step's
+// inputs (top_k + window <= 4096).
+hipError_t launch_attention_topk(const void* q, const uint8_t* cache, int num_pages,
+                                 int page_shift, const int32_t* topk, int topk_stride,
+                                 int topk_width, const int32_t* topk_lens, const int32_t* qsl,
+                                 const int32_t* seq_lens, const int32_t* block_table, int bt_stride,
+                                 int B, int top_k, int window, const float* sinks,
+                                 float softmax_scale, void* out, float* lse, int T, int H,
+                                 hipStream_t stream);
+
 }  // namespace dsv4

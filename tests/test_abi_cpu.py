@@ -169,6 +169,29 @@ def test_indexer_topk_validation(dsv4):
     assert call(T=0) == 0
 
 
+def test_decode_topk_validation(dsv4):
+    lib = dsv4.library()
+    keep, p = _fake()
+
+    def call(**kw):
+        a = dict(q=p, cache=p, npg=4, P=64, topk=p, ts=2048, tw=2048, tl=None, qsl=p, sl=p, bt=p,
+                 bts=8, B=2, top_k=2048, window=128, sinks=None, scale=0.04, out=p, lse=None, T=2,
+                 H=128)
+        a.update(kw)
+        return lib.dsv4_sparse_mla_decode_topk(
+            a["q"], a["cache"], a["npg"], a["P"], a["topk"], a["ts"], a["tw"], a["tl"], a["qsl"],
+            a["sl"], a["bt"], a["bts"], a["B"], a["top_k"], a["window"], a["sinks"], a["scale"],
+            a["out"], a["lse"], a["T"], a["H"], None)
+
+    assert call(window=2049) == 4 and b"4096" in lib.dsv4_last_error()
+    assert call(H=24) == 4
+    assert call(P=48) == 4
+    assert call(top_k=3000) == 2
+    assert call(qsl=None) == 1
+    assert call(out=ctypes.c_void_p(p.value + 2)) == 3
+    assert call(T=0) == 0
+
+
 def test_insert_and_gather_validation(dsv4):
     lib = dsv4.library()
     keep, p = _fake()
