@@ -3,16 +3,17 @@
 
 A step is one pass of the whole path over one decode batch (B = 64 requests, one query
 token each, H = 128 heads, context 32768, top-k 2048 with lengths ~ U{1024..2048}, a
-128-token sliding window, per-head sinks):
-    dsv4_kv_insert               q RMSNorm + RoPE in place, new latent rows -> FP8 cache
-    dsv4_sparse_mla_decode_topk  top-k + window -> one physical index row per token, built
-                                 in LDS, then sparse MLA over it (one launch)
-or, with --unfused, dsv4_kv_insert + dsv4_combine_indices + dsv4_sparse_mla_decode.
+128-token sliding window, per-head sinks): q RMSNorm + RoPE in place and the new latent
+rows into the FP8 cache, top-k + window -> one physical index row per token, sparse MLA
+over it.  By default one launch does it all (dsv4_sparse_mla_decode_step); --launches 2
+times dsv4_kv_insert + dsv4_sparse_mla_decode_topk (the row built in LDS), --launches 3
+(or --unfused) dsv4_kv_insert + dsv4_combine_indices + dsv4_sparse_mla_decode.
 Steps rotate over independent (q, top-k, lengths, sinks) instances so the gathered
 cache records (~69 MB per step, ~550 MB over 8 instances) cannot stay in the 256 MB
-Infinity Cache.  Inputs are resident in HBM before timing starts.  The three calls of a
-step are captured once per instance into a HIP graph (no allocation, no memset node)
-and the timed region replays those graphs; a second pass, outside the timed region,
+Infinity Cache.  Inputs are resident in HBM before timing starts.  The launches of a
+step are captured into HIP graphs (no allocation, no memset node), one per instance and
+one per rotation over all instances (8 complete steps in order), and the timed region
+replays whole rotations; a second pass, outside the timed region,
 runs the same steps eagerly with HIP events around every launch for the per-kernel
 times and the roofline of the decode kernel.
 
@@ -49,11 +50,12 @@ def log(msg):
 def measured_traffic(which="fused"):
     """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     readings (each scaled by the reading of a 256 MiB copy), or None when the kernel's
-    sources have changed since the counters were taken.  `which`: the fused combine +
-    decode launch or the plain decode launch."""
+    sources have changed since the counters were taken.  `which`: the one-launch step,
+    the fused combine + decode launch or the plain decode launch."""
     import hashlib
-    name = ("sparse_mla_decode_topk_b64_h128_traffic.json" if which == "fused"
-            else "sparse_mla_decode_b64_h128_traffic.json")
+    name = {"step": "sparse_mla_decode_step_b64_h128_traffic.json",
+            "fused": "sparse_mla_decode_topk_b64_h128_traffic.json"}.get(
+                which, "sparse_mla_decode_b64_h128_traffic.json")
     path = os.path.join(HERE, "profiles", name)
     try:
         with open(path) as f:
@@ -84,9 +86,10 @@ def parse():
     ap.add_argument("--splits", type=int, default=1,
                     help="pieces per index row for dsv4_sparse_mla_decode_split (1 = the "
                          "one-workgroup-per-(token, head group) decode)")
-    ap.add_argument("--unfused", action="store_true",
-                    help="time the step as three launches (insert, combine, decode) instead of "
-                         "insert + the fused combine/decode")
+    ap.add_argument("--launches", type=int, default=1, choices=[1, 2, 3],
+                    help="1: the whole step in one launch (dsv4_sparse_mla_decode_step); 2: "
+                         "insert + fused combine/decode; 3: insert, combine, decode")
+    ap.add_argument("--unfused", action="store_true", help="same as --launches 3")
     ap.add_argument("--page-size", type=int, default=64, choices=[32, 64, 256],
                     help="cache page size of the decode workload (default 64)")
     ap.add_argument("--workload", choices=["decode", "compressed-prefill", "indexer"],
@@ -205,14 +208,17 @@ def main():
                  P(qsl.data_ptr()), P(seq_lens.data_ptr()), P(bt.data_ptr()), bt.shape[1], wl["B"],
                  wl["top_k"], wl["window"], P(d["sinks"].data_ptr()),
                  ctypes.c_float(wl["softmax_scale"]), P(d["out"].data_ptr()), None, T, H, sp)
-        calls.append((ins, comb, dec, fused))
+        one = ins[:11] + fused[4:]
+        calls.append((ins, comb, dec, fused, one))
 
     def check(st):
         if st != 0:
             raise RuntimeError(lib.dsv4_last_error().decode())
 
     decode_fn = lib.dsv4_sparse_mla_decode_split if splits > 1 else lib.dsv4_sparse_mla_decode
-    fused_step = not args.unfused and splits == 1
+    launches = 3 if (args.unfused or splits > 1) else args.launches
+    fused_step = launches == 2
+    one_launch = launches == 1
 
     def with_stream(args_tuple, stream_ptr):
         return args_tuple[:-1] + (stream_ptr,)
@@ -220,7 +226,7 @@ def main():
     # valid slots per instance (algorithmic work), from one combine per instance
     n_valid = []
     num_slots = npg * PS
-    for (ins, comb, dec, fu), d in zip(calls, inst):
+    for (ins, comb, dec, fu, one), d in zip(calls, inst):
         check(lib.dsv4_combine_indices(*comb))
     torch.cuda.synchronize()
     for d in inst:
@@ -233,9 +239,12 @@ def main():
     n_inst = len(inst)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(6 * (args.steps))]
 
-    def run_step(ins, comb, dec, fu, stream_ptr=None):
+    def run_step(ins, comb, dec, fu, one, stream_ptr=None):
         def s_(a):
             return a if stream_ptr is None else with_stream(a, stream_ptr)
+        if one_launch:
+            check(lib.dsv4_sparse_mla_decode_step(*s_(one)))
+            return
         check(lib.dsv4_kv_insert(*s_(ins)))
         if fused_step:
             check(lib.dsv4_sparse_mla_decode_topk(*s_(fu)))
@@ -244,42 +253,57 @@ def main():
             check(decode_fn(*s_(dec)))
 
     def step(i, timed_idx=None):
-        ins, comb, dec, fu = calls[i % n_inst]
+        ins, comb, dec, fu, one = calls[i % n_inst]
         if timed_idx is None:
-            run_step(ins, comb, dec, fu)
+            run_step(ins, comb, dec, fu, one)
             return
         e = ev[6 * timed_idx:6 * timed_idx + 6]
         e[0].record(stream)
-        check(lib.dsv4_kv_insert(*ins))
+        if not one_launch:
+            check(lib.dsv4_kv_insert(*ins))
         e[1].record(stream)
         e[2].record(stream)
-        if not fused_step:
+        if launches == 3:
             check(lib.dsv4_combine_indices(*comb))
         e[3].record(stream)
         e[4].record(stream)
-        check(lib.dsv4_sparse_mla_decode_topk(*fu) if fused_step else decode_fn(*dec))
+        if one_launch:
+            check(lib.dsv4_sparse_mla_decode_step(*one))
+        else:
+            check(lib.dsv4_sparse_mla_decode_topk(*fu) if fused_step else decode_fn(*dec))
         e[5].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # one HIP graph per instance holding its insert + combine + decode
+    # HIP graphs: one per instance holding its step's launches, and one holding a whole
+    # rotation (every instance's step in order, n_inst complete steps back to back on one
+    # stream), which spares the per-replay gap between steps
     graphs = []
     cap = torch.cuda.Stream()
-    for ins, comb, dec, fu in calls:
+    for ins, comb, dec, fu, one in calls:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            run_step(ins, comb, dec, fu, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            run_step(ins, comb, dec, fu, one,
+                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         graphs.append(g)
+    rotation = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(rotation, stream=cap):
+        for ins, comb, dec, fu, one in calls:
+            run_step(ins, comb, dec, fu, one,
+                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
     for i in range(args.warmup):
         graphs[i % n_inst].replay()
+    rotation.replay()
     torch.cuda.synchronize()
 
-    # timed region: K steps as graph replays
+    # timed region: K steps as graph replays (whole rotations, then single steps)
     t_start = time.perf_counter()
-    for k in range(args.steps):
+    for _ in range(args.steps // n_inst):
+        rotation.replay()
+    for k in range(args.steps - args.steps % n_inst, args.steps):
         graphs[k % n_inst].replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
@@ -300,6 +324,8 @@ def main():
     ls = float(np.mean([lens_sum[i] for i in used]))
     flops = 2.0 * H * (LATENT + NOPE) * nv
     bytes_alg = RECORD * nv + T * H * (LATENT + NOPE) * 2 + 4.0 * ls + 4.0 * T + 4.0 * H
+    if one_launch:  # + the insert's q write-back, kv rows, cache rows, cos/sin, positions
+        bytes_alg += T * H * LATENT * 2 + T * (LATENT * 2 + RECORD + 64 * 4 + 16) + LATENT * 2
     achieved_tflops = flops / dec_s / 1e12
     achieved_gbs = bytes_alg / dec_s / 1e9
     t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
@@ -307,10 +333,11 @@ def main():
     bound = "mfma" if t_mfma >= t_hbm else "hbm"
 
     value = T * args.steps / elapsed
-    dec_name = "combine+decode (fused)" if fused_step else "decode"
+    dec_name = ("insert+combine+decode (one launch)" if one_launch
+                else "combine+decode (fused)" if fused_step else "decode")
     log(f"[bench] {args.steps} steps (graph replays) in {elapsed * 1e3:.2f} ms -> {elapsed / args.steps * 1e6:.1f} us/step; "
-        f"kernel means: insert {ins_ms.mean() * 1e3:.1f} us, "
-        + ("" if fused_step else f"combine {comb_ms.mean() * 1e3:.1f} us, ")
+        "kernel means: " + ("" if one_launch else f"insert {ins_ms.mean() * 1e3:.1f} us, ")
+        + (f"combine {comb_ms.mean() * 1e3:.1f} us, " if launches == 3 else "")
         + f"{dec_name} {dec_ms.mean() * 1e3:.1f} us (median {np.median(dec_ms) * 1e3:.1f}, "
         f"min {dec_ms.min() * 1e3:.1f})")
     log(f"[bench] decode: valid slots/launch {nv:.0f}, {flops / 1e9:.2f} GFLOP, {bytes_alg / 1e6:.1f} MB "
@@ -333,7 +360,8 @@ def main():
         "config": {
             "workload": "sparse MLA decode step: fused q-norm/RoPE/FP8 insert + top-k/window "
                         "index combine + sparse MLA over an FP8/UE8M0 paged latent cache",
-            "launches": ("insert, combine+decode (fused)" if fused_step
+            "launches": ("insert+combine+decode (one launch)" if one_launch
+                         else "insert, combine+decode (fused)" if fused_step
                          else "insert, combine, decode"),
             "batch": T, "heads": H, "top_k": wl["top_k"], "topk_lens": "U{1024..2048}",
             "window": wl["window"], "combined_width": W, "context": int(wl["seq_lens"][0]),
@@ -348,17 +376,22 @@ def main():
             "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
             "frac": round((achieved_tflops / PEAK_BF16_TFLOPS) if bound == "mfma"
                           else (achieved_gbs / PEAK_HBM_GBS), 4),
-            "traffic": (measured_traffic("fused" if fused_step else "decode")
+            "traffic": (measured_traffic("step" if one_launch else "fused" if fused_step
+                                         else "decode")
                         if (splits == 1 and T == 64 and PS == 64) else None),
             "kernel": ("sparse_mla_kernel<2> + split_merge_kernel (dsv4_sparse_mla_decode_split)"
                        if splits > 1 else
+                       "sparse_mla_kernel<2, fused combine, insert> (dsv4_sparse_mla_decode_step)"
+                       if one_launch else
                        "sparse_mla_kernel<2, fused combine> (dsv4_sparse_mla_decode_topk)"
                        if fused_step else "sparse_mla_kernel<2> (dsv4_sparse_mla_decode)"),
             "launch_us": round(dec_s * 1e6, 2),
             "alg_flops": flops, "alg_bytes": bytes_alg,
             "hbm_frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
         },
-        "kernels_us": ({"kv_insert": round(float(ins_ms.mean()) * 1e3, 2),
+        "kernels_us": ({"sparse_mla_decode_step": round(float(dec_ms.mean()) * 1e3, 2)}
+                       if one_launch else
+                       {"kv_insert": round(float(ins_ms.mean()) * 1e3, 2),
                         "sparse_mla_decode_topk": round(float(dec_ms.mean()) * 1e3, 2)}
                        if fused_step else
                        {"kv_insert": round(float(ins_ms.mean()) * 1e3, 2),

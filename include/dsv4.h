@@ -271,6 +271,35 @@ int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_
                                 int T, int H, void* stream);
 
 /*
+ * dsv4_sparse_mla_decode_step — dsv4_kv_insert followed by dsv4_sparse_mla_decode_topk in
+ * one launch, the whole decode step of the layer [p2 Implementation breakdown item 4, the
+ * fused insert, feeding the sparse decode of Key source excerpts xpu_sparse_decode_fp8;
+ * p3 combine kernel; p4 forward_mqa].  Each workgroup normalises and rotates its own q
+ * heads (written back to q in place, as dsv4_kv_insert does) and quantises into the cache
+ * the new latent rows of its request's tokens up to its own before it attends; a token of
+ * no request inserts its own row only.  Arguments: those of dsv4_kv_insert (q, kv,
+ * positions, slot_mapping, cos_sin / max_pos, q_norm_weight, eps, kv_cache) and of
+ * dsv4_sparse_mla_decode_topk, in that order, sharing the cache and T / H.
+ * Precondition for the result (q, cache bytes, out, lse) to equal the two calls in
+ * sequence: a slot read by a token's combined row is written in this call only by
+ * tokens of the same request at positions up to the token's own, i.e. slot_mapping and
+ * positions agree with the block tables and the positions the combine derives from
+ * query_start_loc and seq_lens, as in a decode step.  The inserted rows of a request are
+ * quantised by every workgroup of each of its tokens (a request of n new tokens does
+ * O(n^2) row insertions): meant for decode batches of a few tokens per request; long
+ * prefills use the two entry points.  Requires what both entry points require.
+ */
+int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* positions,
+                                const int64_t* slot_mapping, const float* cos_sin, int max_pos,
+                                const void* q_norm_weight, float eps, uint8_t* kv_cache,
+                                int num_pages, int page_size, const int32_t* topk, int topk_stride,
+                                int topk_width, const int32_t* topk_lens,
+                                const int32_t* query_start_loc, const int32_t* seq_lens,
+                                const int32_t* block_table, int block_table_stride, int B,
+                                int top_k, int window, const float* sinks, float softmax_scale,
+                                void* out, float* lse, int T, int H, void* stream);
+
+/*
  * dsv4_sparse_mla_prefill — the same result as dsv4_sparse_mla_decode, scheduled for
  * many query tokens per call (prefill: each token of a long sequence attends its own
  * combined index row) [p3 Motivation/Implementation breakdown: sparse prefill index

@@ -45,6 +45,8 @@ _lib.dsv4_combine_indices_compressed.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp,
 _lib.dsv4_sparse_mla_decode_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp,
                                              _vp, _i32, _i32, _i32, _i32, _vp, _f32, _vp, _vp,
                                              _i32, _i32, _vp]
+_lib.dsv4_sparse_mla_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _vp, _i32,
+                                             _i32] + _lib.dsv4_sparse_mla_decode_topk.argtypes[4:]
 _lib.dsv4_indexer_topk.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp,
                                    _vp]
 _lib.dsv4_gather_workspace.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp,
@@ -52,14 +54,16 @@ _lib.dsv4_gather_workspace.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i3
 for _f in (_lib.dsv4_kv_insert, _lib.dsv4_combine_indices, _lib.dsv4_sparse_mla_decode,
            _lib.dsv4_sparse_mla_prefill, _lib.dsv4_gather_dequant, _lib.dsv4_sparse_mla_decode_split,
            _lib.dsv4_combine_indices_compressed, _lib.dsv4_gather_workspace,
-           _lib.dsv4_indexer_topk, _lib.dsv4_sparse_mla_decode_topk):
+           _lib.dsv4_indexer_topk, _lib.dsv4_sparse_mla_decode_topk,
+           _lib.dsv4_sparse_mla_decode_step):
     _f.restype = _i32
 
 EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4_kv_insert",
             "dsv4_combine_indices", "dsv4_sparse_mla_decode", "dsv4_sparse_mla_prefill",
             "dsv4_gather_dequant", "dsv4_sparse_mla_split_workspace_bytes",
             "dsv4_sparse_mla_decode_split", "dsv4_combine_indices_compressed",
-            "dsv4_gather_workspace", "dsv4_indexer_topk", "dsv4_sparse_mla_decode_topk"]
+            "dsv4_gather_workspace", "dsv4_indexer_topk", "dsv4_sparse_mla_decode_topk",
+            "dsv4_sparse_mla_decode_step"]
 
 
 class Dsv4Error(RuntimeError):
@@ -243,6 +247,34 @@ def dsv4_sparse_mla_decode_topk(q, kv_cache, topk, topk_lens, query_start_loc, s
         _ptr(topk_lens), _ptr(query_start_loc), _ptr(seq_lens), _ptr(block_table),
         block_table.shape[1], seq_lens.shape[0], top_k, window, _ptr(sinks), float(softmax_scale),
         _ptr(out), _ptr(lse), T, H, _stream(stream)))
+    return out
+
+
+def dsv4_sparse_mla_decode_step(q, kv, positions, slot_mapping, cos_sin, q_norm_weight, eps,
+                                kv_cache, topk, topk_lens, query_start_loc, seq_lens, block_table,
+                                top_k, window, sinks, softmax_scale, out, lse=None, page_size=64,
+                                topk_width=None, stream=None):
+    """dsv4_kv_insert + dsv4_sparse_mla_decode_topk in one launch: the arguments of the
+    two (q normalised in place, the new kv rows inserted into kv_cache) -> out bf16
+    [T, H, 512] (and lse fp32 [T, H] if given)."""
+    _want(q, torch.bfloat16, "q"), _want(kv, torch.bfloat16, "kv")
+    _want(positions, torch.int64, "positions"), _want(slot_mapping, torch.int64, "slot_mapping")
+    _want(cos_sin, torch.float32, "cos_sin"), _want(q_norm_weight, torch.bfloat16, "q_norm_weight")
+    _want(kv_cache, torch.uint8, "kv_cache")
+    for t, n in ((topk, "topk"), (topk_lens, "topk_lens"), (query_start_loc, "query_start_loc"),
+                 (seq_lens, "seq_lens"), (block_table, "block_table")):
+        _want(t, torch.int32, n)
+    _want(sinks, torch.float32, "sinks"), _want(out, torch.bfloat16, "out")
+    _want(lse, torch.float32, "lse")
+    T, H = q.shape[0], q.shape[1]
+    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    width = topk.shape[1] if topk_width is None else topk_width
+    _check(_lib.dsv4_sparse_mla_decode_step(
+        _ptr(q), _ptr(kv), _ptr(positions), _ptr(slot_mapping), _ptr(cos_sin), cos_sin.shape[0],
+        _ptr(q_norm_weight), float(eps), _ptr(kv_cache), num_pages, page_size, _ptr(topk),
+        topk.shape[1], width, _ptr(topk_lens), _ptr(query_start_loc), _ptr(seq_lens),
+        _ptr(block_table), block_table.shape[1], seq_lens.shape[0], top_k, window, _ptr(sinks),
+        float(softmax_scale), _ptr(out), _ptr(lse), T, H, _stream(stream)))
     return out
 
 

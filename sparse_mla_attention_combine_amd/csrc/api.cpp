@@ -315,6 +315,49 @@ int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_
                     fn);
 }
 
+int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* positions,
+                                const int64_t* slot_mapping, const float* cos_sin, int max_pos,
+                                const void* q_norm_weight, float eps, uint8_t* kv_cache,
+                                int num_pages, int page_size, const int32_t* topk, int topk_stride,
+                                int topk_width, const int32_t* topk_lens,
+                                const int32_t* query_start_loc, const int32_t* seq_lens,
+                                const int32_t* block_table, int block_table_stride, int B,
+                                int top_k, int window, const float* sinks, float softmax_scale,
+                                void* out, float* lse, int T, int H, void* stream) {
+  const char* fn = "dsv4_sparse_mla_decode_step";
+  if (T < 0 || B < 0 || top_k < 0 || window < 0 || topk_width < 0 || topk_stride < topk_width ||
+      block_table_stride < 0 || max_pos < 0)
+    return fail(DSV4_ERR_SHAPE, "%s: negative size or topk_stride < topk_width", fn);
+  if (H != 16 && H != 32 && H != 64 && H != 128)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: H = %d not in {16, 32, 64, 128}", fn, H);
+  int st = check_page(fn, page_size, num_pages);
+  if (st) return st;
+  if (top_k > topk_width) return fail(DSV4_ERR_SHAPE, "%s: top_k %d > topk_width %d", fn, top_k, topk_width);
+  if ((int64_t)top_k + window > 4096)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: top_k + window = %lld > 4096", fn, (long long)top_k + window);
+  if (!(softmax_scale == softmax_scale)) return fail(DSV4_ERR_SHAPE, "%s: softmax_scale is NaN", fn);
+  if (!(eps >= 0.f)) return fail(DSV4_ERR_SHAPE, "%s: eps must be >= 0", fn);
+  if (T == 0) return ok();
+  if (!q || !kv || !positions || !slot_mapping || !cos_sin || !q_norm_weight || !out ||
+      !query_start_loc || !seq_lens || (!topk && topk_width > 0) ||
+      (!block_table && block_table_stride > 0) || (!kv_cache && num_pages > 0))
+    return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(q_norm_weight, 16) || !aligned(cos_sin, 16) ||
+      !aligned(out, 16) || (kv_cache && !aligned(kv_cache, 16)))
+    return fail(DSV4_ERR_ALIGN, "%s: q, kv, q_norm_weight, cos_sin, out and kv_cache must be 16-byte aligned", fn);
+  if (!aligned(positions, 8) || !aligned(slot_mapping, 8) || (topk && !aligned(topk, 4)) ||
+      !aligned(query_start_loc, 4) || !aligned(seq_lens, 4))
+    return fail(DSV4_ERR_ALIGN, "%s: positions, slot_mapping 8-byte aligned; int32 arrays 4-byte", fn);
+  return hip_status(dsv4::launch_attention_step(q, kv, positions, slot_mapping, cos_sin, max_pos,
+                                                q_norm_weight, eps, kv_cache, num_pages,
+                                                dsv4::page_shift_of(page_size), topk, topk_stride,
+                                                topk_width, topk_lens, query_start_loc, seq_lens,
+                                                block_table, block_table_stride, B, top_k, window,
+                                                sinks, softmax_scale, out, lse, T, H,
+                                                static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int dsv4_sparse_mla_prefill(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
                             const int32_t* indices, int idx_stride, const int32_t* lens,
                             const float* sinks, float softmax_scale, void* out, float* lse, int T,

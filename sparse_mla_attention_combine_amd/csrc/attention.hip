@@ -34,6 +34,7 @@
 // Numerics: bf16 operands, fp32 accumulation and softmax, P rounded to bf16 for P.V;
 // the per-head sink enters only the final denominator.
 #include "device.hpp"
+#include "insert_rows.hpp"
 #include "launch.hpp"
 
 namespace dsv4 {
@@ -72,6 +73,21 @@ struct TopkIn {
   int window;
 };
 
+// Inputs of the insert step when the decode performs it too (the arguments of
+// dsv4_kv_insert): q is normalised in place and the new latent rows go into the cache,
+// which the decode then reads through `cache`.
+struct StepIn {
+  uint16_t* q;
+  const uint16_t* kv;
+  const int64_t* positions;
+  const int64_t* slot_mapping;
+  const float* cos_sin;
+  int max_pos;
+  const uint16_t* weight;
+  float eps;
+  uint8_t* cache;
+};
+
 // Source of the (all-zero) record read for an invalid or absent slot, so that every
 // lane issues the same loads every chunk: branch-free loads let the compiler wait for
 // exactly the chunk it is about to use while later chunks stay in flight.
@@ -104,9 +120,11 @@ __device__ __forceinline__ void load_raw_slot(RawSlot& r, const CacheRef& c, int
   r.sc = *reinterpret_cast<const uint2*>(base + scale_off(off, c.ps));
 }
 
-// Entry jj of the staged index block (-1 past its end).
+// Entry jj of the staged index block (-1 past its end).  The read is unconditional (at a
+// clamped index) and the value selected afterwards, so no branch surrounds it.
 __device__ __forceinline__ int64_t idx_at(const int32_t* idx_lds, int jj, int n_blk) {
-  return jj < n_blk ? (int64_t)idx_lds[jj] : -1;
+  const int32_t v = idx_lds[min(jj, kIdxBlock - 1)];
+  return jj < n_blk ? (int64_t)v : -1;
 }
 
 // Copies entries [0, n_win) of an index block into LDS with every load in flight before
@@ -131,17 +149,21 @@ __device__ __forceinline__ void stage_idx(int32_t* dst, const int32_t* __restric
 // Every load is unconditional at a clamped, in-bounds address (only uniform conditions
 // skip one) and its value is selected afterwards: a load under a per-lane condition is
 // waited for on the spot, which would serialise them.
+// In two parts: combine_request issues the top-k row loads and finds the token's request
+// (sm.req); combine_rows, after whatever the caller does in between (loads issued there
+// overlap the block-table loads), builds the row.
+constexpr int kCombPer = kIdxBlock / 256;
+
 template <int NHB>
-__device__ __forceinline__ int stage_combined(AttnSmem<NHB>& sm, const TopkIn& c, int64_t t, int ps,
-                                             int tid) {
-  constexpr int kPer = kIdxBlock / 256;
+__device__ __forceinline__ void combine_request(AttnSmem<NHB>& sm, const TopkIn& c, int64_t t,
+                                                int tid, int32_t (&xv)[kCombPer], int& tl) {
+  constexpr int kPer = kCombPer;
   const int kmax = min(c.top_k, c.topk_width);
-  int32_t xv[kPer];
   const int32_t* trow = c.topk + t * c.topk_stride;
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
     xv[u] = 256 * u < kmax ? trow[min(tid + 256 * u, kmax - 1)] : -1;
-  const int tl = c.topk_lens ? c.topk_lens[t] : c.top_k;
+  tl = c.topk_lens ? c.topk_lens[t] : c.top_k;
   if (tid == 0) sm.req[0] = -1;
   __syncthreads();
   const int base = c.qsl[0];
@@ -158,6 +180,13 @@ __device__ __forceinline__ int stage_combined(AttnSmem<NHB>& sm, const TopkIn& c
     }
   }
   __syncthreads();
+}
+
+template <int NHB>
+__device__ __forceinline__ int combine_rows(AttnSmem<NHB>& sm, const TopkIn& c, int64_t t, int ps,
+                                           int tid, const int32_t (&xv)[kCombPer], int tl) {
+  constexpr int kPer = kCombPer;
+  const int kmax = min(c.top_k, c.topk_width);
   const int b = sm.req[0];
   if (b < 0) return 0;
   const int64_t pos = (int64_t)sm.req[3] - sm.req[2] + (t - sm.req[1]);
@@ -189,6 +218,15 @@ __device__ __forceinline__ int stage_combined(AttnSmem<NHB>& sm, const TopkIn& c
     if (j < n) sm.idx[j] = ok ? (int32_t)(((int64_t)pg[u] << ps) + (x & ((1 << ps) - 1))) : -1;
   }
   return n;
+}
+
+template <int NHB>
+__device__ __forceinline__ int stage_combined(AttnSmem<NHB>& sm, const TopkIn& c, int64_t t, int ps,
+                                             int tid) {
+  int32_t xv[kCombPer];
+  int tl;
+  combine_request<NHB>(sm, c, t, tid, xv, tl);
+  return combine_rows<NHB>(sm, c, t, ps, tid, xv, tl);
 }
 
 // Where this lane's pieces of a slot's record live (the zero page for an invalid slot).
@@ -567,6 +605,21 @@ __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnSt
   resolve_chunk<NHB>(sm.p[nb], sm.red[nb], st, s, scale_log2, psum, w, l16, g);
 }
 
+static_assert(32 * kLatent <= kChunk * kVStride, "32 q rows fit one value-tile buffer");
+
+// Q^T fragments of one block of 16 heads from q row `qr` (global memory or LDS): lane
+// (head l16, k-group g); k-step s pairs with the K-fragment dims chosen in load_raw
+// (nope: 64u+16g+8h, rope: 32r+8g).
+__device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[18], const uint16_t* qr, int g) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    qf[2 * u] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 64 * u + 16 * g));
+    qf[2 * u + 1] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 64 * u + 16 * g + 8));
+  }
+  qf[16] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kNope + 8 * g));
+  qf[17] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kNope + 32 + 8 * g));
+}
+
 // The block's last chunk: P.V only.
 template <int NHB>
 __device__ __forceinline__ void pv_last(AttnSmem<NHB>& sm, int cb, AttnState<NHB>& st,
@@ -582,13 +635,21 @@ __device__ __forceinline__ void pv_last(AttnSmem<NHB>& sm, int cb, AttnState<NHB
 
 // FUSED: the index rows are built in the prologue from the combine step's inputs (`tin`)
 // instead of read from `indices` / `lens` (one row per token, no pieces).
-template <int NHB, bool FUSED>
+// STEP (with FUSED): the prologue also performs the insert step (`sti`) for what this
+// workgroup reads: it normalises and rotates its own q heads (written back in place and
+// kept in LDS for the Q fragments) and quantises into the cache the new latent rows of
+// its request's tokens up to its own, plus its own row; `q` and `cache` are unused and
+// the cache is read through sti.cache.  Only this workgroup reads what it wrote (other
+// workgroups that write the same rows write the same bytes), so the barrier's
+// workgroup-scope ordering suffices.
+template <int NHB, bool FUSED, bool STEP>
 __global__ void __launch_bounds__(256) sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int64_t num_slots, int ps,
     const int32_t* __restrict__ indices, int idx_stride, const int32_t* __restrict__ lens,
     const float* __restrict__ sinks, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, int T, int H, int groups, int splits, int split_len,
-    float* __restrict__ part_o, float* __restrict__ part_ml, TopkIn tin) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, TopkIn tin, StepIn sti) {
+  static_assert(FUSED || !STEP, "the step variant builds its index rows itself");
   __shared__ AttnSmem<NHB> sm;
 
   // work item vt = (query token, split); with one split it is the query token
@@ -621,18 +682,37 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   const int lim = FUSED ? kIdxBlock : beg + min(split_len, idx_stride - beg);
 
   AttnState<NHB> st;
-  // Q^T fragments: lane (head l16 of block hb, k-group g); k-step s pairs with the
-  // K-fragment dims chosen in load_raw (nope: 64u+16g+8h, rope: 32r+8g).
+  // STEP: wave w < 2*NHB owns q heads h0 + 8w .. +7 (8 lanes a row, the insert kernel's
+  // partition, so the bits match it); every wave w owns the new latent rows t - w, t - w - 4,
+  // ... of the request.  The q rows, positions and the first latent row are requested here,
+  // beside the combine step's loads.
+  const int c8 = lane & 7;
+  u32x4 qraw[9];  // (a native vector: copies of the struct type would keep it in memory)
+  int64_t qp = -1, kvp = -1, kvs = -1;
+  KvLane kvv;
+  const float* const no_row = reinterpret_cast<const float*>(g_zero_page);  // unused values
+  if constexpr (STEP) {
+    if (w < 2 * NHB) {
+      const uint16_t* qr = sti.q + ((int64_t)t * H + h0 + 8 * w + (lane >> 3)) * kLatent;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) qraw[k] = *reinterpret_cast<const u32x4*>(qr + 8 * (c8 + 8 * k));
+    }
+    qp = sti.positions[t];
+    const int64_t t1 = t >= w ? t - w : t;  // in bounds; used only if in the request
+    kvv = kv_lane_load(sti.kv + t1 * kLatent, lane);
+    kvp = sti.positions[t1];
+    kvs = sti.slot_mapping[t1];
+  } else {
+    // Q^T fragments: lane (head l16 of block hb, k-group g); k-step s pairs with the
+    // K-fragment dims chosen in load_raw (nope: 64u+16g+8h, rope: 32r+8g).
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const uint16_t* qr = q + ((int64_t)t * H + h0 + 16 * hb + l16) * kLatent;
+      load_q_frags(st.qf[hb], qr, g);
+    }
+  }
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    const uint16_t* qr = q + ((int64_t)t * H + h0 + 16 * hb + l16) * kLatent;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      st.qf[hb][2 * u] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 64 * u + 16 * g));
-      st.qf[hb][2 * u + 1] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 64 * u + 16 * g + 8));
-    }
-    st.qf[hb][16] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kNope + 8 * g));
-    st.qf[hb][17] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kNope + 32 + 8 * g));
     st.m_run[hb] = kMFloor;
     st.l_part[hb] = 0.f;
   }
@@ -649,15 +729,73 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   // The first block is requested together with Q and the row length (entries past the
   // length are staged but never used), so the prologue waits for memory only once.
   int end;
-  if constexpr (FUSED) {
+  if constexpr (STEP) {
+    int32_t xv[kCombPer];
+    int tl;
+    combine_request<NHB>(sm, tin, t, tid, xv, tl);
+    // The first round of loads is in.  The q rows wait in LDS (the second value-tile
+    // buffer, first written by chunk 1's staging); the weight chunks and the cos/sin rows
+    // are requested beside the block-table loads, so the insert work below waits for no
+    // further round.
+    const bool qok = qp >= 0 && qp < sti.max_pos;
+    u32x4 wq[9];
+    u32x4* ql = reinterpret_cast<u32x4*>(&sm.v[1][0][0]) + (8 * w + (lane >> 3)) * (kLatent / 8) + c8;
+    if (w < 2 * NHB) {  // chunk k of this lane's row: 16-byte unit c8 + 8k of the row
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        ql[8 * k] = qraw[k];
+        wq[k] = *reinterpret_cast<const u32x4*>(sti.weight + 8 * (c8 + 8 * k));
+      }
+    }
+    const RopeCs qrot = rope_cs_load(qok ? sti.cos_sin + qp * kRope : no_row, c8);
+    const RopeCs kvrot =
+        rope_cs_load(kvp >= 0 && kvp < sti.max_pos ? sti.cos_sin + kvp * kRope : no_row, lane);
+    end = combine_rows<NHB>(sm, tin, t, ps, tid, xv, tl);
+    // this wave's q rows normalised and rotated in LDS (each lane rereads its own chunks)
+    // and written back in place
+    if (w < 2 * NHB && qok) {
+      u32x4* qg = reinterpret_cast<u32x4*>(sti.q + ((int64_t)t * H + h0 + 8 * w + (lane >> 3)) *
+                                                       kLatent) + c8;
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) ss = qn_sum_sq(ql[8 * k], ss);
+      const float inv = qn_inv(ss, sti.eps);
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        const u32x4 y = qn_chunk(ql[8 * k], wq[k], inv, qrot, k == 8);
+        ql[8 * k] = y;
+        qg[8 * k] = y;
+      }
+    }
+    // the new rows this token may read: its request's tokens up to itself (only itself for
+    // a token of no request, whose own row is inserted all the same)
+    const int64_t first = sm.req[0] >= 0 ? (int64_t)max(sm.req[1], 0) : (int64_t)t;
+    int64_t tt = (int64_t)t - w;
+    if (tt >= first && kvp >= 0 && kvp < sti.max_pos && kvs >= 0 && kvs < num_slots)
+      kv_quant_store(kvv, kvrot, sti.cache + page_base(kvs >> ps, ps),
+                     (int)(kvs & ((1 << ps) - 1)), ps, lane);
+    for (tt -= 4; tt >= first; tt -= 4) {
+      const KvLane v = kv_lane_load(sti.kv + tt * kLatent, lane);
+      const int64_t p = sti.positions[tt], sl = sti.slot_mapping[tt];
+      if (p >= 0 && p < sti.max_pos && sl >= 0 && sl < num_slots)
+        kv_quant_store(v, rope_cs_load(sti.cos_sin + p * kRope, lane),
+                       sti.cache + page_base(sl >> ps, ps), (int)(sl & ((1 << ps) - 1)), ps, lane);
+    }
+  } else if constexpr (FUSED) {
     end = stage_combined<NHB>(sm, tin, t, ps, tid);
   } else {
     stage_idx(sm.idx, idx_row + beg, min(lim - beg, kIdxBlock), tid);
     end = min(max(__builtin_amdgcn_readfirstlane(n_lens_v), 0), lim);
   }
-  __syncthreads();
+  __syncthreads();  // (STEP: also the q rows in LDS and this workgroup's cache rows written)
+  if constexpr (STEP) {
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+      load_q_frags(st.qf[hb], reinterpret_cast<const uint16_t*>(&sm.v[1][0][0]) +
+                                  (16 * hb + l16) * kLatent, g);
+  }
   const int row = 16 * w + l16;
-  const CacheRef cr{cache, num_slots, ps};
+  const CacheRef cr{STEP ? sti.cache : cache, num_slots, ps};
   for (int blk0 = beg; blk0 < end; blk0 += kIdxBlock) {
     const int n_blk = min(end - blk0, kIdxBlock);
     if (blk0 != beg) {
@@ -810,27 +948,28 @@ size_t split_workspace_bytes(int T, int H, int splits) {
   return (size_t)T * splits * H * (kNope + 2) * sizeof(float);
 }
 
-template <bool FUSED>
+template <bool FUSED, bool STEP>
 static hipError_t launch_items(const void* q, const uint8_t* cache, int num_pages, int ps,
                                const int32_t* indices, int idx_stride, const int32_t* lens,
                                const float* sinks, float softmax_scale, void* out, float* lse,
                                int T, int H, int splits, int split_len, float* part_o,
-                               float* part_ml, const TopkIn& tin, hipStream_t stream) {
+                               float* part_ml, const TopkIn& tin, const StepIn& sti,
+                               hipStream_t stream) {
   const int64_t num_slots = (int64_t)num_pages << ps;
   const float scale_log2 = softmax_scale * kLog2e;
   const int items = T * splits;
   if (H == 16) {
-    hipLaunchKernelGGL((sparse_mla_kernel<1, FUSED>), dim3(items), dim3(256), 0, stream,
+    hipLaunchKernelGGL((sparse_mla_kernel<1, FUSED, STEP>), dim3(items), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), cache, num_slots, ps, indices, idx_stride, lens,
                        sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, 1, splits,
-                       split_len, part_o, part_ml, tin);
+                       split_len, part_o, part_ml, tin, sti);
   } else {
     const int groups = H / 32;
     const int grid = groups == 1 ? items : 8 * groups * ((items + 7) / 8);
-    hipLaunchKernelGGL((sparse_mla_kernel<2, FUSED>), dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL((sparse_mla_kernel<2, FUSED, STEP>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), cache, num_slots, ps, indices, idx_stride, lens,
                        sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, groups, splits,
-                       split_len, part_o, part_ml, tin);
+                       split_len, part_o, part_ml, tin, sti);
   }
   return hipGetLastError();
 }
@@ -845,9 +984,29 @@ hipError_t launch_attention_topk(const void* q, const uint8_t* cache, int num_pa
   if (T == 0) return hipSuccess;
   const TopkIn tin{topk, topk_stride, topk_width, topk_lens, qsl, seq_lens, block_table,
                    bt_stride, B, top_k, window};
-  return launch_items<true>(q, cache, num_pages, page_shift, nullptr, 0, nullptr, sinks,
-                            softmax_scale, out, lse, T, H, 1, kIdxBlock, nullptr, nullptr, tin,
-                            stream);
+  return launch_items<true, false>(q, cache, num_pages, page_shift, nullptr, 0, nullptr, sinks,
+                                   softmax_scale, out, lse, T, H, 1, kIdxBlock, nullptr, nullptr,
+                                   tin, StepIn{}, stream);
+}
+
+hipError_t launch_attention_step(void* q, const void* kv, const int64_t* positions,
+                                 const int64_t* slot_mapping, const float* cos_sin, int max_pos,
+                                 const void* q_norm_weight, float eps, uint8_t* cache,
+                                 int num_pages, int page_shift, const int32_t* topk,
+                                 int topk_stride, int topk_width, const int32_t* topk_lens,
+                                 const int32_t* qsl, const int32_t* seq_lens,
+                                 const int32_t* block_table, int bt_stride, int B, int top_k,
+                                 int window, const float* sinks, float softmax_scale, void* out,
+                                 float* lse, int T, int H, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const TopkIn tin{topk, topk_stride, topk_width, topk_lens, qsl, seq_lens, block_table,
+                   bt_stride, B, top_k, window};
+  const StepIn sti{static_cast<uint16_t*>(q), static_cast<const uint16_t*>(kv), positions,
+                   slot_mapping, cos_sin, max_pos, static_cast<const uint16_t*>(q_norm_weight),
+                   eps, cache};
+  return launch_items<true, true>(nullptr, nullptr, num_pages, page_shift, nullptr, 0, nullptr,
+                                  sinks, softmax_scale, out, lse, T, H, 1, kIdxBlock, nullptr,
+                                  nullptr, tin, sti, stream);
 }
 
 hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, int page_shift,
@@ -857,9 +1016,9 @@ hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, 
   (void)prefill;  // one schedule serves both entry points for now
   if (T == 0) return hipSuccess;
   const int whole = idx_stride > 0 ? idx_stride : 1;
-  return launch_items<false>(q, cache, num_pages, page_shift, indices, idx_stride, lens, sinks,
-                             softmax_scale, out, lse, T, H, 1, whole, nullptr, nullptr, TopkIn{},
-                             stream);
+  return launch_items<false, false>(q, cache, num_pages, page_shift, indices, idx_stride, lens,
+                                    sinks, softmax_scale, out, lse, T, H, 1, whole, nullptr,
+                                    nullptr, TopkIn{}, StepIn{}, stream);
 }
 
 hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_pages,
@@ -872,9 +1031,9 @@ hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_p
   const int split_len = per > 0 ? ((per + kChunk - 1) / kChunk) * kChunk : kChunk;
   float* part_o = static_cast<float*>(workspace);
   float* part_ml = part_o + (size_t)T * splits * H * kNope;
-  hipError_t e = launch_items<false>(q, cache, num_pages, page_shift, indices, idx_stride, lens,
-                                     sinks, softmax_scale, out, lse, T, H, splits, split_len,
-                                     part_o, part_ml, TopkIn{}, stream);
+  hipError_t e = launch_items<false, false>(q, cache, num_pages, page_shift, indices, idx_stride,
+                                            lens, sinks, softmax_scale, out, lse, T, H, splits,
+                                            split_len, part_o, part_ml, TopkIn{}, StepIn{}, stream);
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)T * H;
   hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,

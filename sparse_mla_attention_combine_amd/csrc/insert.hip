@@ -13,6 +13,7 @@
 // block amax is exact, the exponent is taken from the fp32 bit fields, the scaling by
 // 2^-e is exact and the E4M3 rounding is gfx950's RNE conversion -> bit-exact bytes.
 #include "device.hpp"
+#include "insert_rows.hpp"
 #include "launch.hpp"
 
 namespace dsv4 {
@@ -24,17 +25,9 @@ __device__ __forceinline__ void q_norm_rope(
   const int lane = threadIdx.x & 63;
   const int r8 = lane >> 3, c8 = lane & 7;
   // this lane always touches chunks c8 + 8k (k = 0..8) of a row: keep their weights
-  float w[72];
+  u32x4 w[9];
 #pragma unroll
-  for (int k = 0; k < 9; ++k) {
-    uint4 v = *reinterpret_cast<const uint4*>(weight + 8 * (c8 + 8 * k));
-    uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w[8 * k + 2 * e] = bf16_bits_to_f32(u[e] & 0xFFFF);
-      w[8 * k + 2 * e + 1] = bf16_bits_to_f32(u[e] >> 16);
-    }
-  }
+  for (int k = 0; k < 9; ++k) w[k] = *reinterpret_cast<const u32x4*>(weight + 8 * (c8 + 8 * k));
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)qblocks * blockDim.x) >> 6;
   for (int64_t g = wave; g * 8 < rows; g += nwaves) {
@@ -42,48 +35,22 @@ __device__ __forceinline__ void q_norm_rope(
     if (row >= rows) continue;
     const int64_t t = row / H;
     const int64_t p = positions[t];
-    if (p < 0 || p >= max_pos) continue;  // token left untouched
     uint16_t* qr = q + row * kLatent;
-    float x[72];
+    // the row is requested together with its position; the position is only tested after
+    // the row has been consumed, so the compiler keeps the loads side by side
+    u32x4 x[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) x[k] = *reinterpret_cast<const u32x4*>(qr + 8 * (c8 + 8 * k));
+    const bool ok = p >= 0 && p < max_pos;
+    const RopeCs rot = rope_cs_load(cos_sin + (ok ? p : 0) * kRope, c8);
     float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      uint4 v = *reinterpret_cast<const uint4*>(qr + 8 * (c8 + 8 * k));
-      uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    for (int k = 0; k < 9; ++k) ss = qn_sum_sq(x[k], ss);
+    const float inv = qn_inv(ss, eps);
+    if (!ok) continue;  // token left untouched
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[8 * k + 2 * e] = bf16_bits_to_f32(u[e] & 0xFFFF);
-        x[8 * k + 2 * e + 1] = bf16_bits_to_f32(u[e] >> 16);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 72; ++i) ss += x[i] * x[i];
-    ss += __shfl_xor(ss, 1, 8);
-    ss += __shfl_xor(ss, 2, 8);
-    ss += __shfl_xor(ss, 4, 8);
-    const float inv = 1.0f / sqrtf(ss * (1.0f / kLatent) + eps);
-#pragma unroll
-    for (int i = 0; i < 72; ++i) x[i] = x[i] * inv * w[i];
-    // chunk k = 8 holds dims 512 + 8*c8 .. +7, i.e. rotary pairs 4*c8 .. 4*c8+3
-    const float* cs = cos_sin + p * kRope + 4 * c8;
-    const float4 cv = *reinterpret_cast<const float4*>(cs);
-    const float4 sv = *reinterpret_cast<const float4*>(cs + kRope / 2);
-    const float cc[4] = {cv.x, cv.y, cv.z, cv.w}, sn[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = x[64 + 2 * e], b = x[64 + 2 * e + 1];
-      x[64 + 2 * e] = a * cc[e] - b * sn[e];
-      x[64 + 2 * e + 1] = a * sn[e] + b * cc[e];
-    }
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      uint4 v;
-      v.x = pack_bf16x2(x[8 * k + 0], x[8 * k + 1]);
-      v.y = pack_bf16x2(x[8 * k + 2], x[8 * k + 3]);
-      v.z = pack_bf16x2(x[8 * k + 4], x[8 * k + 5]);
-      v.w = pack_bf16x2(x[8 * k + 6], x[8 * k + 7]);
-      *reinterpret_cast<uint4*>(qr + 8 * (c8 + 8 * k)) = v;
-    }
+    for (int k = 0; k < 9; ++k)
+      *reinterpret_cast<u32x4*>(qr + 8 * (c8 + 8 * k)) = qn_chunk(x[k], w[k], inv, rot, k == 8);
   }
 }
 
@@ -94,66 +61,13 @@ __device__ __forceinline__ void kv_quant_insert(
   const int lane = threadIdx.x & 63;
   const int64_t t = ((int64_t)block * blockDim.x + threadIdx.x) >> 6;
   if (t >= T) return;
+  // the row is requested beside its position and slot
+  const KvLane v = kv_lane_load(kv + t * kLatent, lane);
   const int64_t p = positions[t];
   const int64_t slot = slot_mapping[t];
   if (p < 0 || p >= max_pos || slot < 0 || slot >= num_slots) return;
-  const int64_t page = slot >> ps;
-  const int off = (int)(slot & ((1 << ps) - 1));
-  uint8_t* base = cache + page_base(page, ps);
-  const uint16_t* kr = kv + t * kLatent;
-
-  // nope dims 8*lane .. 8*lane+7, block lane/8
-  uint4 v = *reinterpret_cast<const uint4*>(kr + 8 * lane);
-  uint32_t u[4] = {v.x, v.y, v.z, v.w};
-  float k[8];
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    k[2 * e] = bf16_bits_to_f32(u[e] & 0xFFFF);
-    k[2 * e + 1] = bf16_bits_to_f32(u[e] >> 16);
-    amax = fmaxf(amax, fmaxf(fabsf(k[2 * e]), fabsf(k[2 * e + 1])));
-  }
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
-  // smallest e with amax <= 448 * 2^e: amax = m * 2^k, m in [1,2): e = k-8 if m <= 1.75
-  // else k-7; zero and fp32-subnormal amax (< 2^-126 < 448 * 2^-127) give e = -127.
-  const uint32_t ab = __float_as_uint(amax);
-  const int fexp = (int)(ab >> 23);
-  int e = -127;
-  if (fexp != 0) {
-    e = (fexp - 127) - 8 + ((ab & 0x7FFFFF) > 0x600000 ? 1 : 0);
-    e = max(-127, min(127, e));
-  }
-  uint32_t codes[2] = {0u, 0u};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    int c = 0;
-    c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(k[4 * h + 0], -e),
-                                        __builtin_amdgcn_ldexpf(k[4 * h + 1], -e), c, false);
-    c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(k[4 * h + 2], -e),
-                                        __builtin_amdgcn_ldexpf(k[4 * h + 3], -e), c, true);
-    codes[h] = (uint32_t)c;
-  }
-  *reinterpret_cast<uint2*>(base + nope_off(off) + 8 * lane) = make_uint2(codes[0], codes[1]);
-  if ((lane & 7) == 0) base[scale_off(off, ps) + (lane >> 3)] = (uint8_t)(e + 127);
-
-  // rope dims 512 + 8*lane .. +7 for lanes 0..7, stored rotated (bf16)
-  if (lane < 8) {
-    uint4 rv = *reinterpret_cast<const uint4*>(kr + kNope + 8 * lane);
-    uint32_t ru[4] = {rv.x, rv.y, rv.z, rv.w};
-    const float* cs = cos_sin + p * kRope + 4 * lane;
-    const float4 cv = *reinterpret_cast<const float4*>(cs);
-    const float4 sv = *reinterpret_cast<const float4*>(cs + kRope / 2);
-    const float cc[4] = {cv.x, cv.y, cv.z, cv.w}, sn[4] = {sv.x, sv.y, sv.z, sv.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const float a = bf16_bits_to_f32(ru[e2] & 0xFFFF), b = bf16_bits_to_f32(ru[e2] >> 16);
-      o[e2] = pack_bf16x2(a * cc[e2] - b * sn[e2], a * sn[e2] + b * cc[e2]);
-    }
-    *reinterpret_cast<uint4*>(base + rope_off(off, ps) + 16 * lane) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+  kv_quant_store(v, rope_cs_load(cos_sin + p * kRope, lane), cache + page_base(slot >> ps, ps),
+                 (int)(slot & ((1 << ps) - 1)), ps, lane);
 }
 
 // One launch: blocks [0, qblocks) stream the q rows, the remaining blocks quantise the
@@ -174,7 +88,8 @@ hipError_t launch_insert(void* q, const void* kv, const int64_t* positions,
                          const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                          const void* weight, float eps, uint8_t* cache, int num_pages,
                          int page_shift, int T, int H, hipStream_t stream) {
-  if (T == 0) return hipSuccess;
+  // no valid position: every token is left untouched (and the cos/sin table may be empty)
+  if (T == 0 || max_pos <= 0) return hipSuccess;
   const int64_t rows = (int64_t)T * H;
   const int64_t groups = (rows + 31) / 32;  // 32 q rows per 256-thread block per pass
   const int qblocks = rows > 0 ? (int)(groups < 8192 ? groups : 8192) : 0;

@@ -1,0 +1,153 @@
+// Per-row pieces of the fused insert (per-head q RMSNorm + GPT-J RoPE; FP8 E4M3 / UE8M0
+// quantisation of a latent row into the cache), shared by the insert kernel and the
+// decode kernel that performs the whole step, so that both compute identical bits.
+// Follows PR #42953 (Implementation breakdown item 4; Key source excerpts:
+// _fused_qnorm_rope_kv_insert called with q, kv, kv_cache, slot_mapping, positions).
+#pragma once
+#include "device.hpp"
+
+namespace dsv4 {
+
+// cos and sin of rotary pairs 4j .. 4j+3 (j = lane & 7) of a position's row of the
+// table (64 floats: 32 cos then 32 sin).
+struct RopeCs {
+  float4 c;
+  float4 s;
+};
+
+__device__ __forceinline__ RopeCs rope_cs_load(const float* __restrict__ row, int lane) {
+  RopeCs r;
+  r.c = *reinterpret_cast<const float4*>(row + 4 * (lane & 7));
+  r.s = *reinterpret_cast<const float4*>(row + 4 * (lane & 7) + kRope / 2);
+  return r;
+}
+
+// q row RMSNorm + RoPE.  8 lanes (lane & 7 = c8) hold chunks c8 + 8k (k = 0..8) of one
+// head's 576 dims, i.e. dims 8(c8 + 8k) .. +7.  Two passes over the chunks, in k order:
+//   ss  = qn_sum_sq(chunk k, ss) for k = 0..8   (squares added in dim order in the lane)
+//   inv = qn_inv(ss, eps)                        (sum over the 8 lanes by xor-shuffles,
+//                                                 eps inside the square root)
+//   out = qn_chunk(chunk k, weight chunk k, inv, rot, k == 8)
+// where qn_chunk multiplies by inv and the weight, rotates the GPT-J pairs of dims
+// 512..575 (chunk 8; `rot` holds the position's cos/sin values, rope_cs_load) and rounds
+// once to bf16.  The chunks may live in registers or in LDS: every caller runs this same
+// sequence of operations, so all produce the same bits.
+__device__ __forceinline__ float qn_sum_sq(u32x4 c, float ss) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = bf16_bits_to_f32(c[e] & 0xFFFF), b = bf16_bits_to_f32(c[e] >> 16);
+    ss += a * a;
+    ss += b * b;
+  }
+  return ss;
+}
+
+// All 8 lanes of a row must take part.
+__device__ __forceinline__ float qn_inv(float ss, float eps) {
+  ss += __shfl_xor(ss, 1, 8);
+  ss += __shfl_xor(ss, 2, 8);
+  ss += __shfl_xor(ss, 4, 8);
+  return 1.0f / sqrtf(ss * (1.0f / kLatent) + eps);
+}
+
+__device__ __forceinline__ u32x4 qn_chunk(u32x4 c, u32x4 w, float inv, const RopeCs& rot,
+                                          bool rope) {
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[2 * e] = bf16_bits_to_f32(c[e] & 0xFFFF) * inv * bf16_bits_to_f32(w[e] & 0xFFFF);
+    y[2 * e + 1] = bf16_bits_to_f32(c[e] >> 16) * inv * bf16_bits_to_f32(w[e] >> 16);
+  }
+  if (rope) {
+    // chunk 8 holds dims 512 + 8*c8 .. +7, i.e. rotary pairs 4*c8 .. 4*c8+3
+    const float cc[4] = {rot.c.x, rot.c.y, rot.c.z, rot.c.w};
+    const float sn[4] = {rot.s.x, rot.s.y, rot.s.z, rot.s.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = y[2 * e], b = y[2 * e + 1];
+      y[2 * e] = a * cc[e] - b * sn[e];
+      y[2 * e + 1] = a * sn[e] + b * cc[e];
+    }
+  }
+  u32x4 o;
+  o[0] = pack_bf16x2(y[0], y[1]);
+  o[1] = pack_bf16x2(y[2], y[3]);
+  o[2] = pack_bf16x2(y[4], y[5]);
+  o[3] = pack_bf16x2(y[6], y[7]);
+  return o;
+}
+
+// One lane's share of a latent row (576 bf16) for a wave of 64 lanes: nope dims
+// 8*lane .. 8*lane+7 (quantisation block lane/8) and rope dims 512 + 8*(lane&7) .. +7
+// (used by lanes 0..7; every lane loads, so no load sits under a per-lane condition).
+struct KvLane {
+  uint4 nope;
+  uint4 rope;
+};
+
+__device__ __forceinline__ KvLane kv_lane_load(const uint16_t* __restrict__ kr, int lane) {
+  KvLane v;
+  v.nope = *reinterpret_cast<const uint4*>(kr + 8 * lane);
+  v.rope = *reinterpret_cast<const uint4*>(kr + kNope + 8 * (lane & 7));
+  return v;
+}
+
+// Quantises the row held by a wave (kv_lane_load) into the record of slot `off` of the
+// page at `base` (pages of 2^ps slots); `rot` holds the cos/sin values of the row's
+// position (rope_cs_load).
+// The block amax is exact, the exponent comes from the fp32 bit fields, the scaling by
+// 2^-e is exact and the E4M3 rounding is gfx950's RNE conversion; lanes 0..7 rotate and
+// store the rope dims.  All 64 lanes must take part.
+__device__ __forceinline__ void kv_quant_store(const KvLane& v, const RopeCs& rot,
+                                               uint8_t* __restrict__ base, int off, int ps,
+                                               int lane) {
+  const uint32_t u[4] = {v.nope.x, v.nope.y, v.nope.z, v.nope.w};
+  float k[8];
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    k[2 * e] = bf16_bits_to_f32(u[e] & 0xFFFF);
+    k[2 * e + 1] = bf16_bits_to_f32(u[e] >> 16);
+    amax = fmaxf(amax, fmaxf(fabsf(k[2 * e]), fabsf(k[2 * e + 1])));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+  amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+  // smallest e with amax <= 448 * 2^e: amax = m * 2^k, m in [1,2): e = k-8 if m <= 1.75
+  // else k-7; zero and fp32-subnormal amax (< 2^-126 < 448 * 2^-127) give e = -127.
+  const uint32_t ab = __float_as_uint(amax);
+  const int fexp = (int)(ab >> 23);
+  int e = -127;
+  if (fexp != 0) {
+    e = (fexp - 127) - 8 + ((ab & 0x7FFFFF) > 0x600000 ? 1 : 0);
+    e = max(-127, min(127, e));
+  }
+  uint32_t codes[2] = {0u, 0u};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int c = 0;
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(k[4 * h + 0], -e),
+                                        __builtin_amdgcn_ldexpf(k[4 * h + 1], -e), c, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(k[4 * h + 2], -e),
+                                        __builtin_amdgcn_ldexpf(k[4 * h + 3], -e), c, true);
+    codes[h] = (uint32_t)c;
+  }
+  *reinterpret_cast<uint2*>(base + nope_off(off) + 8 * lane) = make_uint2(codes[0], codes[1]);
+  if ((lane & 7) == 0) base[scale_off(off, ps) + (lane >> 3)] = (uint8_t)(e + 127);
+
+  // rope dims 512 + 8*lane .. +7 for lanes 0..7, stored rotated (bf16)
+  if (lane < 8) {
+    const uint32_t ru[4] = {v.rope.x, v.rope.y, v.rope.z, v.rope.w};
+    const float cc[4] = {rot.c.x, rot.c.y, rot.c.z, rot.c.w};
+    const float sn[4] = {rot.s.x, rot.s.y, rot.s.z, rot.s.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float a = bf16_bits_to_f32(ru[e2] & 0xFFFF), b = bf16_bits_to_f32(ru[e2] >> 16);
+      o[e2] = pack_bf16x2(a * cc[e2] - b * sn[e2], a * sn[e2] + b * cc[e2]);
+    }
+    *reinterpret_cast<uint4*>(base + rope_off(off, ps) + 16 * lane) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+}  // namespace dsv4

@@ -71,4 +71,15 @@ hipError_t launch_attention_topk(const void* q, const uint8_t* cache, int num_pa
                                  float softmax_scale, void* out, float* lse, int T, int H,
                                  hipStream_t stream);
 
+// The insert step and the fused combine + decode in one launch (see sparse_mla_kernel).
+hipError_t launch_attention_step(void* q, const void* kv, const int64_t* positions,
+                                 const int64_t* slot_mapping, const float* cos_sin, int max_pos,
+                                 const void* q_norm_weight, float eps, uint8_t* cache,
+                                 int num_pages, int page_shift, const int32_t* topk,
+                                 int topk_stride, int topk_width, const int32_t* topk_lens,
+                                 const int32_t* qsl, const int32_t* seq_lens,
+                                 const int32_t* block_table, int bt_stride, int B, int top_k,
+                                 int window, const float* sinks, float softmax_scale, void* out,
+                                 float* lse, int T, int H, hipStream_t stream);
+
 }  // namespace dsv4

@@ -192,6 +192,35 @@ def test_decode_topk_validation(dsv4):
     assert call(T=0) == 0
 
 
+def test_decode_step_validation(dsv4):
+    lib = dsv4.library()
+    keep, p = _fake()
+
+    def call(**kw):
+        a = dict(q=p, kv=p, pos=p, sm=p, cs=p, maxp=100, w=p, eps=1e-6, cache=p, npg=4, P=64,
+                 topk=p, ts=2048, tw=2048, tl=None, qsl=p, sl=p, bt=p, bts=8, B=2, top_k=2048,
+                 window=128, sinks=None, scale=0.04, out=p, lse=None, T=2, H=128)
+        a.update(kw)
+        return lib.dsv4_sparse_mla_decode_step(
+            a["q"], a["kv"], a["pos"], a["sm"], a["cs"], a["maxp"], a["w"], a["eps"], a["cache"],
+            a["npg"], a["P"], a["topk"], a["ts"], a["tw"], a["tl"], a["qsl"], a["sl"], a["bt"],
+            a["bts"], a["B"], a["top_k"], a["window"], a["sinks"], a["scale"], a["out"], a["lse"],
+            a["T"], a["H"], None)
+
+    assert call(window=2049) == 4 and b"4096" in lib.dsv4_last_error()
+    assert call(H=24) == 4
+    assert call(P=48) == 4
+    assert call(top_k=3000) == 2
+    assert call(maxp=-1) == 2
+    assert call(eps=-1.0) == 2
+    assert call(kv=None) == 1
+    assert call(w=None) == 1
+    assert call(cs=None) == 1
+    assert call(q=ctypes.c_void_p(p.value + 8)) == 3
+    assert call(pos=ctypes.c_void_p(p.value + 4)) == 3
+    assert call(T=0) == 0
+
+
 def test_insert_and_gather_validation(dsv4):
     lib = dsv4.library()
     keep, p = _fake()

@@ -204,3 +204,27 @@ def test_insert_edge_cases_and_codec_sweep(dsv4):
     wl0 = dict(wl, q=np.zeros((T, 0, 576), np.uint16))
     _, c_gpu0 = _insert_gpu(dsv4, wl0, cache0)
     assert np.array_equal(c_gpu0, c_gpu)
+
+
+def test_insert_without_rope_rows_touches_nothing(dsv4):
+    """max_pos = 0 (a rope table of no rows) leaves every position out of range: q and the
+    cache keep their bytes and the table is never read (called through the C-ABI with a
+    valid table pointer and max_pos 0)."""
+    import ctypes
+    rng = np.random.default_rng(6)
+    T, H, num_pages = 9, 2, 2
+    q0 = bf16_normal(rng, (T, H, 576))
+    cache0 = rng.integers(0, 256, size=num_pages * P * 648, dtype=np.uint8)
+    qd, cache = dev_bf16(q0), dev(cache0)
+    kv = dev_bf16(bf16_normal(rng, (T, 576)))
+    pos, slots = dev(np.zeros(T, np.int64)), dev(np.arange(T, dtype=np.int64))
+    table = torch.zeros(4, 64, dtype=torch.float32, device="cuda")
+    w = dev_bf16(bf16_normal(rng, (576,)))
+    vp = ctypes.c_void_p
+    st = dsv4.library().dsv4_kv_insert(vp(qd.data_ptr()), vp(kv.data_ptr()), vp(pos.data_ptr()),
+                                       vp(slots.data_ptr()), vp(table.data_ptr()), 0,
+                                       vp(w.data_ptr()), ctypes.c_float(1e-6),
+                                       vp(cache.data_ptr()), num_pages, P, T, H, None)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert np.array_equal(host_bits(qd), q0) and np.array_equal(cache.cpu().numpy(), cache0)
