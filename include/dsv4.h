@@ -163,7 +163,8 @@ int dsv4_combine_indices(const int32_t* topk, int topk_stride, int topk_width,
  * unique.)  Tokens of no request are not written.  The output is the topk / topk_lens
  * input of dsv4_combine_indices (compress_ratio 1: ids are positions) and of
  * dsv4_combine_indices_compressed.
- *   logits int32-aligned fp32 [T][logits_stride]; topk int32 [T][topk_stride];
+ *   logits int32-aligned fp32 [T][logits_stride]; topk int32 [T][topk_stride] (may be
+ *   NULL when topk_stride is 0);
  *   topk_lens int32 [T]; query_start_loc int32 [B+1]; seq_lens int32 [B]
  * Requires compress_ratio >= 1, topk_stride >= top_k >= 0.
  */

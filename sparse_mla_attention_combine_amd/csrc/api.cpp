@@ -186,7 +186,8 @@ int dsv4_indexer_topk(const float* logits, int logits_stride, const int32_t* que
   if (topk_stride < top_k)
     return fail(DSV4_ERR_SHAPE, "%s: topk_stride %d < top_k %d", fn, topk_stride, top_k);
   if (B == 0 || T == 0) return ok();
-  if (!query_start_loc || !seq_lens || !topk || !topk_lens || (!logits && logits_stride > 0))
+  if (!query_start_loc || !seq_lens || (!topk && topk_stride > 0) || !topk_lens ||
+      (!logits && logits_stride > 0))
     return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
   if ((logits && !aligned(logits, 4)) || !aligned(topk, 4) || !aligned(topk_lens, 4))
     return fail(DSV4_ERR_ALIGN, "%s: arrays must be 4-byte aligned", fn);

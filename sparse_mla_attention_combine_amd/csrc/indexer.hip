@@ -50,6 +50,156 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int* wsum) {
   return x + add;
 }
 
+template <int NT, bool STAGE>
+struct SelSmem {
+  uint32_t keys[STAGE ? kStageMax : 1];
+  uint32_t hist[kBins];
+  int wsum[NT / 64];
+  uint32_t sh_digit, sh_above;
+};
+
+// The k largest of n keys (0 < k < n), ties to the smaller index j: a radix select of the
+// k-th largest key K (digits of 11, 11 and 10 bits, most significant first) and how many
+// keys equal to K are taken (m), then one ordered pass that calls emit(p, j, key) for
+// every j with key > K and the first m with key == K, p = the pick's rank in ascending j.
+// key_at(j) gives key j for 0 <= j < n; the first pass calls it for every j (eight per
+// thread in flight, at clamped indices) and, with STAGE and n <= kStageMax, keeps the
+// keys in LDS for the other passes; otherwise every pass calls it again.  NT threads,
+// all of which must call; barriers inside.
+template <int NT, bool STAGE, typename KeyAt, typename Emit>
+__device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm, int n, int k, KeyAt key_at,
+                                             Emit emit) {
+  const int tid = threadIdx.x;
+  const bool staged = STAGE && n <= kStageMax;
+  uint32_t prefix = 0, mask = 0;
+  int remaining = k;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+    for (int d = tid; d < kBins; d += NT) sm.hist[d] = 0;
+    __syncthreads();
+    if (staged && pass > 0) {
+      for (int j = tid; j < n; j += NT) {
+        const uint32_t key = sm.keys[j];
+        if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & dmask], 1u);
+      }
+    } else {
+      // eight keys per thread requested at a time, at clamped indices (a load under a
+      // per-lane condition is waited for on the spot); entries past n are ignored
+      for (int j0 = 0; j0 < n; j0 += NT * kSelItems) {
+        uint32_t v[kSelItems];
+#pragma unroll
+        for (int u = 0; u < kSelItems; ++u) v[u] = key_at(min(j0 + u * NT + tid, n - 1));
+#pragma unroll
+        for (int u = 0; u < kSelItems; ++u) {
+          const int j = j0 + u * NT + tid;
+          if (j < n) {
+            if (staged) sm.keys[j] = v[u];
+            if ((v[u] & mask) == prefix) atomicAdd(&sm.hist[(v[u] >> shift) & dmask], 1u);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // thread i owns the kBins/NT digits below dmask - (kBins/NT)*i (from the top); after
+    // the scan of its counts it knows how many matching keys have a larger digit than
+    // each of them, and the one whose range covers `remaining` is the digit
+    constexpr int kPer = kBins / NT;
+    int cnt[kPer];
+    int sum = 0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int d = (int)dmask - kPer * tid - r;
+      cnt[r] = d >= 0 ? (int)sm.hist[d] : 0;
+      sum += cnt[r];
+    }
+    const int incl = block_inclusive_scan<NT>(sum, sm.wsum);
+    int above = incl - sum;  // keys with a digit larger than this thread's first
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int d = (int)dmask - kPer * tid - r;
+      if (d >= 0 && above < remaining && above + cnt[r] >= remaining) {
+        sm.sh_digit = (uint32_t)d;
+        sm.sh_above = (uint32_t)above;
+      }
+      above += cnt[r];
+    }
+    __syncthreads();
+    prefix |= sm.sh_digit << shift;
+    mask |= dmask << shift;
+    remaining -= (int)sm.sh_above;
+    __syncthreads();  // sh_digit / sh_above / hist are rewritten next pass
+  }
+  const uint32_t K = prefix;
+  const int m = remaining;  // keys equal to K that are taken, the smallest indices first
+  int gt_run = 0, eq_run = 0;
+  for (int c0 = 0; c0 < n; c0 += NT * kSelItems) {
+    const int first = c0 + tid * kSelItems;
+    uint32_t key[kSelItems];
+    int cgt = 0, ceq = 0;
+    if (staged) {
+#pragma unroll
+      for (int j = 0; j < kSelItems; ++j) key[j] = first + j < n ? sm.keys[first + j] : 0u;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSelItems; ++j) key[j] = key_at(min(first + j, n - 1));
+    }
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+      cgt += (first + j < n && key[j] > K) ? 1 : 0;
+      ceq += (first + j < n && key[j] == K) ? 1 : 0;
+    }
+    // at most 8192 of each per pass: pack (gt, eq) into one scan
+    const int packed = cgt | (ceq << 16);
+    const int incl = block_inclusive_scan<NT>(packed, sm.wsum);
+    const int excl = incl - packed;
+    const int gt_before = gt_run + (excl & 0xFFFF);
+    const int eq_before = eq_run + (excl >> 16);
+    int p = gt_before + min(eq_before, m);
+    int eq_rank = eq_before;
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+      if (first + j >= n) break;
+      if (key[j] > K) {
+        emit(p++, first + j, key[j]);
+      } else if (key[j] == K) {
+        if (eq_rank < m) emit(p++, first + j, key[j]);
+        ++eq_rank;
+      }
+    }
+    // block totals of this pass: the last thread's inclusive value
+    if (tid == NT - 1) sm.wsum[0] = incl;
+    __syncthreads();
+    const int tot = sm.wsum[0];
+    gt_run += tot & 0xFFFF;
+    eq_run += tot >> 16;
+    __syncthreads();
+  }
+}
+
+// Token i of request b: its position and candidate count (the causal bound).
+struct IdxTok {
+  int64_t t;
+  int n;
+  int k;
+};
+
+__device__ __forceinline__ IdxTok indexer_token(const int32_t* __restrict__ qsl,
+                                                const int32_t* __restrict__ seq_lens, int b,
+                                                int i, int logits_stride, int ratio, int top_k) {
+  const int base = qsl[0];
+  const int q0 = qsl[b] - base;
+  const int qlen = qsl[b + 1] - qsl[b];
+  const int64_t pos = (int64_t)seq_lens[b] - qlen + i;
+  const int64_t n64 = pos + 1 > 0 ? (pos + 1) / ratio : 0;
+  IdxTok r;
+  r.t = (int64_t)q0 + i;
+  r.n = (int)min(n64, (int64_t)logits_stride);
+  r.k = min(r.n, top_k);
+  return r;
+}
+
 // NT threads per token; STAGE keeps the keys of rows up to kStageMax candidates in LDS
 // (few tokens, long rows: one large workgroup per CU), otherwise every pass rereads the
 // row from the caches (many tokens: several small workgroups per CU).
@@ -58,161 +208,24 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(
     const float* __restrict__ logits, int logits_stride, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ seq_lens, int T, int ratio, int top_k, int32_t* __restrict__ topk,
     int topk_stride, int32_t* __restrict__ topk_lens) {
-  constexpr int kSelThreads = NT;
-  __shared__ uint32_t keys[STAGE ? kStageMax : 1];
-  __shared__ uint32_t hist[kBins];
-  __shared__ int wsum[NT / 64];
-  __shared__ uint32_t sh_digit, sh_above;
+  __shared__ SelSmem<NT, STAGE> sm;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  const int base = qsl[0];
-  const int q0 = qsl[b] - base;
   const int qlen = qsl[b + 1] - qsl[b];
-  const int seq_len = seq_lens[b];
   for (int i = blockIdx.y; i < qlen; i += gridDim.y) {
-    const int64_t t = (int64_t)q0 + i;
-    if (t < 0 || t >= T) continue;
-    const int64_t pos = (int64_t)seq_len - qlen + i;
-    int64_t n64 = pos + 1 > 0 ? (pos + 1) / ratio : 0;
-    const int n = (int)min(n64, (int64_t)logits_stride);
-    const int k = min(n, top_k);
-    const float* row = logits + t * (int64_t)logits_stride;
-    int32_t* out = topk + t * (int64_t)topk_stride;
+    const IdxTok tk = indexer_token(qsl, seq_lens, b, i, logits_stride, ratio, top_k);
+    if (tk.t < 0 || tk.t >= T) continue;
+    const int n = tk.n, k = tk.k;
+    const float* row = logits + tk.t * (int64_t)logits_stride;
+    int32_t* out = topk + tk.t * (int64_t)topk_stride;
     if (k == n) {
-      for (int j = tid; j < n; j += kSelThreads) out[j] = j;
+      for (int j = tid; j < n; j += NT) out[j] = j;
     } else if (k > 0) {
-      const bool staged = STAGE && n <= kStageMax;
-      // radix select of the k-th largest key (digits of 11, 11 and 10 bits, most
-      // significant first); the first pass also stages the keys
-      uint32_t prefix = 0, mask = 0;
-      int remaining = k;
-#pragma unroll 1
-      for (int pass = 0; pass < 3; ++pass) {
-        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const uint32_t dmask = pass == 2 ? 1023u : 2047u;
-        for (int d = tid; d < kBins; d += kSelThreads) hist[d] = 0;
-        __syncthreads();
-        if (pass == 0) {
-          for (int j0 = 0; j0 < n; j0 += kSelThreads * kSelItems) {
-            float v[kSelItems];
-#pragma unroll
-            for (int u = 0; u < kSelItems; ++u) {
-              // unconditional load at a clamped index (a load under a per-lane condition
-              // is waited for on the spot); entries past n are ignored below
-              const int j = j0 + u * kSelThreads + tid;
-              v[u] = j0 + u * kSelThreads < n ? row[min(j, n - 1)] : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < kSelItems; ++u) {
-              const int j = j0 + u * kSelThreads + tid;
-              if (j < n) {
-                const uint32_t key = order_key(v[u]);
-                if (staged) keys[j] = key;
-                atomicAdd(&hist[key >> 21], 1u);
-              }
-            }
-          }
-        } else if (staged) {
-          for (int j = tid; j < n; j += kSelThreads) {
-            const uint32_t key = keys[j];
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
-          }
-        } else {
-          // eight loads per thread in flight at a time, at clamped indices
-          for (int j0 = 0; j0 < n; j0 += kSelThreads * kSelItems) {
-            float v[kSelItems];
-#pragma unroll
-            for (int u = 0; u < kSelItems; ++u)
-              v[u] = row[min(j0 + u * kSelThreads + tid, n - 1)];
-#pragma unroll
-            for (int u = 0; u < kSelItems; ++u) {
-              const uint32_t key = order_key(v[u]);
-              if (j0 + u * kSelThreads + tid < n && (key & mask) == prefix)
-                atomicAdd(&hist[(key >> shift) & dmask], 1u);
-            }
-          }
-        }
-        __syncthreads();
-        // thread i owns the kBins/NT digits below dmask - (kBins/NT)*i (from the top);
-        // after the scan of its counts it knows how many matching keys have a larger
-        // digit than each of them, and the one whose range covers `remaining` is the digit
-        constexpr int kPer = kBins / NT;
-        int cnt[kPer];
-        int sum = 0;
-#pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-          const int d = (int)dmask - kPer * tid - r;
-          cnt[r] = d >= 0 ? (int)hist[d] : 0;
-          sum += cnt[r];
-        }
-        const int incl = block_inclusive_scan<NT>(sum, wsum);
-        int above = incl - sum;  // keys with a digit larger than this thread's first
-#pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-          const int d = (int)dmask - kPer * tid - r;
-          if (d >= 0 && above < remaining && above + cnt[r] >= remaining) {
-            sh_digit = (uint32_t)d;
-            sh_above = (uint32_t)above;
-          }
-          above += cnt[r];
-        }
-        __syncthreads();
-        prefix |= sh_digit << shift;
-        mask |= dmask << shift;
-        remaining -= (int)sh_above;
-        __syncthreads();  // sh_digit / sh_above / hist are rewritten next pass
-      }
-      const uint32_t K = prefix;
-      const int m = remaining;  // keys equal to K that are taken, the smallest ids first
-      int gt_run = 0, eq_run = 0;
-      for (int c0 = 0; c0 < n; c0 += kSelThreads * kSelItems) {
-        const int first = c0 + tid * kSelItems;
-        uint32_t key[kSelItems];
-        int cgt = 0, ceq = 0;
-        if (staged) {
-#pragma unroll
-          for (int j = 0; j < kSelItems; ++j) key[j] = first + j < n ? keys[first + j] : 0u;
-        } else {
-          float lv[kSelItems];  // every load first (clamped), then their use
-#pragma unroll
-          for (int j = 0; j < kSelItems; ++j) lv[j] = row[min(first + j, n - 1)];
-#pragma unroll
-          for (int j = 0; j < kSelItems; ++j) key[j] = first + j < n ? order_key(lv[j]) : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < kSelItems; ++j) {
-          cgt += (first + j < n && key[j] > K) ? 1 : 0;
-          ceq += (first + j < n && key[j] == K) ? 1 : 0;
-        }
-        // at most 8192 of each per pass: pack (gt, eq) into one scan
-        const int packed = cgt | (ceq << 16);
-        const int incl = block_inclusive_scan<NT>(packed, wsum);
-        const int excl = incl - packed;
-        const int gt_before = gt_run + (excl & 0xFFFF);
-        const int eq_before = eq_run + (excl >> 16);
-        int p = gt_before + min(eq_before, m);
-        int eq_rank = eq_before;
-#pragma unroll
-        for (int j = 0; j < kSelItems; ++j) {
-          if (first + j >= n) break;
-          if (key[j] > K) {
-            out[p++] = first + j;
-          } else if (key[j] == K) {
-            if (eq_rank < m) out[p++] = first + j;
-            ++eq_rank;
-          }
-        }
-        // block totals of this pass: the last thread's inclusive value
-        if (tid == kSelThreads - 1) wsum[0] = incl;
-        __syncthreads();
-        const int tot = wsum[0];
-        gt_run += tot & 0xFFFF;
-        eq_run += tot >> 16;
-        __syncthreads();
-      }
+      radix_select<NT, STAGE>(sm, n, k, [&](int j) { return order_key(row[j]); },
+                              [&](int p, int j, uint32_t) { out[p] = j; });
     }
-    for (int j = k + tid; j < topk_stride; j += kSelThreads) out[j] = -1;
-    if (tid == 0) topk_lens[t] = k;
+    for (int j = k + tid; j < topk_stride; j += NT) out[j] = -1;
+    if (tid == 0) topk_lens[tk.t] = k;
     __syncthreads();  // LDS reuse by the next token of this workgroup
   }
 }

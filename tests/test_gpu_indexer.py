@@ -129,3 +129,14 @@ def test_indexer_topk_rows_longer_than_the_lds_stage(dsv4):
     ref, rlen = oracle.indexer_topk(logits, qsl, seq, T, 1, top_k, top_k)
     got, glen = _gpu_topk(dsv4, logits, qsl, seq, T, 1, top_k, top_k)
     assert np.array_equal(glen, rlen) and np.array_equal(got, ref)
+
+
+def test_indexer_topk_zero_width_output(dsv4):
+    """top_k 0 with a zero-width topk (a NULL pointer): only the counts are written."""
+    qsl = np.array([0, 2], np.int32)
+    seq = np.array([100], np.int32)
+    lens = torch.full((2,), -7, dtype=torch.int32, device="cuda")
+    out = torch.empty((2, 0), dtype=torch.int32, device="cuda")
+    dsv4.dsv4_indexer_topk(dev(np.zeros((2, 64), np.float32)), dev(qsl), dev(seq), 0, out, lens)
+    torch.cuda.synchronize()
+    assert lens.cpu().tolist() == [0, 0]
