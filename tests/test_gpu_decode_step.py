@@ -2,7 +2,7 @@
 q, cache bytes, output and lse are bit-identical to dsv4_kv_insert followed by
 dsv4_sparse_mla_decode_topk on random multi-token requests (more new tokens per request
 than a workgroup has waves, windows over the new rows, holes, tokens of no request,
-skipped positions) at every head-group shape and two page sizes, with the new rows'
+skipped positions) at every head-group shape and page sizes 32, 64 and 256, with the new rows'
 slots holding garbage beforehand; on the full benchmark workload and under HIP-graph
 replay; and equal to the oracle's insert -> combine -> attention chain within the
 attention bar on a small case."""
@@ -107,10 +107,10 @@ def _random_case(rng, P, H, qmax, B=None, top_k=None, window=None):
     return c, dev_bf16(h["q"]), dev(cache), h
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(10))
 def test_decode_step_equals_insert_then_decode_topk(dsv4, seed):
     rng = np.random.default_rng(3000 + seed)
-    P = [64, 32][seed % 2]
+    P = [64, 32, 256][seed % 3]
     H = [128, 16, 64, 32][seed % 4]
     qmax = [1, 3, 7, 12][seed % 4]
     c, q0, cache0, _ = _random_case(rng, P, H, qmax)
