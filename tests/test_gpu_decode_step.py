@@ -52,12 +52,14 @@ def _run_step(dsv4, c, q0, cache0, out=None, lse=None):
     return q, cache, out, lse
 
 
-def _random_case(rng, P, H, qmax, B=None, top_k=None, window=None):
+def _random_case(rng, P, H, qmax, B=None, top_k=None, window=None, max_len=2500,
+                 full_rows=False):
     B = int(rng.integers(1, 5)) if B is None else B
     top_k = int(rng.choice([16, 300, 2048])) if top_k is None else top_k
     window = int(rng.choice([0, 1, 4, 128])) if window is None else window
     qlens = rng.integers(1, qmax + 1, size=B)
-    seq_lens = np.array([int(rng.integers(ql, 2500)) for ql in qlens], np.int32)
+    lo_len = max_len - 200 if full_rows else 0
+    seq_lens = np.array([int(rng.integers(max(ql, lo_len), max_len)) for ql in qlens], np.int32)
     qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32) + int(rng.integers(0, 2))
     T = int(qsl[-1] - qsl[0]) + 2  # the last two tokens belong to no request
     pages = [int(np.ceil(L / P)) for L in seq_lens]
@@ -88,13 +90,17 @@ def _random_case(rng, P, H, qmax, B=None, top_k=None, window=None):
     ctx_p = np.concatenate([np.arange(L - ql) for L, ql in zip(seq_lens, qlens)]).astype(np.int64)
     keep = bt[ctx_b, ctx_p // P] >= 0
     ctx_s = bt[ctx_b[keep], ctx_p[keep] // P].astype(np.int64) * P + ctx_p[keep] % P
-    cos_sin = rope_table(2600)
+    cos_sin = rope_table(max_len + 100)
     oracle.kv_insert(np.zeros((ctx_s.size, 0, 576), np.uint16),
                      bf16_normal(rng, (ctx_s.size, 576)), ctx_p[keep], ctx_s, cos_sin,
                      np.zeros(576, np.uint16), 1e-6, cache, npg, P, inplace=True)
-    topk = rng.integers(-3, 2600, size=(T, top_k)).astype(np.int32)
+    if full_rows:  # distinct valid picks: every row as long as top_k allows
+        topk = np.stack([rng.permutation(max_len - 200 - 1)[:top_k] for _ in range(T)]).astype(np.int32)
+    else:
+        topk = rng.integers(-3, max_len + 100, size=(T, top_k)).astype(np.int32)
     # fewer picks than the cap in some rows: the causal prefix of the top-k
-    tl = rng.integers(0, top_k + 2, size=T).astype(np.int32) if rng.integers(0, 2) else None
+    tl = (rng.integers(0, top_k + 2, size=T).astype(np.int32)
+          if rng.integers(0, 2) and not full_rows else None)
     sinks = rng.standard_normal(H).astype(np.float32) if rng.integers(0, 2) else None
     h = dict(P=P, top_k=top_k, window=window, B=B, T=T, npg=npg, kv=bf16_normal(rng, (T, 576)),
              pos=pos, slots=slots, cos_sin=cos_sin, w=bf16_normal(rng, (576,), mean=1.0, std=0.1),
@@ -209,3 +215,34 @@ def test_decode_step_against_oracle(dsv4):
     assert np.all(ratio <= 1.0)
     assert_attention_close(host_bits(out), ref, "decode_step vs oracle")
     assert np.max(np.abs(lse.cpu().numpy() - rlse)) <= 2e-3
+
+
+def test_decode_step_longest_row(dsv4):
+    """The longest combined row the one-launch forms take (top_k + window = 4096 entries,
+    the whole LDS index block): both fused entry points against insert + combine +
+    decode."""
+    rng = np.random.default_rng(3100)
+    P, H = 64, 128
+    c, q0, cache0, h = _random_case(rng, P, H, 2, B=3, top_k=3968, window=128, max_len=4600,
+                                    full_rows=True)
+    log(f"decode_step longest row: T={c['T']} top_k=3968 window=128")
+    qa, ca, oa, la = _run_two(dsv4, c, q0, cache0)
+    qb, cb, ob, lb = _run_step(dsv4, c, q0, cache0)
+    # the three-launch reference: insert, combine into rows of 4096, decode
+    q3, c3 = q0.clone(), cache0.clone()
+    T = c["T"]
+    dsv4.dsv4_kv_insert(q3, c["kv"], c["pos"], c["slots"], c["cos_sin"], c["w"], 1e-6, c3,
+                        page_size=P)
+    comb = torch.full((T, 4096), -1, dtype=torch.int32, device="cuda")
+    lens = torch.zeros(T, dtype=torch.int32, device="cuda")
+    dsv4.dsv4_combine_indices(c["topk"], c["tl"], c["qsl"], c["sl"], c["bt"], c["top_k"],
+                              c["window"], comb, lens, page_size=P)
+    o3 = torch.empty(T, H, 512, dtype=torch.bfloat16, device="cuda")
+    l3 = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    dsv4.dsv4_sparse_mla_decode(q3, c3, comb, lens, c["sinks"], c["scale"], o3, l3, page_size=P)
+    torch.cuda.synchronize()
+    assert int(lens.max()) == 4096  # rows of the full length occur
+    assert _same(qa, qb) and torch.equal(ca, cb) and _same(oa, ob) and _same(la, lb)
+    # rows of tokens of no request are empty in the fused forms; compare the request rows
+    nreq = int(h["qsl"][-1] - h["qsl"][0])
+    assert _same(ob[:nreq], o3[:nreq]) and _same(lb[:nreq], l3[:nreq])
