@@ -33,6 +33,12 @@
 //      reads; these MFMAs are issued after the softmax and run across the barrier.
 // Numerics: bf16 operands, fp32 accumulation and softmax, P rounded to bf16 for P.V;
 // the per-head sink enters only the final denominator.
+// Variants of one kernel: the index rows come from memory (decode, prefill, and pieces of
+// rows for the split decode), or each workgroup builds its token's row in LDS from the
+// combine step's inputs (PR #43385 combine kernel: top-k, window, block table), or it
+// also performs the insert step first (PR #42953 Implementation breakdown item 4: q
+// RMSNorm + GPT-J RoPE, FP8/UE8M0 insert of the new latent rows) so that one launch is
+// the whole decode step.
 #include "device.hpp"
 #include "insert_rows.hpp"
 #include "launch.hpp"
@@ -726,8 +732,11 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   // Index blocks of up to 4096 entries are staged in LDS.  Inside a block chunk c lives
   // in register buffer c&1 and LDS tiles c&1; a buffer is refilled with chunk c+2 as
   // soon as staging has consumed it, so two chunks of records are always in flight.
-  // The first block is requested together with Q and the row length (entries past the
-  // length are staged but never used), so the prologue waits for memory only once.
+  // Rows from memory: the first block is requested together with Q and the row length
+  // (entries past the length are staged but never used), so the prologue waits for
+  // memory only once.  Rows built here: the top-k row and the request lookup take one
+  // round of loads, the block-table lookups a second (FUSED; STEP adds its insert work
+  // to those two rounds).
   int end;
   if constexpr (STEP) {
     int32_t xv[kCombPer];
