@@ -47,12 +47,25 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def kernel_code_hash(sources):
+    """sha256 over the kernel's source files with // comments and blank lines removed
+    (comment edits leave the counters valid; any code change invalidates them)."""
+    import hashlib
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(HERE, src)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
 def measured_traffic(which="fused"):
     """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     readings (each scaled by the reading of a 256 MiB copy), or None when the kernel's
     sources have changed since the counters were taken.  `which`: the one-launch step,
     the fused combine + decode launch or the plain decode launch."""
-    import hashlib
     name = {"step": "sparse_mla_decode_step_b64_h128_traffic.json",
             "fused": "sparse_mla_decode_topk_b64_h128_traffic.json"}.get(
                 which, "sparse_mla_decode_b64_h128_traffic.json")
@@ -60,11 +73,7 @@ def measured_traffic(which="fused"):
     try:
         with open(path) as f:
             d = json.load(f)
-        h = hashlib.sha256()
-        for src in d["kernel_sources"]:
-            with open(os.path.join(HERE, src), "rb") as f:
-                h.update(f.read())
-        if h.hexdigest() != d["kernel_source_sha256"]:
+        if kernel_code_hash(d["kernel_sources"]) != d["kernel_code_sha256"]:
             return None
         return (d["fetch_size_kib_per_dispatch"] * 1024 * d["fetch_factor"] +
                 d["write_size_kib_per_dispatch"] * 1024 * d["write_factor"])
