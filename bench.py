@@ -218,6 +218,8 @@ def main():
                  wl["top_k"], wl["window"], P(d["sinks"].data_ptr()),
                  ctypes.c_float(wl["softmax_scale"]), P(d["out"].data_ptr()), None, T, H, sp)
         one = ins[:11] + fused[4:]
+        if splits > 1:  # the split step: pieces merged by their lse, same workspace
+            one = one[:-1] + (splits, P(workspace.data_ptr()), ctypes.c_size_t(ws_bytes), sp)
         calls.append((ins, comb, dec, fused, one))
 
     def check(st):
@@ -225,9 +227,14 @@ def main():
             raise RuntimeError(lib.dsv4_last_error().decode())
 
     decode_fn = lib.dsv4_sparse_mla_decode_split if splits > 1 else lib.dsv4_sparse_mla_decode
-    launches = 3 if (args.unfused or splits > 1) else args.launches
+    launches = 3 if args.unfused else args.launches
+    if splits > 1 and launches == 2:
+        print("bench.py: --splits needs --launches 1 (the split step) or 3", file=sys.stderr)
+        sys.exit(2)
     fused_step = launches == 2
     one_launch = launches == 1
+    step_fn = (lib.dsv4_sparse_mla_decode_step_split if splits > 1
+               else lib.dsv4_sparse_mla_decode_step)
 
     def with_stream(args_tuple, stream_ptr):
         return args_tuple[:-1] + (stream_ptr,)
@@ -252,7 +259,7 @@ def main():
         def s_(a):
             return a if stream_ptr is None else with_stream(a, stream_ptr)
         if one_launch:
-            check(lib.dsv4_sparse_mla_decode_step(*s_(one)))
+            check(step_fn(*s_(one)))
             return
         check(lib.dsv4_kv_insert(*s_(ins)))
         if fused_step:
@@ -277,7 +284,7 @@ def main():
         e[3].record(stream)
         e[4].record(stream)
         if one_launch:
-            check(lib.dsv4_sparse_mla_decode_step(*one))
+            check(step_fn(*one))
         else:
             check(lib.dsv4_sparse_mla_decode_topk(*fu) if fused_step else decode_fn(*dec))
         e[5].record(stream)
@@ -369,7 +376,9 @@ def main():
         "config": {
             "workload": "sparse MLA decode step: fused q-norm/RoPE/FP8 insert + top-k/window "
                         "index combine + sparse MLA over an FP8/UE8M0 paged latent cache",
-            "launches": ("insert+combine+decode (one launch)" if one_launch
+            "launches": ("insert+combine+decode pieces, lse merge (two launches)"
+                         if one_launch and splits > 1 else
+                         "insert+combine+decode (one launch)" if one_launch
                          else "insert, combine+decode (fused)" if fused_step
                          else "insert, combine, decode"),
             "batch": T, "heads": H, "top_k": wl["top_k"], "topk_lens": "U{1024..2048}",
@@ -388,7 +397,9 @@ def main():
             "traffic": (measured_traffic("step" if one_launch else "fused" if fused_step
                                          else "decode")
                         if (splits == 1 and T == 64 and PS == 64) else None),
-            "kernel": ("sparse_mla_kernel<2> + split_merge_kernel (dsv4_sparse_mla_decode_split)"
+            "kernel": ("sparse_mla_kernel<2, fused combine, insert> pieces + split_merge_kernel "
+                       "(dsv4_sparse_mla_decode_step_split)" if splits > 1 and one_launch else
+                       "sparse_mla_kernel<2> + split_merge_kernel (dsv4_sparse_mla_decode_split)"
                        if splits > 1 else
                        "sparse_mla_kernel<2, fused combine, insert> (dsv4_sparse_mla_decode_step)"
                        if one_launch else

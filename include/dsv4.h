@@ -301,6 +301,30 @@ int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* position
                                 void* out, float* lse, int T, int H, void* stream);
 
 /*
+ * dsv4_sparse_mla_decode_step_split — dsv4_sparse_mla_decode_step with each token's row
+ * cut into `splits` pieces attended by separate workgroups and merged by their
+ * log-sum-exp (the split decode's merge), for small batches where one workgroup per
+ * (token, head group) leaves compute units idle.  The pieces are those
+ * dsv4_sparse_mla_decode_split cuts from a combined row of width
+ * round_up(top_k + window, 128), so out and lse equal dsv4_kv_insert +
+ * dsv4_combine_indices (combined_stride = that width) + dsv4_sparse_mla_decode_split with
+ * the same splits; q and the cache bytes equal dsv4_sparse_mla_decode_step's.
+ *   splits     1..64 (1: dsv4_sparse_mla_decode_step, no workspace)
+ *   workspace  caller-owned device memory of at least
+ *              dsv4_sparse_mla_split_workspace_bytes(T, H, splits) bytes, 16-byte
+ *              aligned (DSV4_ERR_WORKSPACE otherwise); it carries nothing between calls
+ * Other arguments and requirements as for dsv4_sparse_mla_decode_step.
+ */
+int dsv4_sparse_mla_decode_step_split(
+    void* q, const void* kv, const int64_t* positions, const int64_t* slot_mapping,
+    const float* cos_sin, int max_pos, const void* q_norm_weight, float eps, uint8_t* kv_cache,
+    int num_pages, int page_size, const int32_t* topk, int topk_stride, int topk_width,
+    const int32_t* topk_lens, const int32_t* query_start_loc, const int32_t* seq_lens,
+    const int32_t* block_table, int block_table_stride, int B, int top_k, int window,
+    const float* sinks, float softmax_scale, void* out, float* lse, int T, int H, int splits,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * dsv4_sparse_mla_prefill — the same result as dsv4_sparse_mla_decode, scheduled for
  * many query tokens per call (prefill: each token of a long sequence attends its own
  * combined index row) [p3 Motivation/Implementation breakdown: sparse prefill index

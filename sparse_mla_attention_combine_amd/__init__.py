@@ -47,6 +47,8 @@ _lib.dsv4_sparse_mla_decode_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _i32, _i
                                              _i32, _i32, _vp]
 _lib.dsv4_sparse_mla_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _vp, _i32,
                                              _i32] + _lib.dsv4_sparse_mla_decode_topk.argtypes[4:]
+_lib.dsv4_sparse_mla_decode_step_split.argtypes = (_lib.dsv4_sparse_mla_decode_step.argtypes[:-1]
+                                                   + [_i32, _vp, ctypes.c_size_t, _vp])
 _lib.dsv4_indexer_topk.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp,
                                    _vp]
 _lib.dsv4_gather_workspace.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp,
@@ -55,7 +57,7 @@ for _f in (_lib.dsv4_kv_insert, _lib.dsv4_combine_indices, _lib.dsv4_sparse_mla_
            _lib.dsv4_sparse_mla_prefill, _lib.dsv4_gather_dequant, _lib.dsv4_sparse_mla_decode_split,
            _lib.dsv4_combine_indices_compressed, _lib.dsv4_gather_workspace,
            _lib.dsv4_indexer_topk, _lib.dsv4_sparse_mla_decode_topk,
-           _lib.dsv4_sparse_mla_decode_step):
+           _lib.dsv4_sparse_mla_decode_step, _lib.dsv4_sparse_mla_decode_step_split):
     _f.restype = _i32
 
 EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4_kv_insert",
@@ -63,7 +65,7 @@ EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4
             "dsv4_gather_dequant", "dsv4_sparse_mla_split_workspace_bytes",
             "dsv4_sparse_mla_decode_split", "dsv4_combine_indices_compressed",
             "dsv4_gather_workspace", "dsv4_indexer_topk", "dsv4_sparse_mla_decode_topk",
-            "dsv4_sparse_mla_decode_step"]
+            "dsv4_sparse_mla_decode_step", "dsv4_sparse_mla_decode_step_split"]
 
 
 class Dsv4Error(RuntimeError):
@@ -253,10 +255,12 @@ def dsv4_sparse_mla_decode_topk(q, kv_cache, topk, topk_lens, query_start_loc, s
 def dsv4_sparse_mla_decode_step(q, kv, positions, slot_mapping, cos_sin, q_norm_weight, eps,
                                 kv_cache, topk, topk_lens, query_start_loc, seq_lens, block_table,
                                 top_k, window, sinks, softmax_scale, out, lse=None, page_size=64,
-                                topk_width=None, stream=None):
+                                topk_width=None, splits=1, workspace=None, stream=None):
     """dsv4_kv_insert + dsv4_sparse_mla_decode_topk in one launch: the arguments of the
     two (q normalised in place, the new kv rows inserted into kv_cache) -> out bf16
-    [T, H, 512] (and lse fp32 [T, H] if given)."""
+    [T, H, 512] (and lse fp32 [T, H] if given).  splits > 1: rows cut into pieces merged
+    by their lse (dsv4_sparse_mla_decode_step_split), with a device workspace of at least
+    split_workspace_bytes(T, H, splits) bytes."""
     _want(q, torch.bfloat16, "q"), _want(kv, torch.bfloat16, "kv")
     _want(positions, torch.int64, "positions"), _want(slot_mapping, torch.int64, "slot_mapping")
     _want(cos_sin, torch.float32, "cos_sin"), _want(q_norm_weight, torch.bfloat16, "q_norm_weight")
@@ -269,12 +273,17 @@ def dsv4_sparse_mla_decode_step(q, kv, positions, slot_mapping, cos_sin, q_norm_
     T, H = q.shape[0], q.shape[1]
     num_pages = kv_cache.numel() // cache_page_bytes(page_size)
     width = topk.shape[1] if topk_width is None else topk_width
-    _check(_lib.dsv4_sparse_mla_decode_step(
-        _ptr(q), _ptr(kv), _ptr(positions), _ptr(slot_mapping), _ptr(cos_sin), cos_sin.shape[0],
-        _ptr(q_norm_weight), float(eps), _ptr(kv_cache), num_pages, page_size, _ptr(topk),
-        topk.shape[1], width, _ptr(topk_lens), _ptr(query_start_loc), _ptr(seq_lens),
-        _ptr(block_table), block_table.shape[1], seq_lens.shape[0], top_k, window, _ptr(sinks),
-        float(softmax_scale), _ptr(out), _ptr(lse), T, H, _stream(stream)))
+    args = (_ptr(q), _ptr(kv), _ptr(positions), _ptr(slot_mapping), _ptr(cos_sin),
+            cos_sin.shape[0], _ptr(q_norm_weight), float(eps), _ptr(kv_cache), num_pages,
+            page_size, _ptr(topk), topk.shape[1], width, _ptr(topk_lens), _ptr(query_start_loc),
+            _ptr(seq_lens), _ptr(block_table), block_table.shape[1], seq_lens.shape[0], top_k,
+            window, _ptr(sinks), float(softmax_scale), _ptr(out), _ptr(lse), T, H)
+    if splits == 1:
+        _check(_lib.dsv4_sparse_mla_decode_step(*args, _stream(stream)))
+    else:
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(_lib.dsv4_sparse_mla_decode_step_split(*args, splits, _ptr(workspace), ws_bytes,
+                                                      _stream(stream)))
     return out
 
 

@@ -316,16 +316,16 @@ int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_
                     fn);
 }
 
-int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* positions,
-                                const int64_t* slot_mapping, const float* cos_sin, int max_pos,
-                                const void* q_norm_weight, float eps, uint8_t* kv_cache,
-                                int num_pages, int page_size, const int32_t* topk, int topk_stride,
-                                int topk_width, const int32_t* topk_lens,
-                                const int32_t* query_start_loc, const int32_t* seq_lens,
-                                const int32_t* block_table, int block_table_stride, int B,
-                                int top_k, int window, const float* sinks, float softmax_scale,
-                                void* out, float* lse, int T, int H, void* stream) {
-  const char* fn = "dsv4_sparse_mla_decode_step";
+static int decode_step_checked(const char* fn, void* q, const void* kv, const int64_t* positions,
+                               const int64_t* slot_mapping, const float* cos_sin, int max_pos,
+                               const void* q_norm_weight, float eps, uint8_t* kv_cache,
+                               int num_pages, int page_size, const int32_t* topk, int topk_stride,
+                               int topk_width, const int32_t* topk_lens,
+                               const int32_t* query_start_loc, const int32_t* seq_lens,
+                               const int32_t* block_table, int block_table_stride, int B,
+                               int top_k, int window, const float* sinks, float softmax_scale,
+                               void* out, float* lse, int T, int H, int splits, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   if (T < 0 || B < 0 || top_k < 0 || window < 0 || topk_width < 0 || topk_stride < topk_width ||
       block_table_stride < 0 || max_pos < 0)
     return fail(DSV4_ERR_SHAPE, "%s: negative size or topk_stride < topk_width", fn);
@@ -336,6 +336,8 @@ int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* position
   if (top_k > topk_width) return fail(DSV4_ERR_SHAPE, "%s: top_k %d > topk_width %d", fn, top_k, topk_width);
   if ((int64_t)top_k + window > 4096)
     return fail(DSV4_ERR_UNSUPPORTED, "%s: top_k + window = %lld > 4096", fn, (long long)top_k + window);
+  if (splits < 1 || splits > 64)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: splits %d not in 1..64", fn, splits);
   if (!(softmax_scale == softmax_scale)) return fail(DSV4_ERR_SHAPE, "%s: softmax_scale is NaN", fn);
   if (!(eps >= 0.f)) return fail(DSV4_ERR_SHAPE, "%s: eps must be >= 0", fn);
   if (T == 0) return ok();
@@ -349,14 +351,52 @@ int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* position
   if (!aligned(positions, 8) || !aligned(slot_mapping, 8) || (topk && !aligned(topk, 4)) ||
       !aligned(query_start_loc, 4) || !aligned(seq_lens, 4))
     return fail(DSV4_ERR_ALIGN, "%s: positions, slot_mapping 8-byte aligned; int32 arrays 4-byte", fn);
+  if (splits > 1) {
+    const size_t need = dsv4::split_workspace_bytes(T, H, splits);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+      return fail(DSV4_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) needed, got %zu",
+                  fn, need, workspace ? workspace_bytes : (size_t)0);
+  }
   return hip_status(dsv4::launch_attention_step(q, kv, positions, slot_mapping, cos_sin, max_pos,
                                                 q_norm_weight, eps, kv_cache, num_pages,
                                                 dsv4::page_shift_of(page_size), topk, topk_stride,
                                                 topk_width, topk_lens, query_start_loc, seq_lens,
                                                 block_table, block_table_stride, B, top_k, window,
-                                                sinks, softmax_scale, out, lse, T, H,
-                                                static_cast<hipStream_t>(stream)),
+                                                sinks, softmax_scale, out, lse, T, H, splits,
+                                                workspace, static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* positions,
+                                const int64_t* slot_mapping, const float* cos_sin, int max_pos,
+                                const void* q_norm_weight, float eps, uint8_t* kv_cache,
+                                int num_pages, int page_size, const int32_t* topk, int topk_stride,
+                                int topk_width, const int32_t* topk_lens,
+                                const int32_t* query_start_loc, const int32_t* seq_lens,
+                                const int32_t* block_table, int block_table_stride, int B,
+                                int top_k, int window, const float* sinks, float softmax_scale,
+                                void* out, float* lse, int T, int H, void* stream) {
+  return decode_step_checked("dsv4_sparse_mla_decode_step", q, kv, positions, slot_mapping,
+                             cos_sin, max_pos, q_norm_weight, eps, kv_cache, num_pages, page_size,
+                             topk, topk_stride, topk_width, topk_lens, query_start_loc, seq_lens,
+                             block_table, block_table_stride, B, top_k, window, sinks,
+                             softmax_scale, out, lse, T, H, 1, nullptr, 0, stream);
+}
+
+int dsv4_sparse_mla_decode_step_split(
+    void* q, const void* kv, const int64_t* positions, const int64_t* slot_mapping,
+    const float* cos_sin, int max_pos, const void* q_norm_weight, float eps, uint8_t* kv_cache,
+    int num_pages, int page_size, const int32_t* topk, int topk_stride, int topk_width,
+    const int32_t* topk_lens, const int32_t* query_start_loc, const int32_t* seq_lens,
+    const int32_t* block_table, int block_table_stride, int B, int top_k, int window,
+    const float* sinks, float softmax_scale, void* out, float* lse, int T, int H, int splits,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_step_checked("dsv4_sparse_mla_decode_step_split", q, kv, positions, slot_mapping,
+                             cos_sin, max_pos, q_norm_weight, eps, kv_cache, num_pages, page_size,
+                             topk, topk_stride, topk_width, topk_lens, query_start_loc, seq_lens,
+                             block_table, block_table_stride, B, top_k, window, sinks,
+                             softmax_scale, out, lse, T, H, splits, workspace, workspace_bytes,
+                             stream);
 }
 
 int dsv4_sparse_mla_prefill(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,

@@ -797,6 +797,23 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     end = min(max(__builtin_amdgcn_readfirstlane(n_lens_v), 0), lim);
   }
   __syncthreads();  // (STEP: also the q rows in LDS and this workgroup's cache rows written)
+  if constexpr (FUSED) {
+    if (splits > 1) {
+      // piece sp of the built row, [sp * split_len, +split_len), moves to the start of
+      // the index block (every entry read before any is written)
+      const int pb = min(sp * split_len, end);
+      const int pn = min(split_len, end - pb);
+      int32_t pv[kCombPer];
+#pragma unroll
+      for (int u = 0; u < kCombPer; ++u) pv[u] = sm.idx[min(pb + tid + 256 * u, kIdxBlock - 1)];
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kCombPer; ++u)
+        if (tid + 256 * u < pn) sm.idx[tid + 256 * u] = pv[u];
+      __syncthreads();
+      end = pn;
+    }
+  }
   if constexpr (STEP) {
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
@@ -1006,16 +1023,33 @@ hipError_t launch_attention_step(void* q, const void* kv, const int64_t* positio
                                  const int32_t* qsl, const int32_t* seq_lens,
                                  const int32_t* block_table, int bt_stride, int B, int top_k,
                                  int window, const float* sinks, float softmax_scale, void* out,
-                                 float* lse, int T, int H, hipStream_t stream) {
+                                 float* lse, int T, int H, int splits, void* workspace,
+                                 hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const TopkIn tin{topk, topk_stride, topk_width, topk_lens, qsl, seq_lens, block_table,
                    bt_stride, B, top_k, window};
   const StepIn sti{static_cast<uint16_t*>(q), static_cast<const uint16_t*>(kv), positions,
                    slot_mapping, cos_sin, max_pos, static_cast<const uint16_t*>(q_norm_weight),
                    eps, cache};
-  return launch_items<true, true>(nullptr, nullptr, num_pages, page_shift, nullptr, 0, nullptr,
-                                  sinks, softmax_scale, out, lse, T, H, 1, kIdxBlock, nullptr,
-                                  nullptr, tin, sti, stream);
+  if (splits <= 1)
+    return launch_items<true, true>(nullptr, nullptr, num_pages, page_shift, nullptr, 0, nullptr,
+                                    sinks, softmax_scale, out, lse, T, H, 1, kIdxBlock, nullptr,
+                                    nullptr, tin, sti, stream);
+  // pieces of the row as the split decode cuts a combined row of width
+  // round_up(top_k + window, 128): 64-entry-aligned, trailing pieces may be empty
+  const int width = (top_k + window + 127) / 128 * 128;
+  const int per = (width + splits - 1) / splits;
+  const int split_len = per > 0 ? ((per + kChunk - 1) / kChunk) * kChunk : kChunk;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_ml = part_o + (size_t)T * splits * H * kNope;
+  hipError_t e = launch_items<true, true>(nullptr, nullptr, num_pages, page_shift, nullptr, 0,
+                                          nullptr, sinks, softmax_scale, out, lse, T, H, splits,
+                                          split_len, part_o, part_ml, tin, sti, stream);
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)T * H;
+  hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                     part_o, part_ml, sinks, static_cast<uint16_t*>(out), lse, T, H, splits);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, int page_shift,

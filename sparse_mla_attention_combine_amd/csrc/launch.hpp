@@ -71,7 +71,9 @@ hipError_t launch_attention_topk(const void* q, const uint8_t* cache, int num_pa
                                  float softmax_scale, void* out, float* lse, int T, int H,
                                  hipStream_t stream);
 
-// The insert step and the fused combine + decode in one launch (see sparse_mla_kernel).
+// The insert step and the fused combine + decode in one launch (see sparse_mla_kernel);
+// with splits > 1 each row is cut into pieces merged by their lse (workspace as for
+// launch_attention_split).
 hipError_t launch_attention_step(void* q, const void* kv, const int64_t* positions,
                                  const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                                  const void* q_norm_weight, float eps, uint8_t* cache,
@@ -80,6 +82,7 @@ hipError_t launch_attention_step(void* q, const void* kv, const int64_t* positio
                                  const int32_t* qsl, const int32_t* seq_lens,
                                  const int32_t* block_table, int bt_stride, int B, int top_k,
                                  int window, const float* sinks, float softmax_scale, void* out,
-                                 float* lse, int T, int H, hipStream_t stream);
+                                 float* lse, int T, int H, int splits, void* workspace,
+                                 hipStream_t stream);
 
 }  // namespace dsv4

@@ -221,6 +221,28 @@ def test_decode_step_validation(dsv4):
     assert call(T=0) == 0
 
 
+def test_decode_step_split_validation(dsv4):
+    lib = dsv4.library()
+    keep, p = _fake()
+    need = lib.dsv4_sparse_mla_split_workspace_bytes(2, 128, 4)
+
+    def call(**kw):
+        a = dict(S=4, ws=p, wsb=need, T=2, H=128, window=128, P=64)
+        a.update(kw)
+        return lib.dsv4_sparse_mla_decode_step_split(
+            p, p, p, p, p, 100, p, 1e-6, p, 4, a["P"], p, 2048, 2048, None, p, p, p, 8, 2, 2048,
+            a["window"], None, 0.04, p, None, a["T"], a["H"], a["S"], a["ws"], a["wsb"], None)
+
+    assert call(S=0) == 4 and call(S=65) == 4
+    assert call(wsb=need - 1) == 5
+    assert call(ws=None) == 5
+    assert call(ws=ctypes.c_void_p(p.value + 8)) == 5
+    assert call(window=2049) == 4
+    assert call(H=24) == 4
+    assert call(P=48) == 4
+    assert call(T=0) == 0
+
+
 def test_insert_and_gather_validation(dsv4):
     lib = dsv4.library()
     keep, p = _fake()

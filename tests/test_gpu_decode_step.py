@@ -246,3 +246,45 @@ def test_decode_step_longest_row(dsv4):
     # rows of tokens of no request are empty in the fused forms; compare the request rows
     nreq = int(h["qsl"][-1] - h["qsl"][0])
     assert _same(ob[:nreq], o3[:nreq]) and _same(lb[:nreq], l3[:nreq])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_step_split_equals_insert_combine_split(dsv4, seed):
+    """The split form of the one-launch step against insert, combine (rows of width
+    round_up(top_k + window, 128)) and the split decode with the same number of pieces:
+    out and lse bit for bit; q and the cache bytes as the unsplit step leaves them."""
+    rng = np.random.default_rng(3200 + seed)
+    P = [64, 32, 256][seed % 3]
+    H = [128, 16, 64][seed % 3]
+    splits = [2, 3, 8][seed % 3]
+    c, q0, cache0, h = _random_case(rng, P, H, [1, 5][seed % 2])
+    T = c["T"]
+    W = (c["top_k"] + c["window"] + 127) // 128 * 128
+    log(f"decode_step split seed={seed} P={P} H={H} T={T} top_k={c['top_k']} "
+        f"window={c['window']} splits={splits}")
+    ws = torch.empty(dsv4.split_workspace_bytes(T, H, splits), dtype=torch.uint8, device="cuda")
+    # reference chain
+    q3, c3 = q0.clone(), cache0.clone()
+    dsv4.dsv4_kv_insert(q3, c["kv"], c["pos"], c["slots"], c["cos_sin"], c["w"], 1e-6, c3,
+                        page_size=P)
+    comb = torch.full((T, W), -1, dtype=torch.int32, device="cuda")
+    lens = torch.zeros(T, dtype=torch.int32, device="cuda")
+    dsv4.dsv4_combine_indices(c["topk"], c["tl"], c["qsl"], c["sl"], c["bt"], c["top_k"],
+                              c["window"], comb, lens, page_size=P)
+    o3 = torch.empty(T, H, 512, dtype=torch.bfloat16, device="cuda")
+    l3 = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    dsv4.dsv4_sparse_mla_decode_split(q3, c3, comb, lens, c["sinks"], c["scale"], o3, splits, ws,
+                                      lse=l3, page_size=P)
+    torch.cuda.synchronize()
+    o3, l3 = o3.clone(), l3.clone()
+    # the split step
+    q, cache = q0.clone(), cache0.clone()
+    out = torch.full((T, H, 512), 3.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, H), 3.0, dtype=torch.float32, device="cuda")
+    dsv4.dsv4_sparse_mla_decode_step(q, c["kv"], c["pos"], c["slots"], c["cos_sin"], c["w"], 1e-6,
+                                     cache, c["topk"], c["tl"], c["qsl"], c["sl"], c["bt"],
+                                     c["top_k"], c["window"], c["sinks"], c["scale"], out, lse,
+                                     page_size=P, splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    assert _same(q, q3) and torch.equal(cache, c3)
+    assert _same(out, o3) and _same(lse, l3)
