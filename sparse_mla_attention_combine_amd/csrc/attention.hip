@@ -820,6 +820,15 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
       load_q_frags(st.qf[hb], reinterpret_cast<const uint16_t*>(&sm.v[1][0][0]) +
                                   (16 * hb + l16) * kLatent, g);
   }
+  if constexpr (NHB == 2 && STEP) {
+    // The step's prologue leaves more values live than the other variants, and the
+    // register allocator would otherwise spill the second head block's Q fragments to
+    // AGPRs and copy each one back into VGPRs before every use (72 copies per chunk).
+    // Placing them in AGPRs from the start lets the MFMAs read them there directly (an
+    // MFMA accepts AGPR A/B operands); the empty asm only fixes the register class.
+#pragma unroll
+    for (int k = 0; k < 18; ++k) asm volatile("" : "+a"(st.qf[1][k]));
+  }
   const int row = 16 * w + l16;
   const CacheRef cr{STEP ? sti.cache : cache, num_slots, ps};
   for (int blk0 = beg; blk0 < end; blk0 += kIdxBlock) {
