@@ -133,17 +133,21 @@ __device__ __forceinline__ int64_t idx_at(const int32_t* idx_lds, int jj, int n_
   return jj < n_blk ? (int64_t)v : -1;
 }
 
-// Copies entries [0, n_win) of an index block into LDS with every load in flight before
-// the first wait: one memory latency per block instead of one per 256 entries.
-__device__ __forceinline__ void stage_idx(int32_t* dst, const int32_t* __restrict__ src, int n_win,
-                                          int tid) {
-  constexpr int kPer = kIdxBlock / 256;
-  int32_t v[kPer];
+// Entries [0, n_win) of an index block, this thread's share, all requested before the
+// first wait (one memory latency per block instead of one per 256 entries); then written
+// into LDS.  In two parts so that other loads can be issued in between.
+constexpr int kStagePer = kIdxBlock / 256;
+__device__ __forceinline__ void stage_idx_load(int32_t (&v)[kStagePer],
+                                               const int32_t* __restrict__ src, int n_win,
+                                               int tid) {
 #pragma unroll
-  for (int k = 0; k < kPer; ++k)
+  for (int k = 0; k < kStagePer; ++k)
     if (256 * k < n_win) v[k] = src[min(tid + 256 * k, n_win - 1)];
+}
+__device__ __forceinline__ void stage_idx_store(int32_t* dst, const int32_t (&v)[kStagePer],
+                                                int n_win, int tid) {
 #pragma unroll
-  for (int k = 0; k < kPer; ++k)
+  for (int k = 0; k < kStagePer; ++k)
     if (tid + 256 * k < n_win) dst[tid + 256 * k] = v[k];
 }
 
@@ -612,6 +616,8 @@ __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnSt
 }
 
 static_assert(32 * kLatent <= kChunk * kVStride, "32 q rows fit one value-tile buffer");
+static_assert(32 * (kNope + 8) <= kChunk * kVStride, "32 staged output rows fit one value-tile buffer");
+static_assert(32 * (kNope + 4) * 4 <= 2 * kChunk * kVStride * 2, "32 staged fp32 partial rows fit both value-tile buffers");
 
 // Q^T fragments of one block of 16 heads from q row `qr` (global memory or LDS): lane
 // (head l16, k-group g); k-step s pairs with the K-fragment dims chosen in load_raw
@@ -708,15 +714,19 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     kvv = kv_lane_load(sti.kv + t1 * kLatent, lane);
     kvp = sti.positions[t1];
     kvs = sti.slot_mapping[t1];
-  } else {
-    // Q^T fragments: lane (head l16 of block hb, k-group g); k-step s pairs with the
-    // K-fragment dims chosen in load_raw (nope: 64u+16g+8h, rope: 32r+8g).
+  }
+  // Q^T fragments from memory (all but STEP): lane (head l16 of block hb, k-group g);
+  // k-step s pairs with the K-fragment dims chosen in load_raw (nope: 64u+16g+8h, rope:
+  // 32r+8g).  Requested after the loads that build the index row: vector-memory loads
+  // complete in order, so a wait for the row would otherwise also wait for all of Q
+  // (144 registers a lane), and the first gathers would leave later.
+  auto load_q_global = [&]() {
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       const uint16_t* qr = q + ((int64_t)t * H + h0 + 16 * hb + l16) * kLatent;
       load_q_frags(st.qf[hb], qr, g);
     }
-  }
+  };
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     st.m_run[hb] = kMFloor;
@@ -732,11 +742,12 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   // Index blocks of up to 4096 entries are staged in LDS.  Inside a block chunk c lives
   // in register buffer c&1 and LDS tiles c&1; a buffer is refilled with chunk c+2 as
   // soon as staging has consumed it, so two chunks of records are always in flight.
-  // Rows from memory: the first block is requested together with Q and the row length
-  // (entries past the length are staged but never used), so the prologue waits for
-  // memory only once.  Rows built here: the top-k row and the request lookup take one
-  // round of loads, the block-table lookups a second (FUSED; STEP adds its insert work
-  // to those two rounds).
+  // Rows from memory: the first block is requested together with the row length and
+  // then Q (entries past the length are staged but never used), so the prologue waits
+  // for memory only once, and only for the row.  Rows built here: the top-k row and the
+  // request lookup take one round of loads, the block-table lookups a second, and Q is
+  // requested after them (FUSED; STEP adds its insert work to those two rounds and reads
+  // Q from LDS).
   int end;
   if constexpr (STEP) {
     int32_t xv[kCombPer];
@@ -792,8 +803,13 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     }
   } else if constexpr (FUSED) {
     end = stage_combined<NHB>(sm, tin, t, ps, tid);
+    load_q_global();
   } else {
-    stage_idx(sm.idx, idx_row + beg, min(lim - beg, kIdxBlock), tid);
+    int32_t iv[kStagePer];
+    const int n_win = min(lim - beg, kIdxBlock);
+    stage_idx_load(iv, idx_row + beg, n_win, tid);
+    load_q_global();
+    stage_idx_store(sm.idx, iv, n_win, tid);
     end = min(max(__builtin_amdgcn_readfirstlane(n_lens_v), 0), lim);
   }
   __syncthreads();  // (STEP: also the q rows in LDS and this workgroup's cache rows written)
@@ -890,16 +906,31 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     // denominator go to the workspace; the merge pass adds the sink and normalises
     float* po = part_o + ((int64_t)vt * H + h) * kNope;
     if constexpr (NHB == 2) {
+      // staged through LDS (both value tiles, free after the barrier above; rows padded
+      // by 16 B) so that each store instruction writes 1 KB of one row instead of 64
+      // separate 16-byte pieces
       const int hi = lane >> 5;
+      float* const ot = reinterpret_cast<float*>(&sm.v[0][0][0]);
+      constexpr int kOStride = kNope + 4;  // fp32 per staged partial row
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const f32x16& o = st.o32[mb];
-          *reinterpret_cast<float4*>(po + 128 * mb + 32 * w + 8 * qd + 4 * hi) =
+          *reinterpret_cast<float4*>(ot + hl * kOStride + 128 * mb + 32 * w + 8 * qd + 4 * hi) =
               make_float4(o[4 * qd], o[4 * qd + 1], o[4 * qd + 2], o[4 * qd + 3]);
         }
       if (w == 0 && hi == 0) *reinterpret_cast<float2*>(part_ml + ((int64_t)vt * H + h) * 2) = make_float2(mr, lt);
+      __syncthreads();
+      float* const pb = part_o + ((int64_t)vt * H + h0) * kNope;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int hr = 8 * w + r;
+          *reinterpret_cast<float4*>(pb + (int64_t)hr * kNope + 256 * half + 4 * lane) =
+              *reinterpret_cast<const float4*>(ot + hr * kOStride + 256 * half + 4 * lane);
+        }
     } else {
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
@@ -917,18 +948,33 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   const float inv = den > 0.f ? f / den : 0.f;
   uint16_t* orow = out + ((int64_t)t * H + h) * kNope;
   if constexpr (NHB == 2) {
+    // A lane holds 4 consecutive output dims of one head per register group, so direct
+    // stores would write 8-byte pieces, 64 rows per instruction.  The normalised rows go
+    // through LDS instead (the first value tile is free after the barrier above; rows
+    // padded by 16 B so that the heads of a write spread over the banks) and leave as
+    // whole 1 KB rows, one per store instruction.
     const int hi = lane >> 5;
+    __bf16* const ot = &sm.v[0][0][0];
+    constexpr int kOStride = kNope + 8;  // bf16 per staged output row
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         const f32x16& o = st.o32[mb];
-        *reinterpret_cast<uint2*>(orow + 128 * mb + 32 * w + 8 * qd + 4 * hi) =
+        *reinterpret_cast<uint2*>(ot + hl * kOStride + 128 * mb + 32 * w + 8 * qd + 4 * hi) =
             make_uint2(pack_bf16x2(o[4 * qd] * inv, o[4 * qd + 1] * inv),
                        pack_bf16x2(o[4 * qd + 2] * inv, o[4 * qd + 3] * inv));
       }
     if (lse && w == 0 && hi == 0)
       lse[(int64_t)t * H + h] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    __syncthreads();
+    uint16_t* const ob = out + ((int64_t)t * H + h0) * kNope;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int hr = 8 * w + r;
+      *reinterpret_cast<uint4*>(ob + (int64_t)hr * kNope + 8 * lane) =
+          *reinterpret_cast<const uint4*>(ot + hr * kOStride + 8 * lane);
+    }
   } else {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
