@@ -889,6 +889,12 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     }
   }
 
+  {  // the thread's indices are recomputed from an opaque copy of the thread id: shared
+     // with the prologue, their address terms would stay live across the chunk loop
+     // and be spilled
+  int tid_e = threadIdx.x;
+  asm volatile("" : "+v"(tid_e));
+  const int lane = tid_e & 63, w = tid_e >> 6, l16 = lane & 15, g = lane >> 4;
   // ---- finalise: sum the waves' partial denominators, add the sink, normalise
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
@@ -984,6 +990,7 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     }
     if (lse && w == 0 && g == 0)
       lse[(int64_t)t * H + h] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+  }
   }
 }
 
