@@ -58,6 +58,29 @@ struct SelSmem {
   uint32_t sh_digit, sh_above;
 };
 
+// One histogram pass that reads the keys from memory (keeping them in LDS if `staged`):
+// ITEMS keys per thread are requested before any is used, at clamped indices (a load
+// under a per-lane condition is waited for on the spot); entries past n are ignored.
+// Each round of ITEMS loads costs one memory latency, so a staged row goes in one round.
+template <int ITEMS, int NT, bool STAGE, typename KeyAt>
+__device__ __forceinline__ void hist_from_memory(SelSmem<NT, STAGE>& sm, int n, int tid,
+                                                 bool staged, uint32_t mask, uint32_t prefix,
+                                                 int shift, uint32_t dmask, KeyAt key_at) {
+  for (int j0 = 0; j0 < n; j0 += NT * ITEMS) {
+    uint32_t v[ITEMS];
+#pragma unroll
+    for (int u = 0; u < ITEMS; ++u) v[u] = key_at(min(j0 + u * NT + tid, n - 1));
+#pragma unroll
+    for (int u = 0; u < ITEMS; ++u) {
+      const int j = j0 + u * NT + tid;
+      if (j < n) {
+        if (staged) sm.keys[j] = v[u];
+        if ((v[u] & mask) == prefix) atomicAdd(&sm.hist[(v[u] >> shift) & dmask], 1u);
+      }
+    }
+  }
+}
+
 // The k largest of n keys (0 < k < n), ties to the smaller index j: a radix select of the
 // k-th largest key K (digits of 11, 11 and 10 bits, most significant first) and how many
 // keys equal to K are taken (m), then one ordered pass that calls emit(p, j, key) for
@@ -85,21 +108,14 @@ __device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm, int n, int 
         if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & dmask], 1u);
       }
     } else {
-      // eight keys per thread requested at a time, at clamped indices (a load under a
-      // per-lane condition is waited for on the spot); entries past n are ignored
-      for (int j0 = 0; j0 < n; j0 += NT * kSelItems) {
-        uint32_t v[kSelItems];
-#pragma unroll
-        for (int u = 0; u < kSelItems; ++u) v[u] = key_at(min(j0 + u * NT + tid, n - 1));
-#pragma unroll
-        for (int u = 0; u < kSelItems; ++u) {
-          const int j = j0 + u * NT + tid;
-          if (j < n) {
-            if (staged) sm.keys[j] = v[u];
-            if ((v[u] & mask) == prefix) atomicAdd(&sm.hist[(v[u] >> shift) & dmask], 1u);
-          }
+      bool done = false;
+      if constexpr (STAGE) {
+        if (staged && n > NT * kSelItems) {  // a long staged row: twice the keys per round
+          hist_from_memory<2 * kSelItems>(sm, n, tid, true, mask, prefix, shift, dmask, key_at);
+          done = true;
         }
       }
+      if (!done) hist_from_memory<kSelItems>(sm, n, tid, staged, mask, prefix, shift, dmask, key_at);
     }
     __syncthreads();
     // thread i owns the kBins/NT digits below dmask - (kBins/NT)*i (from the top); after
