@@ -1024,19 +1024,44 @@ __global__ void __launch_bounds__(256) split_merge_kernel(
   if (row >= (int64_t)T * H) return;
   const int t = (int)(row / H), h = (int)(row - (int64_t)t * H);
   const float z2 = sinks ? sinks[h] * kLog2e : -INFINITY;
-  float M = z2;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(((int64_t)t * splits + s) * H + h) * 2]);
-  float den = (z2 == -INFINITY) ? 0.f : exp2f(z2 - M);
+  // Up to 8 partials per round, every load of a round issued before the first is used
+  // (at clamped indices): one memory round trip per 8 pieces instead of two per piece.
+  // A later round rescales what the earlier ones summed (only with more than 8 pieces;
+  // with at most 8 the arithmetic is the definition's, in its order).
+  constexpr int kRound = 8;
+  float M = z2, den = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) {
-    const int64_t pr = ((int64_t)t * splits + s) * H + h;
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + pr * 2);
-    const float wgt = exp2f(ml.x - M);
-    den += ml.y * wgt;
-    const float4 a = *reinterpret_cast<const float4*>(part_o + pr * kNope + 8 * lane);
-    const float4 b = *reinterpret_cast<const float4*>(part_o + pr * kNope + 8 * lane + 4);
-    acc[0] += a.x * wgt; acc[1] += a.y * wgt; acc[2] += a.z * wgt; acc[3] += a.w * wgt;
-    acc[4] += b.x * wgt; acc[5] += b.y * wgt; acc[6] += b.z * wgt; acc[7] += b.w * wgt;
+  for (int s0 = 0; s0 < splits; s0 += kRound) {
+    float2 ml[kRound];
+    float4 a[kRound], b[kRound];
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      const int64_t pr = ((int64_t)t * splits + min(s0 + j, splits - 1)) * H + h;
+      ml[j] = *reinterpret_cast<const float2*>(part_ml + pr * 2);
+      a[j] = *reinterpret_cast<const float4*>(part_o + pr * kNope + 8 * lane);
+      b[j] = *reinterpret_cast<const float4*>(part_o + pr * kNope + 8 * lane + 4);
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kRound; ++j)
+      if (s0 + j < splits) mb = fmaxf(mb, ml[j].x);
+    if (s0 == 0) {
+      den = (z2 == -INFINITY) ? 0.f : exp2f(z2 - mb);
+    } else {
+      const float c = exp2f(M - mb);
+      den *= c;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= c;
+    }
+    M = mb;
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      if (s0 + j >= splits) break;
+      const float wgt = exp2f(ml[j].x - M);
+      den += ml[j].y * wgt;
+      acc[0] += a[j].x * wgt; acc[1] += a[j].y * wgt; acc[2] += a[j].z * wgt; acc[3] += a[j].w * wgt;
+      acc[4] += b[j].x * wgt; acc[5] += b[j].y * wgt; acc[6] += b[j].z * wgt; acc[7] += b[j].w * wgt;
+    }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   uint4 v;
