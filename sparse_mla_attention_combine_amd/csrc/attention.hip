@@ -30,7 +30,12 @@
 //   4. O^T += V^T P^T on bf16 MFMA 32x32x16: wave w owns output dims 128mb + 32w (mb =
 //      0..3) for all NH heads; V^T fragments come from the row-major LDS tile through
 //      gfx950's transposing LDS read (ds_read_b64_tr_b16), P^T fragments are plain 16 B
-//      reads; these MFMAs are issued after the softmax and run across the barrier.
+//      reads; these MFMAs are scheduled between the softmax operations of the next
+//      chunk (one MFMA, then up to eight VALU operations), so the matrix core works
+//      while the in-order wave issues the softmax.
+// The output rows leave through LDS as whole rows (a lane's accumulators hold 4
+// consecutive dims of one head), and the thread's indices in the epilogue come from an
+// opaque copy of the thread id so that nothing stays live, or spilled, across the loop.
 // Numerics: bf16 operands, fp32 accumulation and softmax, P rounded to bf16 for P.V;
 // the per-head sink enters only the final denominator.
 // Variants of one kernel: the index rows come from memory (decode, prefill, and pieces of
