@@ -696,6 +696,11 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     vt = (k / groups) * 8 + x;
   }
   if (vt >= T * splits) return;
+  // Work items in reverse order: in a launch of many rounds (prefill) the longest rows,
+  // which come last in a causal sequence, then start first and the last round is short
+  // (longest processing time first).  The head groups of a token keep their common
+  // block id mod 8, so they still share an XCD.
+  vt = T * splits - 1 - vt;
   const int t = vt / splits, sp = vt - t * splits;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
