@@ -211,7 +211,7 @@ def main():
                P(d["lens"].data_ptr()), P(d["sinks"].data_ptr()),
                ctypes.c_float(wl["softmax_scale"]), P(d["out"].data_ptr()), None, T, H)
         dec = dec + ((splits, P(workspace.data_ptr()), ctypes.c_size_t(ws_bytes), sp) if splits > 1
-                     else (sp,))
+                     else (None, ctypes.c_size_t(0), sp))
         fused = (P(d["q"].data_ptr()), P(cache.data_ptr()), npg, PS, P(d["topk"].data_ptr()),
                  d["topk"].shape[1], d["topk"].shape[1], P(d["topk_lens"].data_ptr()),
                  P(qsl.data_ptr()), P(seq_lens.data_ptr()), P(bt.data_ptr()), bt.shape[1], wl["B"],

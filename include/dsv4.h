@@ -245,11 +245,34 @@ int dsv4_gather_workspace(const uint8_t* comp_cache, int comp_num_pages,
  * Arithmetic: bf16 operands, fp32 accumulation, probabilities rounded to bf16 for the
  * value product.  Supported: H in {16, 32, 64, 128}, page_size in {32, 64, 256}.
  * Alignment: q, out, kv_cache 16-byte aligned; indices 4-byte aligned.
+ *
+ * Workspace [p2 Review highlights: no allocation on the decode path, so scratch memory
+ * is the caller's]: `workspace` may be NULL with workspace_bytes 0, and the call then
+ * runs one workgroup per (token, head group).  Given at least
+ * dsv4_sparse_mla_workspace_bytes(T, H, idx_stride, 0) bytes (16-byte aligned), a batch
+ * too small to fill the GPU has its rows cut into pieces merged by their log-sum-exp, as
+ * dsv4_sparse_mla_decode_split does with the piece count that function reports; the
+ * result is the same up to rounding order.  The workspace carries nothing between calls;
+ * calls sharing one workspace on different streams race.  A non-NULL workspace that is
+ * misaligned or smaller than that size, or a NULL one with workspace_bytes != 0, is
+ * DSV4_ERR_WORKSPACE.
  */
 int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages,
                            int page_size, const int32_t* indices, int idx_stride,
                            const int32_t* lens, const float* sinks, float softmax_scale,
-                           void* out, float* lse, int T, int H, void* stream);
+                           void* out, float* lse, int T, int H, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * dsv4_sparse_mla_workspace_bytes — device workspace bytes that dsv4_sparse_mla_decode
+ * (is_prefill 0) or dsv4_sparse_mla_prefill (is_prefill 1) may use for T query tokens,
+ * H heads and index rows of `width` entries (idx_stride).  0 when the call's schedule
+ * needs none: a decode batch that fills the GPU (T * H / 32 >= 160 workgroups) and every
+ * prefill.  Otherwise the split workspace of the piece count the decode picks
+ * (min(8, 256 / (T * max(1, H / 32))), lowered until every piece holds >= 256 entries).
+ * Returns 0 for T < 0, width < 0 or an unsupported H.
+ */
+size_t dsv4_sparse_mla_workspace_bytes(int T, int H, int width, int is_prefill);
 
 /*
  * dsv4_sparse_mla_decode_topk — dsv4_combine_indices followed by dsv4_sparse_mla_decode
@@ -287,8 +310,9 @@ int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_
  * positions agree with the block tables and the positions the combine derives from
  * query_start_loc and seq_lens, as in a decode step.  The inserted rows of a request are
  * quantised by every workgroup of each of its tokens (a request of n new tokens does
- * O(n^2) row insertions): meant for decode batches of a few tokens per request; long
- * prefills use the two entry points.  Requires what both entry points require.
+ * O(n^2) row insertions): meant for decode batches of a few tokens per request (MTP);
+ * prefill-sized requests use the two entry points, and T > 64 * max(B, 1) is refused
+ * with DSV4_ERR_UNSUPPORTED.  Requires what both entry points require.
  */
 int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* positions,
                                 const int64_t* slot_mapping, const float* cos_sin, int max_pos,
@@ -308,7 +332,10 @@ int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* position
  * dsv4_sparse_mla_decode_split cuts from a combined row of width
  * round_up(top_k + window, 128), so out and lse equal dsv4_kv_insert +
  * dsv4_combine_indices (combined_stride = that width) + dsv4_sparse_mla_decode_split with
- * the same splits; q and the cache bytes equal dsv4_sparse_mla_decode_step's.
+ * the same splits; q and the cache bytes equal dsv4_sparse_mla_decode_step's.  Every
+ * piece reads the raw q rows; the merge launch, enqueued after all pieces, writes the
+ * normalised rows back in place (a piece never writes q, since the pieces of one row
+ * run at different times and a later one would otherwise read a normalised row).
  *   splits     1..64 (1: dsv4_sparse_mla_decode_step, no workspace)
  *   workspace  caller-owned device memory of at least
  *              dsv4_sparse_mla_split_workspace_bytes(T, H, splits) bytes, 16-byte
@@ -328,12 +355,15 @@ int dsv4_sparse_mla_decode_step_split(
  * dsv4_sparse_mla_prefill — the same result as dsv4_sparse_mla_decode, scheduled for
  * many query tokens per call (prefill: each token of a long sequence attends its own
  * combined index row) [p3 Motivation/Implementation breakdown: sparse prefill index
- * combining; p4 decoder self-attention].  Same arguments, contract and limits.
+ * combining; p4 decoder self-attention].  Same arguments, contract and limits; its
+ * schedule needs no workspace (dsv4_sparse_mla_workspace_bytes(T, H, width, 1) == 0),
+ * so NULL / 0 is the usual argument.
  */
 int dsv4_sparse_mla_prefill(const void* q, const uint8_t* kv_cache, int num_pages,
                             int page_size, const int32_t* indices, int idx_stride,
                             const int32_t* lens, const float* sinks, float softmax_scale,
-                            void* out, float* lse, int T, int H, void* stream);
+                            void* out, float* lse, int T, int H, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * dsv4_sparse_mla_split_workspace_bytes — bytes of device workspace that

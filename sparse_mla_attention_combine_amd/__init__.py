@@ -33,13 +33,15 @@ _lib.dsv4_kv_insert.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _vp, _
                                 _i32, _vp]
 _lib.dsv4_combine_indices.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _vp, _i32, _vp, _vp]
-_attn_args = [_vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _vp]
-_lib.dsv4_sparse_mla_decode.argtypes = _attn_args
-_lib.dsv4_sparse_mla_prefill.argtypes = _attn_args
+_attn_head = [_vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _i32, _i32]
+_lib.dsv4_sparse_mla_decode.argtypes = _attn_head + [_vp, ctypes.c_size_t, _vp]
+_lib.dsv4_sparse_mla_prefill.argtypes = _attn_head + [_vp, ctypes.c_size_t, _vp]
+_lib.dsv4_sparse_mla_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+_lib.dsv4_sparse_mla_workspace_bytes.restype = ctypes.c_size_t
 _lib.dsv4_gather_dequant.argtypes = [_vp, _i32, _i32, _vp, _i32, _vp, _vp]
 _lib.dsv4_sparse_mla_split_workspace_bytes.argtypes = [_i32, _i32, _i32]
 _lib.dsv4_sparse_mla_split_workspace_bytes.restype = ctypes.c_size_t
-_lib.dsv4_sparse_mla_decode_split.argtypes = _attn_args[:-1] + [_i32, _vp, ctypes.c_size_t, _vp]
+_lib.dsv4_sparse_mla_decode_split.argtypes = _attn_head + [_i32, _vp, ctypes.c_size_t, _vp]
 _lib.dsv4_combine_indices_compressed.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]
 _lib.dsv4_sparse_mla_decode_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp,
@@ -65,7 +67,8 @@ EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4
             "dsv4_gather_dequant", "dsv4_sparse_mla_split_workspace_bytes",
             "dsv4_sparse_mla_decode_split", "dsv4_combine_indices_compressed",
             "dsv4_gather_workspace", "dsv4_indexer_topk", "dsv4_sparse_mla_decode_topk",
-            "dsv4_sparse_mla_decode_step", "dsv4_sparse_mla_decode_step_split"]
+            "dsv4_sparse_mla_decode_step", "dsv4_sparse_mla_decode_step_split",
+            "dsv4_sparse_mla_workspace_bytes"]
 
 
 class Dsv4Error(RuntimeError):
@@ -200,7 +203,12 @@ def dsv4_gather_workspace(comp_cache, comp_block_table, swa_cache, swa_block_tab
     return ws_cache
 
 
-def _attention(fn, q, kv_cache, indices, lens, sinks, softmax_scale, out, lse, page_size, stream):
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _attention(fn, q, kv_cache, indices, lens, sinks, softmax_scale, out, lse, page_size,
+               workspace, stream):
     _want(q, torch.bfloat16, "q"), _want(kv_cache, torch.uint8, "kv_cache")
     _want(indices, torch.int32, "indices"), _want(lens, torch.int32, "lens")
     _want(sinks, torch.float32, "sinks"), _want(out, torch.bfloat16, "out")
@@ -209,23 +217,30 @@ def _attention(fn, q, kv_cache, indices, lens, sinks, softmax_scale, out, lse, p
     num_pages = kv_cache.numel() // cache_page_bytes(page_size)
     _check(fn(_ptr(q), _ptr(kv_cache), num_pages, page_size, _ptr(indices), indices.shape[1],
               _ptr(lens), _ptr(sinks), float(softmax_scale), _ptr(out), _ptr(lse), T, H,
-              _stream(stream)))
+              _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return out
 
 
+def workspace_bytes(T, H, width, prefill=False):
+    """Device workspace bytes dsv4_sparse_mla_decode (or _prefill) may use."""
+    return int(_lib.dsv4_sparse_mla_workspace_bytes(T, H, width, int(bool(prefill))))
+
+
 def dsv4_sparse_mla_decode(q, kv_cache, indices, lens, sinks, softmax_scale, out, lse=None,
-                           page_size=64, stream=None):
+                           page_size=64, workspace=None, stream=None):
     """q bf16 [T, H, 576], indices int32 [T, stride] physical slots, lens int32 [T],
-    sinks fp32 [H] or None -> out bf16 [T, H, 512] (and lse fp32 [T, H] if given)."""
+    sinks fp32 [H] or None -> out bf16 [T, H, 512] (and lse fp32 [T, H] if given).
+    workspace: None, or a device tensor of at least workspace_bytes(T, H, stride) bytes
+    (lets a small batch run its rows in pieces)."""
     return _attention(_lib.dsv4_sparse_mla_decode, q, kv_cache, indices, lens, sinks,
-                      softmax_scale, out, lse, page_size, stream)
+                      softmax_scale, out, lse, page_size, workspace, stream)
 
 
 def dsv4_sparse_mla_prefill(q, kv_cache, indices, lens, sinks, softmax_scale, out, lse=None,
-                            page_size=64, stream=None):
+                            page_size=64, workspace=None, stream=None):
     """Same contract as dsv4_sparse_mla_decode, scheduled for many query tokens."""
     return _attention(_lib.dsv4_sparse_mla_prefill, q, kv_cache, indices, lens, sinks,
-                      softmax_scale, out, lse, page_size, stream)
+                      softmax_scale, out, lse, page_size, workspace, stream)
 
 
 def dsv4_sparse_mla_decode_topk(q, kv_cache, topk, topk_lens, query_start_loc, seq_lens,

@@ -232,19 +232,45 @@ int dsv4_gather_workspace(const uint8_t* comp_cache, int comp_num_pages,
                     fn);
 }
 
-int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
-                           const int32_t* indices, int idx_stride, const int32_t* lens,
-                           const float* sinks, float softmax_scale, void* out, float* lse, int T,
-                           int H, void* stream) {
-  const char* fn = "dsv4_sparse_mla_decode";
+// decode and prefill: the same checks, the workspace contract, then the launch
+static int attention_checked(const char* fn, bool prefill, const void* q, const uint8_t* kv_cache,
+                             int num_pages, int page_size, const int32_t* indices, int idx_stride,
+                             const int32_t* lens, const float* sinks, float softmax_scale,
+                             void* out, float* lse, int T, int H, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   int st = check_attention(fn, q, kv_cache, num_pages, page_size, indices, idx_stride, lens, sinks,
                            softmax_scale, out, T, H);
   if (st) return st;
+  if (!workspace && workspace_bytes != 0)
+    return fail(DSV4_ERR_WORKSPACE, "%s: workspace is NULL but workspace_bytes is %zu", fn,
+                workspace_bytes);
+  if (workspace) {
+    const size_t need = dsv4::attention_workspace_bytes(T, H, idx_stride, prefill);
+    if (!aligned(workspace, 16) || workspace_bytes < need)
+      return fail(DSV4_ERR_WORKSPACE,
+                  "%s: a workspace must be 16-byte aligned and hold %zu bytes (got %zu)", fn, need,
+                  workspace_bytes);
+  }
   if (T == 0) return ok();
-  return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size), indices, idx_stride, lens, sinks,
-                                           softmax_scale, out, lse, T, H, false,
+  return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size),
+                                           indices, idx_stride, lens, sinks, softmax_scale, out,
+                                           lse, T, H, prefill, workspace, workspace_bytes,
                                            static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
+                           const int32_t* indices, int idx_stride, const int32_t* lens,
+                           const float* sinks, float softmax_scale, void* out, float* lse, int T,
+                           int H, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_checked("dsv4_sparse_mla_decode", false, q, kv_cache, num_pages, page_size,
+                           indices, idx_stride, lens, sinks, softmax_scale, out, lse, T, H,
+                           workspace, workspace_bytes, stream);
+}
+
+size_t dsv4_sparse_mla_workspace_bytes(int T, int H, int width, int is_prefill) {
+  if (T < 0 || width < 0 || (H != 16 && H != 32 && H != 64 && H != 128)) return 0;
+  return dsv4::attention_workspace_bytes(T, H, width, is_prefill != 0);
 }
 
 size_t dsv4_sparse_mla_split_workspace_bytes(int T, int H, int splits) {
@@ -265,8 +291,8 @@ int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num
   if (T == 0) return ok();
   if (splits == 1)
     return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size), indices, idx_stride, lens,
-                                             sinks, softmax_scale, out, lse, T, H, false,
-                                             static_cast<hipStream_t>(stream)),
+                                             sinks, softmax_scale, out, lse, T, H, false, nullptr,
+                                             0, static_cast<hipStream_t>(stream)),
                       fn);
   if ((int64_t)T * splits >= ((int64_t)1 << 31) / 8)
     return fail(DSV4_ERR_SHAPE, "%s: T * splits = %lld too large", fn, (long long)T * splits);
@@ -316,6 +342,8 @@ int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_
                     fn);
 }
 
+constexpr int kMaxStepQueriesPerRequest = 64;
+
 static int decode_step_checked(const char* fn, void* q, const void* kv, const int64_t* positions,
                                const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                                const void* q_norm_weight, float eps, uint8_t* kv_cache,
@@ -338,6 +366,13 @@ static int decode_step_checked(const char* fn, void* q, const void* kv, const in
     return fail(DSV4_ERR_UNSUPPORTED, "%s: top_k + window = %lld > 4096", fn, (long long)top_k + window);
   if (splits < 1 || splits > 64)
     return fail(DSV4_ERR_UNSUPPORTED, "%s: splits %d not in 1..64", fn, splits);
+  // every workgroup of a token re-quantises its request's new rows up to its own, so the
+  // insert work grows with the square of a request's query count: decode batches only
+  if ((int64_t)T > (int64_t)kMaxStepQueriesPerRequest * (B > 0 ? B : 1))
+    return fail(DSV4_ERR_UNSUPPORTED,
+                "%s: T = %d exceeds %d query tokens per request on average (B = %d); use "
+                "dsv4_kv_insert + dsv4_sparse_mla_decode_topk for prefill-sized requests",
+                fn, T, kMaxStepQueriesPerRequest, B);
   if (!(softmax_scale == softmax_scale)) return fail(DSV4_ERR_SHAPE, "%s: softmax_scale is NaN", fn);
   if (!(eps >= 0.f)) return fail(DSV4_ERR_SHAPE, "%s: eps must be >= 0", fn);
   if (T == 0) return ok();
@@ -402,16 +437,10 @@ int dsv4_sparse_mla_decode_step_split(
 int dsv4_sparse_mla_prefill(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
                             const int32_t* indices, int idx_stride, const int32_t* lens,
                             const float* sinks, float softmax_scale, void* out, float* lse, int T,
-                            int H, void* stream) {
-  const char* fn = "dsv4_sparse_mla_prefill";
-  int st = check_attention(fn, q, kv_cache, num_pages, page_size, indices, idx_stride, lens, sinks,
-                           softmax_scale, out, T, H);
-  if (st) return st;
-  if (T == 0) return ok();
-  return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size), indices, idx_stride, lens, sinks,
-                                           softmax_scale, out, lse, T, H, true,
-                                           static_cast<hipStream_t>(stream)),
-                    fn);
+                            int H, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_checked("dsv4_sparse_mla_prefill", true, q, kv_cache, num_pages, page_size,
+                           indices, idx_stride, lens, sinks, softmax_scale, out, lse, T, H,
+                           workspace, workspace_bytes, stream);
 }
 
 int dsv4_gather_dequant(const uint8_t* kv_cache, int num_pages, int page_size, const int32_t* slots,

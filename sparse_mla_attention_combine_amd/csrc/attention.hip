@@ -798,7 +798,12 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
         rope_cs_load(kvp >= 0 && kvp < sti.max_pos ? sti.cos_sin + kvp * kRope : no_row, lane);
     end = combine_rows<NHB>(sm, tin, t, ps, tid, xv, tl);
     // this wave's q rows normalised and rotated in LDS (each lane rereads its own chunks)
-    // and written back in place
+    // and, when the row is not cut into pieces, written back in place.  With pieces, the
+    // workgroups of a token's other pieces may still be about to read the raw rows (a
+    // grid of several dispatch rounds starts them at different times), so every piece
+    // reads raw q and only the merge launch, stream-ordered after all of them, writes
+    // the normalised rows.
+    const bool q_writer = splits == 1;
     if (w < 2 * NHB && qok) {
       u32x4* qg = reinterpret_cast<u32x4*>(sti.q + ((int64_t)t * H + h0 + 8 * w + (lane >> 3)) *
                                                        kLatent) + c8;
@@ -810,7 +815,7 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
       for (int k = 0; k < 9; ++k) {
         const u32x4 y = qn_chunk(ql[8 * k], wq[k], inv, qrot, k == 8);
         ql[8 * k] = y;
-        qg[8 * k] = y;
+        if (q_writer) qg[8 * k] = y;
       }
     }
     // the new rows this token may read: its request's tokens up to itself (only itself for
@@ -1025,10 +1030,18 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
 //   M = max(z, max_s m_s),  den = 2^(z-M) + sum_s l_s 2^(m_s-M),
 //   out = sum_s O_s 2^(m_s-M) / den,  lse = (M + log2 den) ln 2.
 // One wave per (token, head); lane l owns output dims 8l..8l+7.
+// For the split form of the whole step, blocks past the merge's normalise and rotate q in
+// place (the insert's q part, the same per-row arithmetic): the pieces read raw q, and
+// this launch runs after all of them.
 __global__ void __launch_bounds__(256) split_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const float* __restrict__ sinks, uint16_t* __restrict__ out, float* __restrict__ lse, int T,
-    int H, int splits) {
+    int H, int splits, int merge_blocks, int qblocks, StepIn sti) {
+  if ((int)blockIdx.x >= merge_blocks) {
+    q_norm_rope_rows(sti.q, sti.positions, sti.cos_sin, sti.max_pos, sti.weight, sti.eps,
+                     (int64_t)T * H, H, (int)blockIdx.x - merge_blocks, qblocks);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * H + h
   if (row >= (int64_t)T * H) return;
@@ -1160,17 +1173,42 @@ hipError_t launch_attention_step(void* q, const void* kv, const int64_t* positio
                                           split_len, part_o, part_ml, tin, sti, stream);
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)T * H;
-  hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
-                     part_o, part_ml, sinks, static_cast<uint16_t*>(out), lse, T, H, splits);
+  const int merge_blocks = (int)((rows + 3) / 4);
+  // the q rows, 32 per block per pass (the insert kernel's partition); positions outside
+  // [0, max_pos) leave their rows untouched, and with no valid position none is touched
+  const int64_t qgroups = (rows + 31) / 32;
+  const int qblocks = max_pos > 0 ? (int)(qgroups < 8192 ? qgroups : 8192) : 0;
+  hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)(merge_blocks + qblocks)), dim3(256), 0,
+                     stream, part_o, part_ml, sinks, static_cast<uint16_t*>(out), lse, T, H,
+                     splits, merge_blocks, qblocks, sti);
   return hipGetLastError();
+}
+
+int auto_splits(int T, int H, int width, bool prefill) {
+  // workgroups of the unsplit schedule: (token, 32 heads), or (token, 16 heads) at H = 16
+  const int64_t wgs = (int64_t)T * (H == 16 ? 1 : H / 32);
+  if (prefill || wgs <= 0 || wgs >= 160) return 1;
+  int s = (int)(256 / wgs);
+  s = s < 8 ? s : 8;                             // the merge's one-round maximum
+  while (s > 1 && width < 256 * s) --s;          // pieces of at least 256 entries
+  return s > 1 ? s : 1;
+}
+
+size_t attention_workspace_bytes(int T, int H, int width, bool prefill) {
+  const int s = auto_splits(T, H, width, prefill);
+  return s > 1 ? split_workspace_bytes(T, H, s) : 0;
 }
 
 hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, int page_shift,
                             const int32_t* indices, int idx_stride, const int32_t* lens,
                             const float* sinks, float softmax_scale, void* out, float* lse, int T,
-                            int H, bool prefill, hipStream_t stream) {
-  (void)prefill;  // one schedule serves both entry points for now
+                            int H, bool prefill, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  const int splits = auto_splits(T, H, idx_stride, prefill);
+  if (splits > 1 && workspace && workspace_bytes >= split_workspace_bytes(T, H, splits))
+    return launch_attention_split(q, cache, num_pages, page_shift, indices, idx_stride, lens,
+                                  sinks, softmax_scale, out, lse, T, H, splits, workspace, stream);
   const int whole = idx_stride > 0 ? idx_stride : 1;
   return launch_items<false, false>(q, cache, num_pages, page_shift, indices, idx_stride, lens,
                                     sinks, softmax_scale, out, lse, T, H, 1, whole, nullptr,
@@ -1192,8 +1230,10 @@ hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_p
                                             split_len, part_o, part_ml, TopkIn{}, StepIn{}, stream);
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)T * H;
-  hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
-                     part_o, part_ml, sinks, static_cast<uint16_t*>(out), lse, T, H, splits);
+  const int merge_blocks = (int)((rows + 3) / 4);
+  hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)merge_blocks), dim3(256), 0, stream,
+                     part_o, part_ml, sinks, static_cast<uint16_t*>(out), lse, T, H, splits,
+                     merge_blocks, 0, StepIn{});
   return hipGetLastError();
 }
 

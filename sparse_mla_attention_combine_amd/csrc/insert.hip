@@ -18,42 +18,6 @@
 
 namespace dsv4 {
 
-__device__ __forceinline__ void q_norm_rope(
-    uint16_t* __restrict__ q, const int64_t* __restrict__ positions,
-    const float* __restrict__ cos_sin, int max_pos, const uint16_t* __restrict__ weight, float eps,
-    int64_t rows, int H, int qblocks) {
-  const int lane = threadIdx.x & 63;
-  const int r8 = lane >> 3, c8 = lane & 7;
-  // this lane always touches chunks c8 + 8k (k = 0..8) of a row: keep their weights
-  u32x4 w[9];
-#pragma unroll
-  for (int k = 0; k < 9; ++k) w[k] = *reinterpret_cast<const u32x4*>(weight + 8 * (c8 + 8 * k));
-  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)qblocks * blockDim.x) >> 6;
-  for (int64_t g = wave; g * 8 < rows; g += nwaves) {
-    const int64_t row = g * 8 + r8;
-    if (row >= rows) continue;
-    const int64_t t = row / H;
-    const int64_t p = positions[t];
-    uint16_t* qr = q + row * kLatent;
-    // the row is requested together with its position; the position is only tested after
-    // the row has been consumed, so the compiler keeps the loads side by side
-    u32x4 x[9];
-#pragma unroll
-    for (int k = 0; k < 9; ++k) x[k] = *reinterpret_cast<const u32x4*>(qr + 8 * (c8 + 8 * k));
-    const bool ok = p >= 0 && p < max_pos;
-    const RopeCs rot = rope_cs_load(cos_sin + (ok ? p : 0) * kRope, c8);
-    float ss = 0.f;
-#pragma unroll
-    for (int k = 0; k < 9; ++k) ss = qn_sum_sq(x[k], ss);
-    const float inv = qn_inv(ss, eps);
-    if (!ok) continue;  // token left untouched
-#pragma unroll
-    for (int k = 0; k < 9; ++k)
-      *reinterpret_cast<u32x4*>(qr + 8 * (c8 + 8 * k)) = qn_chunk(x[k], w[k], inv, rot, k == 8);
-  }
-}
-
 __device__ __forceinline__ void kv_quant_insert(
     const uint16_t* __restrict__ kv, const int64_t* __restrict__ positions,
     const int64_t* __restrict__ slot_mapping, const float* __restrict__ cos_sin, int max_pos,
@@ -78,7 +42,8 @@ __global__ void __launch_bounds__(256) insert_kernel(
     const uint16_t* __restrict__ weight, float eps, uint8_t* __restrict__ cache, int64_t num_slots,
     int ps, int T, int H, int qblocks) {
   if ((int)blockIdx.x < qblocks)
-    q_norm_rope(q, positions, cos_sin, max_pos, weight, eps, (int64_t)T * H, H, qblocks);
+    q_norm_rope_rows(q, positions, cos_sin, max_pos, weight, eps, (int64_t)T * H, H,
+                     (int)blockIdx.x, qblocks);
   else
     kv_quant_insert(kv, positions, slot_mapping, cos_sin, max_pos, cache, num_slots, ps, T,
                     (int)blockIdx.x - qblocks);

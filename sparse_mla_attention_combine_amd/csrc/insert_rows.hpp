@@ -150,4 +150,44 @@ __device__ __forceinline__ void kv_quant_store(const KvLane& v, const RopeCs& ro
   }
 }
 
+// q RMSNorm + RoPE in place over q rows [T*H][576] for the waves of `nblocks` blocks of
+// 256 threads, this one being block `block`: wave k handles rows 8k .. 8k+7, then
+// 8(k + nwaves) ..., each row over 8 lanes (the partition above).  A row whose token's
+// position lies outside [0, max_pos) is left untouched.
+__device__ __forceinline__ void q_norm_rope_rows(
+    uint16_t* __restrict__ q, const int64_t* __restrict__ positions,
+    const float* __restrict__ cos_sin, int max_pos, const uint16_t* __restrict__ weight, float eps,
+    int64_t rows, int H, int block, int nblocks) {
+  const int lane = threadIdx.x & 63;
+  const int r8 = lane >> 3, c8 = lane & 7;
+  // this lane always touches chunks c8 + 8k (k = 0..8) of a row: keep their weights
+  u32x4 w[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) w[k] = *reinterpret_cast<const u32x4*>(weight + 8 * (c8 + 8 * k));
+  const int64_t wave = ((int64_t)block * 256 + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)nblocks * 256) >> 6;
+  for (int64_t g = wave; g * 8 < rows; g += nwaves) {
+    const int64_t row = g * 8 + r8;
+    if (row >= rows) continue;
+    const int64_t t = row / H;
+    const int64_t p = positions[t];
+    uint16_t* qr = q + row * kLatent;
+    // the row is requested together with its position; the position is only tested after
+    // the row has been consumed, so the compiler keeps the loads side by side
+    u32x4 x[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) x[k] = *reinterpret_cast<const u32x4*>(qr + 8 * (c8 + 8 * k));
+    const bool ok = p >= 0 && p < max_pos;
+    const RopeCs rot = rope_cs_load(cos_sin + (ok ? p : 0) * kRope, c8);
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) ss = qn_sum_sq(x[k], ss);
+    const float inv = qn_inv(ss, eps);
+    if (!ok) continue;  // token left untouched
+#pragma unroll
+    for (int k = 0; k < 9; ++k)
+      *reinterpret_cast<u32x4*>(qr + 8 * (c8 + 8 * k)) = qn_chunk(x[k], w[k], inv, rot, k == 8);
+  }
+}
+
 }  // namespace dsv4

@@ -48,10 +48,18 @@ hipError_t launch_insert(void* q, const void* kv, const int64_t* positions,
 hipError_t launch_gather(const uint8_t* cache, int num_pages, int page_shift, const int32_t* slots,
                          int n, void* out, hipStream_t stream);
 
+// Decode / prefill over index rows from memory.  With a workspace of at least
+// attention_workspace_bytes(T, H, idx_stride, prefill) bytes the call may cut rows into
+// pieces (a decode batch too small to fill the compute units); workspace may be NULL.
 hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, int page_shift,
                             const int32_t* indices, int idx_stride, const int32_t* lens,
                             const float* sinks, float softmax_scale, void* out, float* lse,
-                            int T, int H, bool prefill, hipStream_t stream);
+                            int T, int H, bool prefill, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+// Pieces per row the decode picks for T tokens, H heads and rows of `width` entries
+// (1: no split), and the workspace that schedule needs (0 with no split).
+int auto_splits(int T, int H, int width, bool prefill);
+size_t attention_workspace_bytes(int T, int H, int width, bool prefill);
 
 // Split-slot decode: the row of each token is cut into `splits` 64-aligned pieces whose
 // partials go to `workspace` (split_workspace_bytes(T, H, splits) bytes) and are merged.

@@ -50,11 +50,14 @@ def errors(got_bits, ref):
     return d, rms
 
 
-def assert_attention_close(got_bits, ref, what, max_abs=1e-2, mean_abs=1e-3):
+def assert_attention_close(got_bits, ref, what, max_abs=1e-2, mean_abs=1e-3, out_rounding=False):
     """The 1e-2 max / 1e-3 mean absolute bar holds for outputs of unit scale.  An element
     of magnitude m > 1 gets the bar scaled by m (the bf16 result alone carries a relative
     rounding of 2^-9, i.e. 0.0156 absolute at |out| = 4-8); the mean bar is scaled by
-    max(1, RMS of the oracle output)."""
+    max(1, RMS of the oracle output).  out_rounding: the mean bar also allows the bf16
+    output format's own rounding of the oracle value (ulp / 4 on average for round to
+    nearest), which alone is ~1e-3 for outputs near 0.8: the case of peaked logits over
+    long rows, whose outputs are whole value rows of unit scale."""
     d, rms = errors(got_bits, ref)
     g = bits_to_f64(got_bits)
     assert np.all(np.isfinite(g)), what
@@ -66,4 +69,5 @@ def assert_attention_close(got_bits, ref, what, max_abs=1e-2, mean_abs=1e-3):
         f"max|d|/rms={d.max() / max(rms, 1e-30):.3e} max|d|/ulp_bf16(ref)={np.max(d / ulp):.2f} "
         f"worst/bound={np.max(d / bound):.3f}")
     assert np.all(d <= bound), what
-    assert d.mean() <= mean_abs * max(1.0, rms), what
+    extra = float(np.mean(ulp) / 4) if out_rounding else 0.0
+    assert d.mean() <= mean_abs * max(1.0, rms) + extra, (what, d.mean(), extra)

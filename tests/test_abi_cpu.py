@@ -47,9 +47,10 @@ def test_attention_validation(dsv4):
                 scale=0.04, out=p, lse=None, T=2, H=16)
 
     def call(fn, **kw):
-        a = dict(args, **kw)
+        a = dict(args, ws=None, wsb=0, **kw)
         return fn(a["q"], a["cache"], a["num_pages"], a["page_size"], a["idx"], a["stride"],
-                  a["lens"], a["sinks"], a["scale"], a["out"], a["lse"], a["T"], a["H"], None)
+                  a["lens"], a["sinks"], a["scale"], a["out"], a["lse"], a["T"], a["H"], a["ws"],
+                  a["wsb"], None)
 
     for fn in (lib.dsv4_sparse_mla_decode, lib.dsv4_sparse_mla_prefill):
         assert call(fn, H=24) == 4 and b"H = 24" in lib.dsv4_last_error()
@@ -61,6 +62,43 @@ def test_attention_validation(dsv4):
         assert call(fn, num_pages=-3) == 2
         assert call(fn, out=ctypes.c_void_p(p.value + 2)) == 3
         assert call(fn, T=0, q=None) == 0 and lib.dsv4_last_error() == b""
+
+
+def test_attention_workspace_contract(dsv4):
+    """dsv4_sparse_mla_workspace_bytes: 0 for a batch that fills the GPU and for prefill,
+    the split workspace of the chosen piece count otherwise; the decode / prefill reject
+    a short, misaligned or inconsistent workspace before launching anything."""
+    lib = dsv4.library()
+    wsb = lib.dsv4_sparse_mla_workspace_bytes
+    split = lib.dsv4_sparse_mla_split_workspace_bytes
+    assert wsb(64, 128, 2176, 0) == 0              # 256 workgroups: no split
+    assert wsb(8192, 64, 2176, 1) == 0             # prefill: never
+    assert wsb(8, 128, 2176, 1) == 0
+    assert wsb(8, 128, 2176, 0) == split(8, 128, 8)  # 32 workgroups -> 8 pieces
+    assert wsb(32, 128, 2176, 0) == split(32, 128, 2)
+    assert wsb(8, 128, 600, 0) == split(8, 128, 2)   # pieces of >= 256 entries
+    assert wsb(8, 128, 255, 0) == 0
+    assert wsb(2, 16, 4096, 0) == split(2, 16, 8)
+    assert wsb(-1, 128, 2176, 0) == 0 and wsb(8, 24, 2176, 0) == 0 and wsb(8, 128, -1, 0) == 0
+    keep, p = _fake()
+    need = wsb(2, 16, 4096, 0)
+
+    def call(fn, **kw):
+        a = dict(q=p, cache=p, num_pages=4, page_size=64, idx=p, stride=4096, lens=p, sinks=None,
+                 scale=0.04, out=p, lse=None, T=2, H=16, ws=p, wsb=need)
+        a.update(kw)
+        return fn(a["q"], a["cache"], a["num_pages"], a["page_size"], a["idx"], a["stride"],
+                  a["lens"], a["sinks"], a["scale"], a["out"], a["lse"], a["T"], a["H"], a["ws"],
+                  a["wsb"], None)
+
+    for fn in (lib.dsv4_sparse_mla_decode, lib.dsv4_sparse_mla_prefill):
+        assert call(fn, T=0, q=None) == 0
+        assert call(fn, ws=None, wsb=16) == 5 and b"NULL" in lib.dsv4_last_error()
+        assert call(fn, ws=ctypes.c_void_p(p.value + 8), T=0) == 5
+    assert call(lib.dsv4_sparse_mla_decode, wsb=need - 1) == 5  # fails before any launch
+    assert b"hold" in lib.dsv4_last_error()
+    assert call(lib.dsv4_sparse_mla_prefill, wsb=0, T=0) == 0   # prefill needs none
+    assert call(lib.dsv4_sparse_mla_decode, H=24) == 4
 
 
 def test_split_decode_validation(dsv4):
@@ -241,6 +279,10 @@ def test_decode_step_split_validation(dsv4):
     assert call(H=24) == 4
     assert call(P=48) == 4
     assert call(T=0) == 0
+    # B = 2 requests: more than 64 query tokens per request on average is refused (the
+    # step re-quantises a request's new rows in every workgroup of its tokens)
+    assert call(T=129) == 4 and b"query tokens per request" in lib.dsv4_last_error()
+    assert call(T=128) == 5  # within the bound: the workspace check comes next
 
 
 def test_insert_and_gather_validation(dsv4):

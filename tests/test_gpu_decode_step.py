@@ -288,3 +288,43 @@ def test_decode_step_split_equals_insert_combine_split(dsv4, seed):
     torch.cuda.synchronize()
     assert _same(q, q3) and torch.equal(cache, c3)
     assert _same(out, o3) and _same(lse, l3)
+
+
+@pytest.mark.parametrize("splits", [3, 5])
+def test_decode_step_split_many_rounds(dsv4, splits):
+    """The split step on the benchmark batch (64 tokens x 4 head groups x `splits` pieces =
+    768 / 1280 workgroups, several dispatch rounds, so the pieces of one row start at
+    different times): q, cache bytes, out and lse bit for bit equal to insert, combine
+    and the split decode.  Every piece reads the raw q rows; a piece that read rows a
+    sibling had already normalised would normalise them twice and differ here."""
+    c, q0, cache0 = _bench_case(dsv4, seed=12)
+    T, H, P = q0.shape[0], q0.shape[1], 64
+    W = (c["top_k"] + c["window"] + 127) // 128 * 128
+    log(f"decode_step split many rounds: T={T} H={H} splits={splits} "
+        f"workgroups={T * (H // 32) * splits}")
+    ws = torch.empty(dsv4.split_workspace_bytes(T, H, splits), dtype=torch.uint8, device="cuda")
+    q3, c3 = q0.clone(), cache0.clone()
+    dsv4.dsv4_kv_insert(q3, c["kv"], c["pos"], c["slots"], c["cos_sin"], c["w"], 1e-6, c3,
+                        page_size=P)
+    comb = torch.full((T, W), -1, dtype=torch.int32, device="cuda")
+    lens = torch.zeros(T, dtype=torch.int32, device="cuda")
+    dsv4.dsv4_combine_indices(c["topk"], c["tl"], c["qsl"], c["sl"], c["bt"], c["top_k"],
+                              c["window"], comb, lens, page_size=P)
+    o3 = torch.empty(T, H, 512, dtype=torch.bfloat16, device="cuda")
+    l3 = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    dsv4.dsv4_sparse_mla_decode_split(q3, c3, comb, lens, c["sinks"], c["scale"], o3, splits, ws,
+                                      lse=l3, page_size=P)
+    torch.cuda.synchronize()
+    o3, l3 = o3.clone(), l3.clone()
+    for rep in range(2):
+        q, cache = q0.clone(), cache0.clone()
+        out = torch.full((T, H, 512), 3.0, dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((T, H), 3.0, dtype=torch.float32, device="cuda")
+        dsv4.dsv4_sparse_mla_decode_step(q, c["kv"], c["pos"], c["slots"], c["cos_sin"], c["w"],
+                                         1e-6, cache, c["topk"], c["tl"], c["qsl"], c["sl"],
+                                         c["bt"], c["top_k"], c["window"], c["sinks"], c["scale"],
+                                         out, lse, page_size=P, splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        assert _same(q, q3), ("q", rep)
+        assert torch.equal(cache, c3), ("cache", rep)
+        assert _same(out, o3) and _same(lse, l3), ("out / lse", rep)
