@@ -400,6 +400,30 @@ int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dsv4_sparse_mla_decode_split_noalloc — dsv4_sparse_mla_decode_split for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels, with the workspace in a static
+ * device array that the library holds on each GPU it runs on until the process ends
+ * (DSV4_NOALLOC_SCRATCH_BYTES = 32 MiB per GPU).  The call allocates nothing.
+ *   Arguments as dsv4_sparse_mla_decode_split, without workspace / workspace_bytes.
+ *   Result: bit-identical to dsv4_sparse_mla_decode_split with the same splits.
+ *   Limit: dsv4_sparse_mla_split_workspace_bytes(T, H, splits) <= 32 MiB (e.g. 256
+ *   workgroups' worth of pieces at H >= 32: T * splits <= 63 at H = 128), else
+ *   DSV4_ERR_WORKSPACE with nothing launched.
+ *   Every call on one GPU shares that GPU's array (the contents of the last call stay
+ *   there; nothing in it needs to start at zero): calls that overlap on one GPU, i.e. on
+ *   different streams without ordering, race and give wrong results.
+ * Errors: as dsv4_sparse_mla_decode_split; DSV4_ERR_HIP if the array's device address
+ * cannot be obtained.
+ */
+#define DSV4_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int dsv4_sparse_mla_decode_split_noalloc(const void* q, const uint8_t* kv_cache, int num_pages,
+                                         int page_size, const int32_t* indices, int idx_stride,
+                                         const int32_t* lens, const float* sinks,
+                                         float softmax_scale, void* out, float* lse, int T, int H,
+                                         int splits, void* stream);
+
+/*
  * dsv4_gather_dequant — gather + dequantise slots into bf16 rows [p2 Key source
  * excerpts: _dequant_gather_slots_kernel, one program per slot; a negative slot gives
  * a zero row; FP8 -> fp32 times 2^(byte-127) -> bf16; the bf16 RoPE part is copied].

@@ -42,6 +42,7 @@ _lib.dsv4_gather_dequant.argtypes = [_vp, _i32, _i32, _vp, _i32, _vp, _vp]
 _lib.dsv4_sparse_mla_split_workspace_bytes.argtypes = [_i32, _i32, _i32]
 _lib.dsv4_sparse_mla_split_workspace_bytes.restype = ctypes.c_size_t
 _lib.dsv4_sparse_mla_decode_split.argtypes = _attn_head + [_i32, _vp, ctypes.c_size_t, _vp]
+_lib.dsv4_sparse_mla_decode_split_noalloc.argtypes = _attn_head + [_i32, _vp]
 _lib.dsv4_combine_indices_compressed.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]
 _lib.dsv4_sparse_mla_decode_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp,
@@ -59,7 +60,8 @@ for _f in (_lib.dsv4_kv_insert, _lib.dsv4_combine_indices, _lib.dsv4_sparse_mla_
            _lib.dsv4_sparse_mla_prefill, _lib.dsv4_gather_dequant, _lib.dsv4_sparse_mla_decode_split,
            _lib.dsv4_combine_indices_compressed, _lib.dsv4_gather_workspace,
            _lib.dsv4_indexer_topk, _lib.dsv4_sparse_mla_decode_topk,
-           _lib.dsv4_sparse_mla_decode_step, _lib.dsv4_sparse_mla_decode_step_split):
+           _lib.dsv4_sparse_mla_decode_step, _lib.dsv4_sparse_mla_decode_step_split,
+           _lib.dsv4_sparse_mla_decode_split_noalloc):
     _f.restype = _i32
 
 EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4_kv_insert",
@@ -68,7 +70,9 @@ EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4
             "dsv4_sparse_mla_decode_split", "dsv4_combine_indices_compressed",
             "dsv4_gather_workspace", "dsv4_indexer_topk", "dsv4_sparse_mla_decode_topk",
             "dsv4_sparse_mla_decode_step", "dsv4_sparse_mla_decode_step_split",
-            "dsv4_sparse_mla_workspace_bytes"]
+            "dsv4_sparse_mla_workspace_bytes", "dsv4_sparse_mla_decode_split_noalloc"]
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class Dsv4Error(RuntimeError):
@@ -323,6 +327,24 @@ def dsv4_sparse_mla_decode_split(q, kv_cache, indices, lens, sinks, softmax_scal
         _ptr(q), _ptr(kv_cache), num_pages, page_size, _ptr(indices), indices.shape[1], _ptr(lens),
         _ptr(sinks), float(softmax_scale), _ptr(out), _ptr(lse), T, H, int(splits), _ptr(workspace),
         ws_bytes, _stream(stream)))
+    return out
+
+
+def dsv4_sparse_mla_decode_split_noalloc(q, kv_cache, indices, lens, sinks, softmax_scale, out,
+                                         splits, lse=None, page_size=64, stream=None):
+    """dsv4_sparse_mla_decode_split with its workspace in the library's static per-GPU
+    scratch array (no allocation; split_workspace_bytes(T, H, splits) must fit
+    NOALLOC_SCRATCH_BYTES).  Calls that overlap on one GPU race."""
+    _want(q, torch.bfloat16, "q"), _want(kv_cache, torch.uint8, "kv_cache")
+    _want(indices, torch.int32, "indices"), _want(lens, torch.int32, "lens")
+    _want(sinks, torch.float32, "sinks"), _want(out, torch.bfloat16, "out")
+    _want(lse, torch.float32, "lse")
+    T, H = q.shape[0], q.shape[1]
+    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    _check(_lib.dsv4_sparse_mla_decode_split_noalloc(
+        _ptr(q), _ptr(kv_cache), num_pages, page_size, _ptr(indices), indices.shape[1], _ptr(lens),
+        _ptr(sinks), float(softmax_scale), _ptr(out), _ptr(lse), T, H, int(splits),
+        _stream(stream)))
     return out
 
 

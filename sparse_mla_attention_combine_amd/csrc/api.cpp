@@ -306,6 +306,44 @@ int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num
                     fn);
 }
 
+int dsv4_sparse_mla_decode_split_noalloc(const void* q, const uint8_t* kv_cache, int num_pages,
+                                         int page_size, const int32_t* indices, int idx_stride,
+                                         const int32_t* lens, const float* sinks,
+                                         float softmax_scale, void* out, float* lse, int T, int H,
+                                         int splits, void* stream) {
+  const char* fn = "dsv4_sparse_mla_decode_split_noalloc";
+  int st = check_attention(fn, q, kv_cache, num_pages, page_size, indices, idx_stride, lens, sinks,
+                           softmax_scale, out, T, H);
+  if (st) return st;
+  if (splits < 1 || splits > 64) return fail(DSV4_ERR_SHAPE, "%s: splits %d not in 1..64", fn, splits);
+  if (T == 0) return ok();
+  if (splits == 1)
+    return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size),
+                                             indices, idx_stride, lens, sinks, softmax_scale, out,
+                                             lse, T, H, false, nullptr, 0,
+                                             static_cast<hipStream_t>(stream)),
+                      fn);
+  if ((int64_t)T * splits >= ((int64_t)1 << 31) / 8)
+    return fail(DSV4_ERR_SHAPE, "%s: T * splits = %lld too large", fn, (long long)T * splits);
+  const size_t need = dsv4::split_workspace_bytes(T, H, splits);
+  if (need > dsv4::kNoallocScratchBytes)
+    return fail(DSV4_ERR_WORKSPACE,
+                "%s: T = %d, H = %d, splits = %d need %zu bytes of workspace, more than the %zu "
+                "bytes of the library's static scratch array (use dsv4_sparse_mla_decode_split "
+                "with a workspace of your own)",
+                fn, T, H, splits, need, dsv4::kNoallocScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = dsv4::noalloc_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(DSV4_ERR_HIP, "%s: the address of the static scratch array: %s", fn,
+                hipGetErrorString(e));
+  return hip_status(dsv4::launch_attention_split(q, kv_cache, num_pages,
+                                                 dsv4::page_shift_of(page_size), indices,
+                                                 idx_stride, lens, sinks, softmax_scale, out, lse,
+                                                 T, H, splits, ws, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
                                 const int32_t* topk, int topk_stride, int topk_width,
                                 const int32_t* topk_lens, const int32_t* query_start_loc,

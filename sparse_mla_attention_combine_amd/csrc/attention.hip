@@ -44,6 +44,8 @@
 // also performs the insert step first (PR #42953 Implementation breakdown item 4: q
 // RMSNorm + GPT-J RoPE, FP8/UE8M0 insert of the new latent rows) so that one launch is
 // the whole decode step.
+#include <mutex>
+
 #include "device.hpp"
 #include "insert_rows.hpp"
 #include "launch.hpp"
@@ -1213,6 +1215,32 @@ hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, 
   return launch_items<false, false>(q, cache, num_pages, page_shift, indices, idx_stride, lens,
                                     sinks, softmax_scale, out, lse, T, H, 1, whole, nullptr,
                                     nullptr, TopkIn{}, StepIn{}, stream);
+}
+
+// Workspace of the split decode for callers that cannot allocate: one static device array
+// per GPU the library runs on (held until the process ends).  Host code never passes the
+// array's name to a kernel or a copy: its host-side symbol is only a stand-in, so the
+// device address is taken once per device, with that device current, and kept.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* dev_ptr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!dev_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_pages,

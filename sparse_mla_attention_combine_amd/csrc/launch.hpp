@@ -69,6 +69,12 @@ hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_p
                                   int T, int H, int splits, void* workspace, hipStream_t stream);
 size_t split_workspace_bytes(int T, int H, int splits);
 
+// The split decode's workspace for callers that cannot allocate: a static device array of
+// kNoallocScratchBytes per GPU; *ptr receives its address on the current device (taken
+// once per device).  Calls that overlap on one GPU share it and race.
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Decode that builds each token's combined index row itself from the combine step's
 // inputs (top_k + window <= 4096).
 hipError_t launch_attention_topk(const void* q, const uint8_t* cache, int num_pages,

@@ -101,6 +101,27 @@ def test_attention_workspace_contract(dsv4):
     assert call(lib.dsv4_sparse_mla_decode, H=24) == 4
 
 
+def test_noalloc_split_decode_validation(dsv4):
+    """The entry point without a workspace argument refuses a size past its static array
+    (32 MiB) and a bad piece count before launching anything."""
+    lib = dsv4.library()
+    keep, p = _fake()
+
+    def call(**kw):
+        a = dict(T=2, H=16, splits=4, stride=128)
+        a.update(kw)
+        return lib.dsv4_sparse_mla_decode_split_noalloc(
+            p, p, 4, 64, p, a["stride"], p, None, 0.04, p, None, a["T"], a["H"], a["splits"],
+            None)
+
+    assert dsv4.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert lib.dsv4_sparse_mla_split_workspace_bytes(64, 128, 8) > dsv4.NOALLOC_SCRATCH_BYTES
+    assert call(T=64, H=128, splits=8) == 5 and b"static scratch" in lib.dsv4_last_error()
+    assert call(splits=0) == 2 and call(splits=65) == 2
+    assert call(H=24) == 4
+    assert call(T=0) == 0
+
+
 def test_split_decode_validation(dsv4):
     lib = dsv4.library()
     keep, p = _fake()
