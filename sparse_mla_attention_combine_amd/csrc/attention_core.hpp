@@ -1,0 +1,632 @@
+// Helpers of the gfx950 sparse MLA attention kernel (attention.hip): the LDS layout, the
+// gather of a chunk's records, the FP8 dequantisation into MFMA fragments and the value
+// tile, the online-softmax pieces, the P.V fragments, and the combine step built into a
+// workgroup's prologue (written for any thread count and any LDS layout with an index
+// block and request fields).  See attention.hip for the arithmetic they implement and
+// the pages it follows.
+#pragma once
+#include "device.hpp"
+#include "insert_rows.hpp"
+#include "launch.hpp"
+
+namespace dsv4 {
+
+constexpr int kChunk = 64;
+constexpr int kVStride = 512;  // bf16 per LDS value row (1024 B, 16 B units XOR-swizzled)
+constexpr int kPStride = 72;   // bf16 per LDS probability row: 144 B
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+constexpr int kIdxBlock = 4096;  // index entries staged in LDS at a time (64 chunks)
+
+template <int NHB>
+struct AttnSmem {
+  __bf16 v[2][kChunk][kVStride];
+  __bf16 p[2][16 * NHB][kPStride];
+  float red[2][4][16 * NHB];
+  float lsum[4][16 * NHB];
+  int32_t idx[kIdxBlock];
+  int req[4];  // fused combine: request of the token, its first token, its query count, its length
+};
+
+// Inputs of the combine step when the decode builds its index rows itself (the
+// arguments of dsv4_combine_indices; the page geometry comes with the cache).
+struct TopkIn {
+  const int32_t* topk;
+  int topk_stride;
+  int topk_width;
+  const int32_t* topk_lens;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int bt_stride;
+  int B;
+  int top_k;
+  int window;
+};
+
+// Inputs of the insert step when the decode performs it too (the arguments of
+// dsv4_kv_insert): q is normalised in place and the new latent rows go into the cache,
+// which the decode then reads through `cache`.
+struct StepIn {
+  uint16_t* q;
+  const uint16_t* kv;
+  const int64_t* positions;
+  const int64_t* slot_mapping;
+  const float* cos_sin;
+  int max_pos;
+  const uint16_t* weight;
+  float eps;
+  uint8_t* cache;
+};
+
+// Source of the (all-zero) record read for an invalid or absent slot, so that every
+// lane issues the same loads every chunk: branch-free loads let the compiler wait for
+// exactly the chunk it is about to use while later chunks stay in flight.
+static __device__ __attribute__((aligned(64))) uint8_t g_zero_page[kMaxPage * kRecord];
+
+// The cache as the kernels see it: base pointer, number of slots, log2 of the page size.
+struct CacheRef {
+  const uint8_t* base;
+  int64_t num_slots;
+  int ps;
+};
+
+struct RawSlot {
+  uint4 nope[8];  // 128 codes: dims 64u + 16g .. 64u + 16g + 15 for u = 0..7
+  uint4 rope[2];  // rope dims 8g..8g+7 and 32+8g..32+8g+7 (bf16)
+  uint2 sc;       // the slot's 8 scale bytes
+  int valid;
+};
+
+__device__ __forceinline__ void load_raw_slot(RawSlot& r, const CacheRef& c, int64_t slot, int g) {
+  r.valid = (slot >= 0 && slot < c.num_slots) ? 1 : 0;
+  const uint8_t* base = r.valid ? c.base + page_base(slot >> c.ps, c.ps) : g_zero_page;
+  const int off = r.valid ? (int)(slot & ((1 << c.ps) - 1)) : 0;
+  const uint8_t* np = base + nope_off(off) + 16 * g;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) r.nope[u] = *reinterpret_cast<const uint4*>(np + 64 * u);
+  const uint8_t* rp = base + rope_off(off, c.ps) + 16 * g;
+  r.rope[0] = *reinterpret_cast<const uint4*>(rp);
+  r.rope[1] = *reinterpret_cast<const uint4*>(rp + 64);
+  r.sc = *reinterpret_cast<const uint2*>(base + scale_off(off, c.ps));
+}
+
+// Entry jj of the staged index block (-1 past its end).  The read is unconditional (at a
+// clamped index) and the value selected afterwards, so no branch surrounds it.
+__device__ __forceinline__ int64_t idx_at(const int32_t* idx_lds, int jj, int n_blk) {
+  const int32_t v = idx_lds[min(jj, kIdxBlock - 1)];
+  return jj < n_blk ? (int64_t)v : -1;
+}
+
+// Entries [0, n_win) of an index block, this thread's share, all requested before the
+// first wait (one memory latency per block instead of one per NT entries); then written
+// into LDS.  In two parts so that other loads can be issued in between.  NT = threads of
+// the workgroup.
+template <int NT = 256>
+__device__ __forceinline__ void stage_idx_load(int32_t (&v)[kIdxBlock / NT],
+                                               const int32_t* __restrict__ src, int n_win,
+                                               int tid) {
+#pragma unroll
+  for (int k = 0; k < kIdxBlock / NT; ++k)
+    if (NT * k < n_win) v[k] = src[min(tid + NT * k, n_win - 1)];
+}
+template <int NT = 256>
+__device__ __forceinline__ void stage_idx_store(int32_t* dst, const int32_t (&v)[kIdxBlock / NT],
+                                                int n_win, int tid) {
+#pragma unroll
+  for (int k = 0; k < kIdxBlock / NT; ++k)
+    if (tid + NT * k < n_win) dst[tid + NT * k] = v[k];
+}
+constexpr int kStagePer = kIdxBlock / 256;
+
+// The combine step for token t, written straight into the LDS index block (the rules of
+// combine_kernel: valid top-k entries outside the window, then the window ascending, each
+// mapped through the request's block table; -1 for the rest).  The top-k row is requested
+// before the token's request is known; returns the row length tk + sw (0 for a token of
+// no request), the same in every thread.  Contains barriers: call from all threads.
+// Every load is unconditional at a clamped, in-bounds address (only uniform conditions
+// skip one) and its value is selected afterwards: a load under a per-lane condition is
+// waited for on the spot, which would serialise them.
+// In two parts: combine_request issues the top-k row loads and finds the token's request
+// (sm.req); combine_rows, after whatever the caller does in between (loads issued there
+// overlap the block-table loads), builds the row.
+constexpr int kCombPer = kIdxBlock / 256;
+
+template <int NT = 256, class SM>
+__device__ __forceinline__ void combine_request(SM& sm, const TopkIn& c, int64_t t,
+                                                int tid, int32_t (&xv)[kIdxBlock / NT], int& tl) {
+  constexpr int kPer = kIdxBlock / NT;
+  const int kmax = min(c.top_k, c.topk_width);
+  const int32_t* trow = c.topk + t * c.topk_stride;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    xv[u] = NT * u < kmax ? trow[min(tid + NT * u, kmax - 1)] : -1;
+  tl = c.topk_lens ? c.topk_lens[t] : c.top_k;
+  if (tid == 0) sm.req[0] = -1;
+  __syncthreads();
+  const int base = c.qsl[0];
+  // thread r tests request r and brings its length along, so the token's position is
+  // known right after one round of loads
+  for (int r = tid; r < c.B; r += NT) {
+    const int lo = c.qsl[r] - base, hi = c.qsl[r + 1] - base;
+    const int L = c.seq_lens[r];
+    if (t >= lo && t < hi) {  // at most one request holds the token
+      sm.req[0] = r;
+      sm.req[1] = lo;
+      sm.req[2] = hi - lo;
+      sm.req[3] = L;
+    }
+  }
+  __syncthreads();
+}
+
+template <int NT = 256, class SM>
+__device__ __forceinline__ int combine_rows(SM& sm, const TopkIn& c, int64_t t, int ps,
+                                           int tid, const int32_t (&xv)[kIdxBlock / NT], int tl) {
+  constexpr int kPer = kIdxBlock / NT;
+  const int kmax = min(c.top_k, c.topk_width);
+  const int b = sm.req[0];
+  if (b < 0) return 0;
+  const int64_t pos = (int64_t)sm.req[3] - sm.req[2] + (t - sm.req[1]);
+  int64_t tk = min(pos + 1, (int64_t)c.top_k);
+  tk = min(tk, (int64_t)tl);
+  tk = max(tk, (int64_t)0);
+  const int64_t sw = max(min(pos + 1, (int64_t)c.window), (int64_t)0);
+  const int64_t lo = pos - sw + 1;
+  const int32_t* bt_row = c.block_table + (int64_t)b * c.bt_stride;
+  const int n = (int)(tk + sw);
+  int64_t xs[kPer];
+  int32_t pg[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = tid + NT * u;
+    int64_t x = j < tk ? (j < kmax ? (int64_t)xv[u] : -1) : lo + (j - tk);
+    if (j < tk && !(x >= 0 && x < lo)) x = -1;  // invalid, beyond pos, or in the window
+    if (j >= n) x = -1;
+    xs[u] = x;
+    const int64_t lp = x >> ps;
+    pg[u] = (NT * u < n && c.bt_stride > 0)
+                ? bt_row[lp < 0 ? 0 : (lp < c.bt_stride ? lp : c.bt_stride - 1)] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = tid + NT * u;
+    const int64_t x = xs[u];
+    const bool ok = x >= 0 && (x >> ps) < c.bt_stride && pg[u] >= 0;
+    if (j < n) sm.idx[j] = ok ? (int32_t)(((int64_t)pg[u] << ps) + (x & ((1 << ps) - 1))) : -1;
+  }
+  return n;
+}
+
+template <int NT = 256, class SM>
+__device__ __forceinline__ int stage_combined(SM& sm, const TopkIn& c, int64_t t, int ps, int tid) {
+  int32_t xv[kIdxBlock / NT];
+  int tl;
+  combine_request<NT>(sm, c, t, tid, xv, tl);
+  return combine_rows<NT>(sm, c, t, ps, tid, xv, tl);
+}
+
+// Where this lane's pieces of a slot's record live (the zero page for an invalid slot).
+struct RecPtr {
+  const uint8_t* np;  // value codes, already offset by 16g
+  const uint8_t* rp;  // rope, already offset by 16g
+  const uint8_t* sp;  // scale bytes
+  int valid;
+};
+__device__ __forceinline__ RecPtr rec_ptr(const CacheRef& c, int64_t slot, int g) {
+  RecPtr p;
+  p.valid = (slot >= 0 && slot < c.num_slots) ? 1 : 0;
+  const uint8_t* base = p.valid ? c.base + page_base(slot >> c.ps, c.ps) : g_zero_page;
+  const int off = p.valid ? (int)(slot & ((1 << c.ps) - 1)) : 0;
+  p.np = base + nope_off(off) + 16 * g;
+  p.rp = base + rope_off(off, c.ps) + 16 * g;
+  p.sp = base + scale_off(off, c.ps);
+  return p;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(p));
+}
+
+// V tile layout: row j of the chunk occupies 1024 B; its 16 B unit k (value dims
+// 8k..8k+7) is stored at unit k ^ swz(j), swz(j) = 4*(j & 3) + ((j >> 2) & 3).  The four
+// rows that one 16-lane group of a transposing read touches then sit on disjoint banks,
+// and the 16 rows of a wave's 16 B row writes are spread over all of them.
+__device__ __forceinline__ int v_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int v_off(int row, int unit) {  // in bf16 elements
+  return row * kVStride + ((unit ^ v_swz(row)) << 3);
+}
+
+// max / sum with the lane 16 (resp. 32) apart, without going through LDS: the swap
+// hands each lane its partner's value in one of the two results and keeps its own in
+// the other.
+__device__ __forceinline__ float max_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// A probability may exceed 1 by up to 2^kPLimit before the reference max must move:
+// the reference agreed on after a chunk's barrier applies to the next chunk, and a
+// chunk that beats it by more than this is recomputed (fp32/bf16 hold it exactly).
+constexpr float kPLimit = 20.0f;
+// Starting reference: finite, so that masked scores (-inf) give exp2(-inf) = 0 without a
+// test, and below any real score, so the first valid chunk always moves it.
+constexpr float kMFloor = -1.0e30f;
+
+template <int NHB>
+struct AttnState {
+  bf16x8 qf[NHB][18];  // Q^T fragments (registers for the whole kernel)
+  float m_run[NHB];    // reference max per head (log2 domain), same in every wave
+  float l_part[NHB];   // this lane's share of the softmax denominator
+  // O^T, per wave 128 of the 512 output dims:
+  //   NHB == 1: o16[mb] = dims 128w + 16mb + 4g + i, head l16 (16x16 MFMA layout)
+  //   NHB == 2: o32[mb] = dims 128mb + 32w + 8(r/4) + 4(lane/32) + r%4, head lane%32
+  f32x4 o16[8];
+  f32x16 o32[4];
+};
+
+// Dequantise this lane's slot of a chunk (row 16w + l16, k-group g), stage its value
+// dims as bf16 into `vtile` and return S^T fragments: sacc[hb][i] = q.k of chunk row
+// 16w + 4g + i and head 16hb + l16.  Two accumulator chains per head block.
+template <int NHB>
+__device__ __forceinline__ void stage_chunk(__bf16* __restrict__ vtile, const RawSlot& cur,
+                                            const AttnState<NHB>& st, f32x4 (&sacc)[NHB], int w,
+                                            int l16, int g) {
+  f32x4 sa[NHB], sb[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    sa[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sb[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int vr = 16 * w + l16;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t sbyte = ((u < 4 ? cur.sc.x : cur.sc.y) >> (8 * (u & 3))) & 0xFF;
+    const float scale = e8m0_as_scale(sbyte);
+    const bf16x8 k0 = dequant8(cur.nope[u].x, cur.nope[u].y, scale);
+    const bf16x8 k1 = dequant8(cur.nope[u].z, cur.nope[u].w, scale);
+    *reinterpret_cast<bf16x8*>(vtile + v_off(vr, 8 * u + 2 * g)) = k0;
+    *reinterpret_cast<bf16x8*>(vtile + v_off(vr, 8 * u + 2 * g + 1)) = k1;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      sa[hb] = mfma16(k0, st.qf[hb][2 * u], sa[hb]);
+      sb[hb] = mfma16(k1, st.qf[hb][2 * u + 1], sb[hb]);
+    }
+  }
+  const bf16x8 k16 = as_bf16x8(cur.rope[0]);
+  const bf16x8 k17 = as_bf16x8(cur.rope[1]);
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    sa[hb] = mfma16(k16, st.qf[hb][16], sa[hb]);
+    sb[hb] = mfma16(k17, st.qf[hb][17], sb[hb]);
+    sacc[hb] = sa[hb] + sb[hb];
+  }
+}
+
+// O^T[c][h] += V^T[c][j] P^T[j][h] over the 64 rows of a staged chunk, for this wave's
+// 128 output dims.  Transposing reads: input lane 4r+q of a 16-lane group addresses row
+// row0+r, dims col0+4q..col0+4q+3 (16 B unit col0/8 + q/2, half q&1); lane L of the
+// group receives dim col0+L of rows row0..row0+3.
+// NHB == 1: O^T[c][h] += V^T[c][j] P^T[j][h] over the 64 rows of a staged chunk for
+// this wave's 128 output dims, on 16x16x32 MFMA: A = V^T (16 dims x 32 rows), B = P^T
+// (32 rows x 16 heads).  Transposing reads: input lane 4r+q of a 16-lane group addresses
+// row row0+r, dims col0+4q..col0+4q+3; lane L of the group receives dim col0+L of rows
+// row0..row0+3.
+template <int NHB>
+__device__ __forceinline__ void pv_chunk(const __bf16* __restrict__ vtile,
+                                         const __bf16 (*__restrict__ ptile)[kPStride],
+                                         AttnState<NHB>& st, int w, int lane) {
+  static_assert(NHB == 1, "the two-block path uses pv_reads2 / pv_mfma2");
+  const int l16 = lane & 15, G = lane >> 4;
+  const int r = l16 >> 2, q4 = l16 & 3;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8 pf = *reinterpret_cast<const bf16x8*>(&ptile[l16][32 * ks + 8 * G]);
+    const int row0 = 32 * ks + 8 * G + r;
+    bf16x4 t0[8], t1[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const int unit = 16 * w + 2 * mb + (q4 >> 1);
+      t0[mb] = lds_read_tr16(vtile + v_off(row0, unit) + 4 * (q4 & 1));
+      t1[mb] = lds_read_tr16(vtile + v_off(row0 + 4, unit) + 4 * (q4 & 1));
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      bf16x8 vf;
+      vf[0] = t0[mb][0]; vf[1] = t0[mb][1]; vf[2] = t0[mb][2]; vf[3] = t0[mb][3];
+      vf[4] = t1[mb][0]; vf[5] = t1[mb][1]; vf[6] = t1[mb][2]; vf[7] = t1[mb][3];
+      st.o16[mb] = mfma16(vf, pf, st.o16[mb]);
+    }
+  }
+}
+
+// NHB == 2 pieces of a pipelined chunk step.  Output dims of wave w are the 32-dim
+// blocks 128mb + 32w (mb = 0..3), so that in the transposing reads the lane-dependent
+// part of the swizzle lands on the wave's own unit bits and every LDS access of a lane
+// is one base register plus a compile-time constant.
+
+// Staging of one chunk: dequantise this lane's slot (row 16w + l16, k-group g), write its
+// value dims into `vn`, S^T fragments into sacc (two accumulator chains per head block).
+// If REFILL, each piece of `cur` is re-requested for the chunk at `nxt` as soon as it has
+// been converted, so the record loads of a chunk go out one by one across the staging
+// work instead of as one burst: a burst fills the memory pipeline's queue and stalls
+// the wave's in-order issue until it drains.
+template <bool REFILL>
+__device__ __forceinline__ void stage2(__bf16* __restrict__ vn, RawSlot& cur, const RecPtr& nxt,
+                                       const AttnState<2>& st, f32x4 (&sacc)[2], int w,
+                                       int lane) {
+  const int l16 = lane & 15, g = lane >> 4;
+  const int vr = 16 * w + l16;
+  // unit 8u + 2g + h of row vr goes to unit (8u + 2g + h) ^ swz(vr): bit 3 of swz flips
+  // the parity of u, bit 0 flips h, bits 1-2 act on g only.
+  const int sw = v_swz(vr);
+  const int ub = (sw >> 3) & 1;
+  const int c0 = (2 * g) ^ (sw & 6);
+  __bf16* const rowp = vn + vr * kVStride + 8 * c0;
+  __bf16* const wb[2][2] = {{rowp + 64 * ub + 8 * (sw & 1), rowp + 64 * ub + 8 * (1 - (sw & 1))},
+                            {rowp - 64 * ub + 8 * (sw & 1), rowp - 64 * ub + 8 * (1 - (sw & 1))}};
+  f32x4 sa[2], sb[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    sa[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sb[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t sbyte = ((u < 4 ? cur.sc.x : cur.sc.y) >> (8 * (u & 3))) & 0xFF;
+    const float scale = e8m0_as_scale(sbyte);
+    const bf16x8 k0 = dequant8(cur.nope[u].x, cur.nope[u].y, scale);
+    const bf16x8 k1 = dequant8(cur.nope[u].z, cur.nope[u].w, scale);
+    if constexpr (REFILL) cur.nope[u] = *reinterpret_cast<const uint4*>(nxt.np + 64 * u);
+    *reinterpret_cast<bf16x8*>(wb[u & 1][0] + 64 * u) = k0;
+    *reinterpret_cast<bf16x8*>(wb[u & 1][1] + 64 * u) = k1;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      sa[hb] = mfma16(k0, st.qf[hb][2 * u], sa[hb]);
+      sb[hb] = mfma16(k1, st.qf[hb][2 * u + 1], sb[hb]);
+    }
+  }
+  const bf16x8 k16 = as_bf16x8(cur.rope[0]);
+  const bf16x8 k17 = as_bf16x8(cur.rope[1]);
+  if constexpr (REFILL) {
+    cur.rope[0] = *reinterpret_cast<const uint4*>(nxt.rp);
+    cur.rope[1] = *reinterpret_cast<const uint4*>(nxt.rp + 64);
+    cur.sc = *reinterpret_cast<const uint2*>(nxt.sp);
+    cur.valid = nxt.valid;
+  }
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    sa[hb] = mfma16(k16, st.qf[hb][16], sa[hb]);
+    sb[hb] = mfma16(k17, st.qf[hb][17], sb[hb]);
+    sacc[hb] = sa[hb] + sb[hb];
+  }
+}
+
+// P.V operands of a staged chunk.  32x32x16 MFMA: A = V^T (32 dims x 16 rows), lane L
+// holding dim L%32 of rows 8(L/32)..+7; B = P^T, lane L holding head L%32 of the same rows.
+// Transposing read: input lane 4r+q of a 16-lane group addresses row row0+r, dims
+// col0+4q..+3 (unit col0/8 + q/2, half q&1); lane L of the group receives dim col0+L of
+// rows row0..row0+3.  Row 16ks + 8hi + r (+4) has swz 4r + 2hi (+1).
+struct PvFrags {
+  bf16x8 pf[4];
+  bf16x4 t0[4][4], t1[4][4];
+};
+__device__ __forceinline__ void pv_reads2(const __bf16* __restrict__ vt,
+                                          const __bf16 (*__restrict__ pt)[kPStride], PvFrags& f,
+                                          int w, int lane) {
+  const int l16 = lane & 15, G = lane >> 4, hi = lane >> 5;
+  const int r = l16 >> 2, q4 = l16 & 3;
+  const int lo = 2 * (G & 1) + (q4 >> 1);  // unit bits 0-1 before the swizzle
+  const __bf16* const rb0 =
+      vt + (8 * hi + r) * kVStride + 8 * (4 * (w ^ r) + (lo ^ (2 * hi))) + 4 * (q4 & 1);
+  const __bf16* const rb1 =
+      vt + (8 * hi + r + 4) * kVStride + 8 * (4 * (w ^ r) + (lo ^ (2 * hi + 1))) + 4 * (q4 & 1);
+  const __bf16* const pb = &pt[lane & 31][8 * hi];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    f.pf[ks] = *reinterpret_cast<const bf16x8*>(pb + 16 * ks);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      f.t0[ks][mb] = lds_read_tr16(rb0 + 16 * ks * kVStride + 128 * mb);
+      f.t1[ks][mb] = lds_read_tr16(rb1 + 16 * ks * kVStride + 128 * mb);
+    }
+  }
+}
+__device__ __forceinline__ void pv_mfma2(const PvFrags& f, AttnState<2>& st) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      bf16x8 vf;
+      vf[0] = f.t0[ks][mb][0]; vf[1] = f.t0[ks][mb][1]; vf[2] = f.t0[ks][mb][2]; vf[3] = f.t0[ks][mb][3];
+      vf[4] = f.t1[ks][mb][0]; vf[5] = f.t1[ks][mb][1]; vf[6] = f.t1[ks][mb][2]; vf[7] = f.t1[ks][mb][3];
+      st.o32[mb] = mfma32(vf, f.pf[ks], st.o32[mb]);
+    }
+}
+
+// Scores of the freshly staged chunk -> s (raw q.k, invalid rows -inf), this wave's
+// per-head maxima (log2 domain) into `red`, probabilities against the current reference into
+// `ptile` (clamped at 2^kPLimit; a chunk that needs more is recomputed after the
+// barrier), and their per-lane sums into psum.
+template <int NHB>
+__device__ __forceinline__ void softmax_local(__bf16 (*__restrict__ ptile)[kPStride],
+                                              float (*__restrict__ red)[16 * NHB],
+                                              const f32x4 (&sacc)[NHB], uint64_t vmask,
+                                              const AttnState<NHB>& st, float scale_log2,
+                                              float (&s)[NHB][4], float (&psum)[NHB], int w,
+                                              int l16, int g) {
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[hb][i] = ((vmask >> (4 * g + i)) & 1) ? sacc[hb][i] : -INFINITY;
+    float mx = fmaxf(fmaxf(s[hb][0], s[hb][1]), fmaxf(s[hb][2], s[hb][3]));
+    mx = max_xor32(max_xor16(mx));
+    // every lane stores (the 4 lanes of a head hold the same value): a lane condition here
+    // would end the basic block, and with it the interleaving of the softmax with the
+    // P.V MFMAs in pipelined_step
+    red[w][16 * hb + l16] = mx * scale_log2;
+    const float nmr = -st.m_run[hb];
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      p[i] = __builtin_amdgcn_exp2f(fminf(__builtin_fmaf(s[hb][i], scale_log2, nmr), kPLimit));
+    psum[hb] = (p[0] + p[1]) + (p[2] + p[3]);
+    *reinterpret_cast<uint2*>(&ptile[16 * hb + l16][16 * w + 4 * g]) =
+        make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+  }
+}
+
+// After the barrier that publishes a chunk's maxima: if any head's chunk max beats the
+// reference by more than kPLimit (always the case for the first chunk with a valid
+// row), every wave moves the reference, rescales O and the denominator, rewrites the
+// chunk's probabilities and meets at one more barrier.  The decision reads the same LDS
+// words in every wave, so the workgroup takes the branch together.
+template <int NHB>
+__device__ __forceinline__ void resolve_chunk(__bf16 (*__restrict__ ptile)[kPStride],
+                                              const float (*__restrict__ red)[16 * NHB],
+                                              AttnState<NHB>& st, const float (&s)[NHB][4],
+                                              float scale_log2, float (&psum)[NHB], int w, int l16,
+                                              int g) {
+  float cm[NHB];
+  bool fix = false;
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    cm[hb] = fmaxf(fmaxf(red[0][16 * hb + l16], red[1][16 * hb + l16]),
+                   fmaxf(red[2][16 * hb + l16], red[3][16 * hb + l16]));
+    fix |= cm[hb] > st.m_run[hb] + kPLimit;
+  }
+  if (__builtin_amdgcn_ballot_w64(fix)) {
+    float alpha[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const float mn = fmaxf(st.m_run[hb], cm[hb]);
+      alpha[hb] = __builtin_amdgcn_exp2f(st.m_run[hb] - mn);
+      st.m_run[hb] = mn;
+      st.l_part[hb] *= alpha[hb];
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p[i] = __builtin_amdgcn_exp2f(fminf(__builtin_fmaf(s[hb][i], scale_log2, -mn), kPLimit));
+      psum[hb] = (p[0] + p[1]) + (p[2] + p[3]);
+      *reinterpret_cast<uint2*>(&ptile[16 * hb + l16][16 * w + 4 * g]) =
+          make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    }
+    if constexpr (NHB == 2) {
+      const float a = (g & 1) ? alpha[1] : alpha[0];  // this lane's head is lane % 32
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) st.o32[mb] *= a;
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) st.o16[mb] *= alpha[0];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) st.l_part[hb] += psum[hb];
+}
+
+// Chunk i's P.V (tiles vt/pt, published by the last barrier) in the same basic block as
+// chunk i+1's staging (raw -> vn, scores), so the matrix cores, the LDS and the VALU
+// work on both at once; then chunk i+1's softmax, the chunk's only barrier, and its
+// reference check.
+template <int NHB>
+__device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnState<NHB>& st,
+                                               RawSlot& raw, int pf_jj, int n_blk,
+                                               const CacheRef& cr, int w, int lane,
+                                               float scale_log2) {
+  const int l16 = lane & 15, g = lane >> 4;
+  const int nb = cb ^ 1;
+  const int64_t next_slot = idx_at(sm.idx, pf_jj, n_blk);  // read early: off the LDS queue
+  f32x4 sacc[NHB];
+  float s[NHB][4], psum[NHB];
+  if constexpr (NHB == 2) {
+    // staging + S first, so the scores are ready by the softmax; the P.V operands are
+    // requested next and consumed last, so their MFMAs run across the barrier.
+    const uint64_t vmask = __ballot(raw.valid);  // bit j (j < 16) = row 16w + j valid
+    const RecPtr nxt = rec_ptr(cr, next_slot, g);
+    stage2<true>(&sm.v[nb][0][0], raw, nxt, st, sacc, w, lane);
+    PvFrags f;
+    pv_reads2(&sm.v[cb][0][0], sm.p[cb], f, w, lane);
+    // With one wave per SIMD the wave issues in order, so left to itself the softmax
+    // (VALU only) and the P.V MFMAs run one after the other.  Scheduled as one MFMA then
+    // up to eight VALU operations, sixteen times, each P.V MFMA runs on the matrix core
+    // while the next softmax operations issue (plain decode 64.3 -> 61.4 us, step 72.9
+    // -> 70.8 us; 4, 5 and 6 VALU a group measured within 0.6 us of it).  The
+    // scheduling barrier keeps the staging, whose own MFMAs and conversions are already
+    // interleaved, out of that pattern.
+    __builtin_amdgcn_sched_barrier(0);
+    softmax_local<NHB>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
+    pv_mfma2(f, st);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one P.V MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then up to eight VALU
+    }
+  } else {
+    stage_chunk<NHB>(&sm.v[nb][0][0], raw, st, sacc, w, l16, g);
+    pv_chunk<NHB>(&sm.v[cb][0][0], sm.p[cb], st, w, lane);
+    const uint64_t vmask = __ballot(raw.valid);
+    load_raw_slot(raw, cr, next_slot, g);
+    softmax_local<NHB>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
+  }
+  __syncthreads();
+  resolve_chunk<NHB>(sm.p[nb], sm.red[nb], st, s, scale_log2, psum, w, l16, g);
+}
+
+static_assert(32 * kLatent <= kChunk * kVStride, "32 q rows fit one value-tile buffer");
+static_assert(32 * (kNope + 8) <= kChunk * kVStride, "32 staged output rows fit one value-tile buffer");
+static_assert(32 * (kNope + 4) * 4 <= 2 * kChunk * kVStride * 2, "32 staged fp32 partial rows fit both value-tile buffers");
+
+// Q^T fragments of one block of 16 heads from q row `qr` (global memory or LDS): lane
+// (head l16, k-group g); k-step s pairs with the K-fragment dims chosen in load_raw
+// (nope: 64u+16g+8h, rope: 32r+8g).
+__device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[18], const uint16_t* qr, int g) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    qf[2 * u] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 64 * u + 16 * g));
+    qf[2 * u + 1] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 64 * u + 16 * g + 8));
+  }
+  qf[16] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kNope + 8 * g));
+  qf[17] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kNope + 32 + 8 * g));
+}
+
+// The block's last chunk: P.V only.
+template <int NHB>
+__device__ __forceinline__ void pv_last(AttnSmem<NHB>& sm, int cb, AttnState<NHB>& st,
+                                        int w, int lane) {
+  if constexpr (NHB == 2) {
+    PvFrags f;
+    pv_reads2(&sm.v[cb][0][0], sm.p[cb], f, w, lane);
+    pv_mfma2(f, st);
+  } else {
+    pv_chunk<NHB>(&sm.v[cb][0][0], sm.p[cb], st, w, lane);
+  }
+}
+
+}  // namespace dsv4
