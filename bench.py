@@ -67,7 +67,10 @@ def measured_traffic(which="fused"):
     sources have changed since the counters were taken.  `which`: the one-launch step,
     the fused combine + decode launch or the plain decode launch."""
     name = {"step": "sparse_mla_decode_step_b64_h128_traffic.json",
-            "fused": "sparse_mla_decode_topk_b64_h128_traffic.json"}.get(
+            "fused": "sparse_mla_decode_topk_b64_h128_traffic.json",
+            "insert": "insert_t4096_h128_traffic.json",
+            "prefill": "sparse_mla_prefill_l8192_h64_traffic.json",
+            "mtp": "sparse_mla_decode_step_mtp_b256x2_h128_traffic.json"}.get(
                 which, "sparse_mla_decode_b64_h128_traffic.json")
     path = os.path.join(HERE, "profiles", name)
     try:
@@ -101,12 +104,24 @@ def parse():
     ap.add_argument("--unfused", action="store_true", help="same as --launches 3")
     ap.add_argument("--page-size", type=int, default=64, choices=[32, 64, 256],
                     help="cache page size of the decode workload (default 64)")
-    ap.add_argument("--workload", choices=["decode", "compressed-prefill", "indexer"],
+    ap.add_argument("--workload",
+                    choices=["decode", "insert", "mtp", "prefill", "compressed-prefill", "indexer"],
                     default="decode",
-                    help="decode (default: the headline decode step) or compressed-prefill (one "
-                         "8192-token sequence over a 4x compressed cache: insert + compressed "
-                         "combine + workspace fill + prefill attention) or indexer (the top-k "
-                         "selection over 64 x 32768 indexer logits, top-k 2048)")
+                    help="decode (default: the headline decode step); insert (the fused q-norm/"
+                         "RoPE/FP8 insert of 4096 tokens x 128 heads); mtp (MTP-style decode: 256 "
+                         "requests x 2 query tokens, contexts U{8192..131072}); prefill (one "
+                         "8192-token sequence, 64 heads: insert + combine + sparse prefill); "
+                         "compressed-prefill (the same over a 4x compressed cache: insert + "
+                         "compressed combine + workspace fill + prefill attention); indexer (the "
+                         "top-k selection over 64 x 32768 indexer logits, top-k 2048)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed replays of the step before the warm-up steps, so that the GPU "
+                         "runs at its sustained clock when timing starts (default 200 ms; 0 = off)")
+    ap.add_argument("--reps", type=int, default=5,
+                    help="repetitions of the K timed steps for the median (the first is the "
+                         "reported value; default 5)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the cache-flushed pass (512 MB written between steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device-to-device copy 3 times (the known-size "
                          "kernel that scales FETCH_SIZE / WRITE_SIZE counter readings)")
@@ -136,6 +151,12 @@ def main():
         return bench_compressed_prefill(args, torch, dsv4)
     if args.workload == "indexer":
         return bench_indexer(args, torch, dsv4)
+    if args.workload == "insert":
+        return bench_insert(args, torch, dsv4)
+    if args.workload == "mtp":
+        return bench_mtp(args, torch, dsv4)
+    if args.workload == "prefill":
+        return bench_prefill(args, torch, dsv4)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -310,24 +331,44 @@ def main():
             run_step(ins, comb, dec, fu, one,
                      ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
+    settle(args, torch, rotation.replay)
     for i in range(args.warmup):
         graphs[i % n_inst].replay()
     rotation.replay()
     torch.cuda.synchronize()
 
     # timed region: K steps as graph replays (whole rotations, then single steps)
-    t_start = time.perf_counter()
-    for _ in range(args.steps // n_inst):
-        rotation.replay()
-    for k in range(args.steps - args.steps % n_inst, args.steps):
-        graphs[k % n_inst].replay()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    def timed_steps():
+        t0_ = time.perf_counter()
+        for _ in range(args.steps // n_inst):
+            rotation.replay()
+        for k in range(args.steps - args.steps % n_inst, args.steps):
+            graphs[k % n_inst].replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0_
+
+    elapsed = timed_steps()
+    reps = [elapsed] + [timed_steps() for _ in range(max(args.reps, 1) - 1)]
 
     # per-kernel times (not part of the timed region): eager steps with events
     for k in range(args.steps):
         step(k, timed_idx=k)
     torch.cuda.synchronize()
+
+    # cache-flushed variant: 512 MB written between steps (not timed), each step timed alone
+    flushed_us = None
+    if not args.no_flush:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for k in range(args.steps):
+            scratch.fill_(k & 0xFF)
+            fe[k][0].record(stream)
+            run_step(*calls[k % n_inst])
+            fe[k][1].record(stream)
+        torch.cuda.synchronize()
+        flushed_us = float(np.mean([a.elapsed_time(b) for a, b in fe])) * 1e3
+        del scratch
 
     ins_ms = np.array([ev[6 * k].elapsed_time(ev[6 * k + 1]) for k in range(args.steps)])
     comb_ms = np.array([ev[6 * k + 2].elapsed_time(ev[6 * k + 3]) for k in range(args.steps)])
@@ -409,6 +450,10 @@ def main():
             "alg_flops": flops, "alg_bytes": bytes_alg,
             "hbm_frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
         },
+        "reps_ms_per_step": [round(r / args.steps * 1e3, 5) for r in reps],
+        "median_ms_per_step": round(float(np.median(reps)) / args.steps * 1e3, 5),
+        "flushed_us_per_step": None if flushed_us is None else round(flushed_us, 2),
+        "settle_ms": args.settle_ms,
         "kernels_us": ({"sparse_mla_decode_step": round(float(dec_ms.mean()) * 1e3, 2)}
                        if one_launch else
                        {"kv_insert": round(float(ins_ms.mean()) * 1e3, 2),
@@ -613,6 +658,342 @@ def bench_compressed_prefill(args, torch, dsv4):
     print(json.dumps(result), flush=True)
 
 
+def _graph_of(torch, fn):
+    """A HIP graph holding fn's launches (captured on a side stream)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _timed_graph(args, torch, g):
+    """settle, W warm-up replays, then K replays timed (repeated args.reps times); returns
+    the list of elapsed seconds, the first being the reported one."""
+    settle(args, torch, g.replay)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(max(args.reps, 1)):
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        reps.append(time.perf_counter() - t0)
+    return reps
+
+
+def _event_times(torch, launches, steps):
+    """Per-launch durations (us) of an eager pass: `launches` is a list of callables, each
+    one library call; HIP events around each on the current stream."""
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+          for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record(st)
+        for i, f in enumerate(launches):
+            f()
+            ev[k][i + 1].record(st)
+    torch.cuda.synchronize()
+    return np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) * 1e3 for i in range(len(launches))]
+                     for k in range(steps)])
+
+
+def _roofline(flops, nbytes, seconds, kernel, traffic=None):
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    tflops, gbs = flops / seconds / 1e12, nbytes / seconds / 1e9
+    return {"bound": bound,
+            "achieved": round(tflops if bound == "mfma" else gbs, 2),
+            "peak": PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS,
+            "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic, "kernel": kernel, "launch_us": round(seconds * 1e6, 2),
+            "alg_flops": flops, "alg_bytes": nbytes,
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
+def _result(args, metric, value, unit, reps, steps, config, roofline, kernels_us, dtype="bf16"):
+    return {"metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1,
+            "steps": steps, "warmup": args.warmup,
+            "ms_per_step": round(reps[0] / steps * 1e3, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+            "config": config, "roofline": roofline,
+            "reps_ms_per_step": [round(r / steps * 1e3, 5) for r in reps],
+            "median_ms_per_step": round(float(np.median(reps)) / steps * 1e3, 5),
+            "settle_ms": args.settle_ms, "kernels_us": kernels_us}
+
+
+def bench_insert(args, torch, dsv4):
+    """The fused insert at its own configuration: 4096 new tokens of 32 requests, 128 heads
+    (q RMSNorm + GPT-J RoPE in place, the new latent rows quantised into a 2048-page FP8
+    cache at distinct random slots, positions < 131072).  HBM-bound: q read and written
+    once (604 MB each way) dominates."""
+    from synth_inputs import insert_workload
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = insert_workload(seed=args.seed)
+    T, H = wl["T"], wl["H"]
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, kv = bf(wl["q"]), bf(wl["kv"])
+    pos = torch.from_numpy(wl["positions"]).to(dev)
+    slots = torch.from_numpy(wl["slot_mapping"]).to(dev)
+    cs = torch.from_numpy(wl["cos_sin"]).to(dev)
+    w = bf(wl["q_norm_weight"])
+    cache = dsv4.new_cache(wl["num_pages"])
+
+    def step():
+        dsv4.dsv4_kv_insert(q, kv, pos, slots, cs, w, wl["eps"], cache)
+
+    step()
+    g = _graph_of(torch, step)
+    reps = _timed_graph(args, torch, g)
+    us = _event_times(torch, [step], args.steps)[:, 0]
+    nbytes = 2.0 * T * H * LATENT * 2 + T * (LATENT * 2 + RECORD + 16 + 64 * 4) + LATENT * 2
+    roof = _roofline(0.0, nbytes, float(us.mean()) * 1e-6, "insert_kernel (dsv4_kv_insert)",
+                     measured_traffic("insert"))
+    log(f"[bench] insert {T} tokens x {H} heads: {reps[0] / args.steps * 1e6:.1f} us/step (graph), "
+        f"kernel {us.mean():.1f} us = {nbytes / (us.mean() * 1e-6) / 1e9:.0f} GB/s "
+        f"({roof['frac'] * 100:.1f}% of HBM)")
+    res = _result(args, "fused insert tokens/s + % of HBM roofline (T=4096, H=128)",
+                  T * args.steps / reps[0], "tokens/s", reps, args.steps,
+                  {"workload": "fused q RMSNorm + GPT-J RoPE + FP8/UE8M0 KV insert", "tokens": T,
+                   "requests": wl["requests"], "heads": H, "cache_pages": wl["num_pages"],
+                   "page_size": 64, "max_pos": 131072}, roof,
+                  {"kv_insert": round(float(us.mean()), 2)})
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build()
+        n, el, k = 0, 0.0, 0
+        cache_h = np.zeros(wl["num_pages"] * 64 * RECORD, np.uint8)
+        while el < 10.0 and k + 32 <= T:
+            qs = np.array(wl["q"][k:k + 32], copy=True)
+            t0 = time.perf_counter()
+            oracle.kv_insert(qs, wl["kv"][k:k + 32], wl["positions"][k:k + 32],
+                             wl["slot_mapping"][k:k + 32], wl["cos_sin"], wl["q_norm_weight"],
+                             wl["eps"], cache_h, wl["num_pages"], 64, inplace=True)
+            el += time.perf_counter() - t0
+            n += 32
+            k += 32
+        res["cpu_baseline"] = {"value": round(n / el, 3), "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle", "cpu": cpu_model(),
+                               "sample": f"the first {n} tokens (all {H} heads), fp64, {el:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
+def _compact_cache(wl, idx, lens, tokens):
+    """Host cache holding only the rows that `tokens` reference, renumbered to slots 0..m-1,
+    and their index rows remapped (the attention result does not depend on slot numbers)."""
+    import oracle
+    rows = []
+    for t in tokens:
+        r = idx[t, :lens[t]]
+        rows.append(r[r >= 0])
+    need = np.unique(np.concatenate(rows))
+    new_slot = {int(sl): i for i, sl in enumerate(need)}
+    where = {int(sl): i for i, sl in enumerate(wl["ctx_slot"])}
+    src = np.array([where[int(sl)] for sl in need], np.int64)
+    npg = (len(need) + 63) // 64
+    cache = np.zeros(npg * 64 * RECORD, np.uint8)
+    oracle.kv_insert(np.zeros((len(need), 0, LATENT), np.uint16), wl["ctx_kv"][src],
+                     wl["ctx_pos"][src], np.arange(len(need), dtype=np.int64), wl["cos_sin"],
+                     np.zeros(LATENT, np.uint16), wl["eps"], cache, npg, 64, inplace=True)
+    idx2 = np.full((len(tokens), idx.shape[1]), -1, np.int32)
+    for i, t in enumerate(tokens):
+        for j in range(int(lens[t])):
+            v = int(idx[t, j])
+            idx2[i, j] = new_slot[v] if v >= 0 else -1
+    return cache, npg, idx2
+
+
+def _attention_cpu_baseline(wl, it, idx, lens, H, unit_tokens, budget_s=10.0):
+    """The oracle's attention on groups of query tokens spread evenly over the batch (so
+    that short causal rows and long ones are sampled alike) until ~budget_s of host work,
+    all cores; the rate is scaled by the sample's share of the batch's slot visits."""
+    import oracle
+    oracle.build()
+    cores = len(os.sched_getaffinity(0))
+    T = idx.shape[0]
+    step = max(cores, 8)
+    order = np.random.default_rng(0).permutation(T)
+    n, el, visits = 0, 0.0, 0
+    while el < budget_s and n + step <= T:
+        toks = np.sort(order[n:n + step])
+        cache, npg, idx2 = _compact_cache(wl, idx, lens, toks)
+        t0 = time.perf_counter()
+        oracle.sparse_mla(it["q"][toks], cache, npg, 64, idx2, lens[toks], it["sinks"],
+                          wl["softmax_scale"], nthreads=cores, with_lse=False)
+        el += time.perf_counter() - t0
+        visits += int(lens[toks].sum())
+        n += step
+    # query tokens per second at the batch's mean row length
+    rate = (visits / el) / (float(lens.sum()) / T)
+    return {"value": round(rate, 3), "unit": unit_tokens, "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"the attention of {n} query tokens drawn uniformly from the batch (H={H}, "
+                      f"fp64, all cores; the cache rows they reference renumbered into a compact "
+                      f"cache), {el:.1f} s; tokens/s at the batch's mean row length"}
+
+
+def bench_mtp(args, torch, dsv4):
+    """MTP-style decode: 256 requests x 2 query tokens (speculative), 128 heads, contexts
+    U{8192..131072} (an ~11.6 GB cache in random page order), top-k 2048 causal per token
+    position + a 128-token window, no sinks.  A step is the whole decode step in one launch
+    (q norm/RoPE + the 512 new rows + the combine + attention)."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    wl = attention_workload_mtp(args)
+    it = wl["instances"][0]
+    T, H, W, B = wl["T"], wl["H"], wl["W"], wl["B"]
+    log(f"[bench] MTP workload in {time.time() - t0:.1f}s: T={T} H={H} pages={wl['num_pages']} "
+        f"context rows={wl['ctx_kv'].shape[0]}")
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def dv(a, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).to(dev)
+
+    cache = dsv4.new_cache(wl["num_pages"])
+    cs = dv(wl["cos_sin"], np.float32)
+    dsv4.dsv4_kv_insert(None, bf(wl["ctx_kv"]), dv(wl["ctx_pos"], np.int64),
+                        dv(wl["ctx_slot"], np.int64), cs, None, wl["eps"], cache)
+    qsl, sl, bt = dv(wl["qsl"], np.int32), dv(wl["seq_lens"], np.int32), dv(wl["block_table"], np.int32)
+    qlens = np.diff(wl["qsl"])
+    pos = np.concatenate([np.arange(L - ql, L) for L, ql in zip(wl["seq_lens"], qlens)]).astype(np.int64)
+    req = np.repeat(np.arange(B), qlens)
+    slots = wl["block_table"][req, pos // 64].astype(np.int64) * 64 + pos % 64
+    from synth_inputs import bf16_normal
+    rng = np.random.default_rng(2000 + args.seed)
+    kv_new = bf(bf16_normal(rng, (T, LATENT)))
+    q = bf(it["q"])
+    positions, slot_mapping = dv(pos), dv(slots)
+    w = bf(wl["q_norm_weight"])
+    topk = dv(it["topk"], np.int32)
+    out = torch.empty(T, H, NOPE, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        dsv4.dsv4_sparse_mla_decode_step(q, kv_new, positions, slot_mapping, cs, w, wl["eps"], cache,
+                                         topk, None, qsl, sl, bt, wl["top_k"], wl["window"], None,
+                                         wl["softmax_scale"], out)
+
+    step()
+    g = _graph_of(torch, step)
+    reps = _timed_graph(args, torch, g)
+    us = _event_times(torch, [step], args.steps)[:, 0]
+    # algorithmic work from the combined rows (what the decode attends)
+    comb = torch.full((T, W), -1, dtype=torch.int32, device=dev)
+    lens = torch.zeros(T, dtype=torch.int32, device=dev)
+    dsv4.dsv4_combine_indices(topk, None, qsl, sl, bt, wl["top_k"], wl["window"], comb, lens)
+    c_np, l_np = comb.cpu().numpy(), lens.cpu().numpy()
+    nv = int(((np.arange(W)[None, :] < l_np[:, None]) & (c_np >= 0)).sum())
+    flops = 2.0 * H * (LATENT + NOPE) * nv
+    nbytes = (RECORD * nv + T * H * (LATENT + NOPE) * 2 + 4.0 * l_np.sum() + 4.0 * T +
+              T * H * LATENT * 2 + T * (LATENT * 2 + RECORD + 64 * 4 + 16) + LATENT * 2)
+    roof = _roofline(flops, nbytes, float(us.mean()) * 1e-6,
+                     "sparse_mla_kernel<2, fused combine, insert> (dsv4_sparse_mla_decode_step)",
+                     measured_traffic("mtp"))
+    log(f"[bench] MTP step: {reps[0] / args.steps * 1e6:.1f} us/step (graph), kernel {us.mean():.1f} us, "
+        f"{nv} valid slots, {flops / 1e9:.1f} GFLOP, {nbytes / 1e6:.0f} MB -> "
+        f"{flops / (us.mean() * 1e-6) / 1e12:.0f} TFLOP/s, {nbytes / (us.mean() * 1e-6) / 1e9:.0f} GB/s")
+    res = _result(args, "sparse MLA MTP decode query-tokens/s + % of HBM/MFMA roofline "
+                        "(B=256 x 2 tokens, H=128, k=2048)",
+                  T * args.steps / reps[0], "query-tokens/s", reps, args.steps,
+                  {"workload": "MTP decode step: fused q-norm/RoPE/FP8 insert + top-k/window index "
+                               "combine + sparse MLA, one launch",
+                   "requests": B, "query_tokens": T, "heads": H, "top_k": wl["top_k"],
+                   "window": wl["window"], "context": "U{8192..131072}", "page_size": 64,
+                   "sinks": False, "cache_GB": round(wl["num_pages"] * 64 * RECORD / 1e9, 2)},
+                  roof, {"sparse_mla_decode_step": round(float(us.mean()), 2)})
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = _attention_cpu_baseline(wl, it, c_np, l_np, H, "query-tokens/s")
+    print(json.dumps(res), flush=True)
+
+
+def attention_workload_mtp(args):
+    from synth_inputs import attention_workload
+    return attention_workload(3, seed=args.seed, instances=1)
+
+
+def bench_prefill(args, torch, dsv4):
+    """Sparse prefill of one 8192-token sequence, 64 heads: every query token attends its
+    own causal top-k (min(pos+1, 2048) distinct picks) merged with a 128-token causal
+    window, sinks on, over the FP8 cache the step's own insert fills.  A step: dsv4_kv_insert
+    (q norm/RoPE in place + the 8192 new latent rows) + dsv4_combine_indices +
+    dsv4_sparse_mla_prefill."""
+    from synth_inputs import attention_workload
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    wl = attention_workload(4, seed=args.seed, instances=1)
+    it = wl["instances"][0]
+    T, H, W = wl["T"], wl["H"], wl["W"]
+    log(f"[bench] prefill workload in {time.time() - t0:.1f}s: T={T} H={H} pages={wl['num_pages']}")
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def dv(a, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).to(dev)
+
+    cache = dsv4.new_cache(wl["num_pages"])
+    cs = dv(wl["cos_sin"], np.float32)
+    q, kv = bf(it["q"]), bf(wl["ctx_kv"])
+    positions, slots = dv(wl["ctx_pos"], np.int64), dv(wl["ctx_slot"], np.int64)
+    w = bf(wl["q_norm_weight"])
+    qsl, sl, bt = dv(wl["qsl"], np.int32), dv(wl["seq_lens"], np.int32), dv(wl["block_table"], np.int32)
+    topk = dv(it["topk"], np.int32)
+    sinks = dv(it["sinks"], np.float32)
+    comb = torch.full((T, W), -1, dtype=torch.int32, device=dev)
+    lens = torch.zeros(T, dtype=torch.int32, device=dev)
+    out = torch.empty(T, H, NOPE, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    launches = [
+        lambda: dsv4.dsv4_kv_insert(q, kv, positions, slots, cs, w, wl["eps"], cache),
+        lambda: dsv4.dsv4_combine_indices(topk, None, qsl, sl, bt, wl["top_k"], wl["window"],
+                                          comb, lens),
+        lambda: dsv4.dsv4_sparse_mla_prefill(q, cache, comb, lens, sinks, wl["softmax_scale"], out),
+    ]
+
+    def step():
+        for f in launches:
+            f()
+
+    step()
+    g = _graph_of(torch, step)
+    reps = _timed_graph(args, torch, g)
+    kt = _event_times(torch, launches, args.steps)
+    c_np, l_np = comb.cpu().numpy(), lens.cpu().numpy()
+    nv = int(((np.arange(W)[None, :] < l_np[:, None]) & (c_np >= 0)).sum())
+    attn_s = float(kt[:, 2].mean()) * 1e-6
+    flops = 2.0 * H * (LATENT + NOPE) * nv
+    nbytes = RECORD * T + T * H * (LATENT + NOPE) * 2 + 4.0 * l_np.sum() + 4.0 * T + 4.0 * H
+    roof = _roofline(flops, nbytes, attn_s, "sparse_mla_kernel<2> (dsv4_sparse_mla_prefill)",
+                     measured_traffic("prefill"))
+    log(f"[bench] prefill step: {reps[0] / args.steps * 1e3:.3f} ms/step (graph); insert "
+        f"{kt[:, 0].mean():.1f} us, combine {kt[:, 1].mean():.1f} us, attention {kt[:, 2].mean():.1f} us "
+        f"({nv} slot visits, {flops / 1e12:.3f} TFLOP -> {flops / attn_s / 1e12:.0f} TFLOP/s)")
+    res = _result(args, "sparse MLA prefill query-tokens/s + % of MFMA roofline (L=8192, H=64, k=2048)",
+                  T * args.steps / reps[0], "query-tokens/s", reps, args.steps,
+                  {"workload": "sparse prefill step: fused q-norm/RoPE/FP8 insert + top-k/window "
+                               "index combine + sparse MLA prefill",
+                   "tokens": T, "heads": H, "top_k": wl["top_k"], "window": wl["window"],
+                   "page_size": 64, "sinks": True}, roof,
+                  {"kv_insert": round(float(kt[:, 0].mean()), 2),
+                   "combine_indices": round(float(kt[:, 1].mean()), 2),
+                   "sparse_mla_prefill": round(float(kt[:, 2].mean()), 2)})
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = _attention_cpu_baseline(wl, it, c_np, l_np, H, "query-tokens/s")
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline(wl, d0, calls, H, T, W, PS=64):
     """The CPU oracle (fp64, as it stands) timed on this host on one full step of
     instance 0: insert + combine + attention for all 64 query tokens."""
@@ -654,10 +1035,43 @@ def cpu_baseline(wl, d0, calls, H, T, W, PS=64):
         el += time.perf_counter() - t0
         reps += 1
     log(f"[bench] cpu oracle: {reps} steps ({T} query tokens each) in {el:.2f} s on {cores} threads")
+    # one core: the attention step of the first 4 query tokens (the step's dominant part)
+    n1 = 4
+    idx, lens = oracle.combine(it["topk"], it["topk_lens"], wl["qsl"], wl["seq_lens"],
+                               wl["block_table"], T, wl["top_k"], wl["window"], PS, W)
+    q1 = np.array(it["q"][:n1], copy=True)
+    t0 = time.perf_counter()
+    oracle.sparse_mla(q1, cache, npg, PS, idx[:n1], lens[:n1], it["sinks"], wl["softmax_scale"],
+                      nthreads=1, with_lse=False)
+    el1 = time.perf_counter() - t0
     return {"value": round(T * reps / el, 3), "unit": "query-tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
+            "value_1core": round(n1 / el1, 3),
             "sample": f"{reps} full decode steps of the same workload (instance 0: {T} query "
-                      f"tokens, H={H}; fp64 insert + combine + attention), {el:.1f} s wall"}
+                      f"tokens, H={H}; fp64 insert + combine + attention), {el:.1f} s wall; "
+                      f"1 core: the attention of {n1} query tokens, {el1:.2f} s"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def settle(args, torch, replay):
+    """Untimed replays for about args.settle_ms, so that timing starts at the sustained clock
+    (the decode kernel's duration falls over its first ~40 launches on a fresh process)."""
+    if args.settle_ms <= 0:
+        return
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        replay()
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
