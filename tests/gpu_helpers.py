@@ -71,3 +71,22 @@ def assert_attention_close(got_bits, ref, what, max_abs=1e-2, mean_abs=1e-3, out
     assert np.all(d <= bound), what
     extra = float(np.mean(ulp) / 4) if out_rounding else 0.0
     assert d.mean() <= mean_abs * max(1.0, rms) + extra, (what, d.mean(), extra)
+
+
+def within_rotation_bound(got_bits, ref_bits, rope_dims_last):
+    """|gpu - oracle| <= 1 bf16 ulp of the oracle value + 2^-20 * the norm of the rotated
+    pair it belongs to.  The GPU rotates in fp32 (rounding error ~2^-23 of the pair norm,
+    visible as many ulps when a*c - b*s cancels to a tiny value); the oracle rounds the
+    exact fp64 value once."""
+    g = bits_to_f64(got_bits)
+    r = bits_to_f64(ref_bits)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126))) - 7)
+    tol = ulp.copy()
+    rr = r[..., -rope_dims_last:]
+    pair = np.sqrt(rr[..., 0::2] ** 2 + rr[..., 1::2] ** 2)
+    tol[..., -rope_dims_last:] += np.repeat(pair, 2, axis=-1) * 2.0 ** -20
+    same = got_bits == ref_bits  # includes untouched bytes that happen to encode NaN
+    with np.errstate(invalid="ignore"):
+        d = np.where(same, 0.0, np.abs(g - r))
+    ok = bool(np.all(same | (d <= tol)))
+    return ok, float(np.mean(same)), float(np.nanmax(np.where(same, 0.0, d / tol)))

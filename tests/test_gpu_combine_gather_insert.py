@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from synth_inputs import attention_workload, bf16_normal, insert_workload, rope_table
-from tests.gpu_helpers import bits_to_f64, dev, dev_bf16, host_bits, log, oracle_cache
+from tests.gpu_helpers import dev, dev_bf16, host_bits, log, within_rotation_bound
 
 pytestmark = pytest.mark.gpu
 P = 64
@@ -105,25 +105,6 @@ def _insert_gpu(dsv4, wl, cache0, q=None):
     return (host_bits(qd) if qd is not None else None), cache.cpu().numpy()
 
 
-def _within_rotation_bound(got_bits, ref_bits, rope_dims_last):
-    """|gpu - oracle| <= 1 bf16 ulp of the oracle value + 2^-20 * the norm of the rotated
-    pair it belongs to.  The GPU rotates in fp32 (rounding error ~2^-23 of the pair norm,
-    visible as many ulps when a*c - b*s cancels to a tiny value); the oracle rounds the
-    exact fp64 value once."""
-    g = bits_to_f64(got_bits)
-    r = bits_to_f64(ref_bits)
-    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126))) - 7)
-    tol = ulp.copy()
-    rr = r[..., -rope_dims_last:]
-    pair = np.sqrt(rr[..., 0::2] ** 2 + rr[..., 1::2] ** 2)
-    tol[..., -rope_dims_last:] += np.repeat(pair, 2, axis=-1) * 2.0 ** -20
-    same = got_bits == ref_bits  # includes untouched bytes that happen to encode NaN
-    with np.errstate(invalid="ignore"):
-        d = np.where(same, 0.0, np.abs(g - r))
-    ok = bool(np.all(same | (d <= tol)))
-    return ok, float(np.mean(same)), float(np.nanmax(np.where(same, 0.0, d / tol)))
-
-
 def _compare_insert(q_gpu, cache_gpu, q_ref, cache_ref, num_pages):
     pg_g = cache_gpu.reshape(num_pages, -1)
     pg_r = cache_ref.reshape(num_pages, -1)
@@ -131,12 +112,12 @@ def _compare_insert(q_gpu, cache_gpu, q_ref, cache_ref, num_pages):
     scale_eq = np.array_equal(pg_g[:, P * 640:], pg_r[:, P * 640:])
     rope_g = np.ascontiguousarray(pg_g[:, P * 512:P * 640]).view(np.uint16).reshape(-1, 64)
     rope_r = np.ascontiguousarray(pg_r[:, P * 512:P * 640]).view(np.uint16).reshape(-1, 64)
-    rok, rexact, rworst = _within_rotation_bound(rope_g, rope_r, 64)
+    rok, rexact, rworst = within_rotation_bound(rope_g, rope_r, 64)
     log(f"  cache nope bit-exact={nope_eq} scales bit-exact={scale_eq} rope within bound={rok} "
         f"exact frac={rexact:.6f} worst/bound={rworst:.3f}")
     assert nope_eq and scale_eq and rok
     if q_gpu is not None:
-        qok, qexact, qworst = _within_rotation_bound(q_gpu, q_ref, 64)
+        qok, qexact, qworst = within_rotation_bound(q_gpu, q_ref, 64)
         log(f"  q within bound={qok} exact frac={qexact:.6f} worst/bound={qworst:.3f}")
         assert qok
 

@@ -8,7 +8,8 @@ import torch
 
 import oracle
 from synth_inputs import bf16_normal, rope_table
-from tests.gpu_helpers import assert_attention_close, bits_to_f64, dev, dev_bf16, host_bits, log
+from tests.gpu_helpers import (assert_attention_close, dev, dev_bf16, host_bits, log,
+                               within_rotation_bound)
 
 pytestmark = pytest.mark.gpu
 PAGE_SIZES = [32, 256]
@@ -48,18 +49,16 @@ def test_insert_page_size(dsv4, P):
     torch.cuda.synchronize()
     c_gpu = cache.cpu().numpy().reshape(num_pages, -1)
     c_ref = c_ref.reshape(num_pages, -1)
-    # codes and scale bytes: bit-exact; rope and q: the fp32 rotation may differ from the
-    # oracle's fp64-then-rounded value by one bf16 ulp (plus cancellation, see the P=64 test)
+    # codes and scale bytes: bit-exact; rope and q: one bf16 ulp of the oracle value plus
+    # 2^-20 of the rotated pair's norm (the same bar as the 64-slot insert test)
     assert np.array_equal(c_gpu[:, :P * 512], c_ref[:, :P * 512])
     assert np.array_equal(c_gpu[:, P * 640:], c_ref[:, P * 640:])
-    rg = np.ascontiguousarray(c_gpu[:, P * 512:P * 640]).view(np.uint16)
-    rr = np.ascontiguousarray(c_ref[:, P * 512:P * 640]).view(np.uint16)
-    for got, ref in ((rg, rr), (host_bits(qd), q_ref)):
-        g, r = bits_to_f64(got), bits_to_f64(ref)
-        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126))) - 7)
-        with np.errstate(invalid="ignore"):
-            ok = (got == ref) | (np.abs(g - r) <= 2 * ulp + 1e-6)
-        assert ok.all()
+    rg = np.ascontiguousarray(c_gpu[:, P * 512:P * 640]).view(np.uint16).reshape(-1, 64)
+    rr = np.ascontiguousarray(c_ref[:, P * 512:P * 640]).view(np.uint16).reshape(-1, 64)
+    for what, got, ref in (("rope", rg, rr), ("q", host_bits(qd), q_ref)):
+        ok, exact, worst = within_rotation_bound(got, ref, 64)
+        log(f"  {what} within bound={ok} exact frac={exact:.6f} worst/bound={worst:.3f}")
+        assert ok
 
 
 @pytest.mark.parametrize("P", PAGE_SIZES)
