@@ -21,6 +21,9 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 LATENT, NOPE, ROPE, RECORD = 576, 512, 64, 648
+# kv-cache dtypes: the packed FP8 record with UE8M0 block scales, plain bf16 records,
+# plain E4M3 records with one per-tensor scale
+KV_FP8_DS, KV_BF16, KV_FP8_E4M3 = 0, 1, 2
 
 
 def build(force: bool = False) -> str:
@@ -48,6 +51,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_bf16_to_double.argtypes, L.oracle_bf16_to_double.restype = [ctypes.c_uint16], dbl
         L.oracle_ue8m0_exponent.argtypes, L.oracle_ue8m0_exponent.restype = [dbl], i32
         L.oracle_gather_dequant.argtypes = [vp, i32, i32, vp, i32, vp]
+        L.oracle_gather_dequant_kv.argtypes = [vp, i32, i32, i32, dbl, vp, i32, vp]
+        L.oracle_kv_record_bytes.argtypes, L.oracle_kv_record_bytes.restype = [i32], i32
         L.oracle_combine.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      vp, i32, vp]
         L.oracle_combine_compressed.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32,
@@ -56,11 +61,16 @@ def lib() -> ctypes.CDLL:
                                               i32, i32, i32, vp, i32]
         L.oracle_indexer_topk.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp]
         L.oracle_kv_insert.argtypes = [vp, vp, vp, vp, vp, i32, vp, dbl, vp, i32, i32, i32, i32]
+        L.oracle_kv_insert_kv.argtypes = [vp, vp, vp, vp, vp, i32, vp, dbl, vp, i32, i32, i32, dbl,
+                                          i32, i32]
         L.oracle_sparse_mla.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, dbl, vp, vp, i32, i32,
                                         i32]
-        for f in (L.oracle_gather_dequant, L.oracle_combine, L.oracle_combine_compressed,
-                  L.oracle_gather_workspace, L.oracle_indexer_topk, L.oracle_kv_insert,
-                  L.oracle_sparse_mla):
+        L.oracle_sparse_mla_kv.argtypes = [vp, vp, i32, i32, i32, dbl, vp, i32, vp, vp, dbl, vp, vp,
+                                           i32, i32, i32]
+        for f in (L.oracle_gather_dequant, L.oracle_gather_dequant_kv, L.oracle_combine,
+                  L.oracle_combine_compressed, L.oracle_gather_workspace, L.oracle_indexer_topk,
+                  L.oracle_kv_insert, L.oracle_kv_insert_kv, L.oracle_sparse_mla,
+                  L.oracle_sparse_mla_kv):
             f.restype = None
         _lib = L
     return _lib
@@ -101,11 +111,22 @@ def ue8m0_exponent(amax: float) -> int:
 
 # ---- steps ----------------------------------------------------------------------------
 
-def gather_dequant(cache: np.ndarray, num_pages: int, page_size: int, slots: np.ndarray) -> np.ndarray:
+def kv_record_bytes(kv_dtype: int = KV_FP8_DS) -> int:
+    """Bytes of one slot's record in a cache of ``kv_dtype``."""
+    return lib().oracle_kv_record_bytes(int(kv_dtype))
+
+
+def gather_dequant(cache: np.ndarray, num_pages: int, page_size: int, slots: np.ndarray,
+                   kv_dtype: int = KV_FP8_DS, kv_scale: float = 1.0) -> np.ndarray:
     """bf16 bits [n, 576] of the dequantised records of ``slots`` (zeros when invalid)."""
     slots = _c(slots, np.int32)
     out = np.zeros((slots.shape[0], LATENT), np.uint16)
-    lib().oracle_gather_dequant(_ptr(cache), num_pages, page_size, _ptr(slots), slots.shape[0], _ptr(out))
+    if kv_dtype == KV_FP8_DS:
+        lib().oracle_gather_dequant(_ptr(cache), num_pages, page_size, _ptr(slots), slots.shape[0],
+                                    _ptr(out))
+    else:
+        lib().oracle_gather_dequant_kv(_ptr(cache), num_pages, page_size, int(kv_dtype),
+                                       float(kv_scale), _ptr(slots), slots.shape[0], _ptr(out))
     return out
 
 
@@ -175,7 +196,7 @@ def indexer_topk(logits, qsl, seq_lens, T, ratio, top_k, topk_stride, fill=-7):
 
 
 def kv_insert(q_bits, kv_bits, positions, slot_mapping, cos_sin, weight_bits, eps, cache,
-              num_pages, page_size, inplace=False):
+              num_pages, page_size, inplace=False, kv_dtype=KV_FP8_DS, kv_scale=1.0):
     """Returns (q_out_bits, cache_out); works on copies unless ``inplace`` (then q_bits and
     cache must be C-contiguous uint16 / uint8 arrays and are updated)."""
     if inplace:
@@ -190,13 +211,18 @@ def kv_insert(q_bits, kv_bits, positions, slot_mapping, cos_sin, weight_bits, ep
     cs = _c(cos_sin, np.float32)
     w = _c(weight_bits, np.uint16)
     T, H = q.shape[0], q.shape[1]
-    lib().oracle_kv_insert(_ptr(q), _ptr(kv), _ptr(pos), _ptr(sm), _ptr(cs), cs.shape[0], _ptr(w),
-                           float(eps), _ptr(c), num_pages, page_size, T, H)
+    if kv_dtype == KV_FP8_DS:
+        lib().oracle_kv_insert(_ptr(q), _ptr(kv), _ptr(pos), _ptr(sm), _ptr(cs), cs.shape[0],
+                               _ptr(w), float(eps), _ptr(c), num_pages, page_size, T, H)
+    else:
+        lib().oracle_kv_insert_kv(_ptr(q), _ptr(kv), _ptr(pos), _ptr(sm), _ptr(cs), cs.shape[0],
+                                  _ptr(w), float(eps), _ptr(c), num_pages, page_size,
+                                  int(kv_dtype), float(kv_scale), T, H)
     return q, c
 
 
 def sparse_mla(q_bits, cache, num_pages, page_size, indices, lens, sinks, scale, nthreads=1,
-               with_lse=True):
+               with_lse=True, kv_dtype=KV_FP8_DS, kv_scale=1.0):
     """fp64 outputs ``[T, H, 512]`` and lse ``[T, H]`` (or None)."""
     q = _c(q_bits, np.uint16)
     idx = _c(indices, np.int32)
@@ -205,7 +231,12 @@ def sparse_mla(q_bits, cache, num_pages, page_size, indices, lens, sinks, scale,
     T, H = q.shape[0], q.shape[1]
     out = np.zeros((T, H, NOPE), np.float64)
     lse = np.zeros((T, H), np.float64) if with_lse else None
-    lib().oracle_sparse_mla(_ptr(q), _ptr(cache), num_pages, page_size, _ptr(idx), idx.shape[1],
-                            _ptr(ln), _ptr(sk), float(scale), _ptr(out), _ptr(lse), T, H,
-                            int(nthreads))
+    if kv_dtype == KV_FP8_DS:
+        lib().oracle_sparse_mla(_ptr(q), _ptr(cache), num_pages, page_size, _ptr(idx),
+                                idx.shape[1], _ptr(ln), _ptr(sk), float(scale), _ptr(out),
+                                _ptr(lse), T, H, int(nthreads))
+    else:
+        lib().oracle_sparse_mla_kv(_ptr(q), _ptr(cache), num_pages, page_size, int(kv_dtype),
+                                   float(kv_scale), _ptr(idx), idx.shape[1], _ptr(ln), _ptr(sk),
+                                   float(scale), _ptr(out), _ptr(lse), T, H, int(nthreads))
     return out, lse

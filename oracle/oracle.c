@@ -16,7 +16,8 @@
  *   [p3] PR #43385 "[ROCm][DSv4][Perf] Support DeepSeek v4 MTP" — Key source excerpts
  *        (rocm.py _combine_topk_swa_indices_kernel).
  *   [p4] PR #43477 "Enable DeepSeek V4 and GLM-5.1 on SM120" — Key source excerpts
- *        (flashinfer_mla_sparse_sm120.py forward_mqa; flashinfer_sparse.py supports_sink).
+ *        (flashinfer_mla_sparse_sm120.py forward_mqa; flashinfer_sparse.py supports_sink;
+ *        flashinfer_mla_sparse.py supported_kv_cache_dtypes; get_kv_cache_shape).
  *
  * Readings taken where the pages are silent are listed beside each function.
  * Every function here is pinned by the CPU test suite against closed forms, library
@@ -163,13 +164,68 @@ static int dequant_slot(const uint8_t* cache, int num_pages, int P, int64_t slot
   return 1;
 }
 
-void oracle_gather_dequant(const uint8_t* cache, int num_pages, int P, const int32_t* slots,
-                           int n, uint16_t* out_bf16 /* [n][576] */) {
+/* ------------------------------------------------------------------------------- */
+/* The other kv-cache dtypes [p4 Key source excerpts: the SM100 backend lists "auto",   */
+/* "float16", "bfloat16", "fp8" and "fp8_e4m3" as kv-cache dtypes (block sizes 32, 64)  */
+/* and get_kv_cache_shape gives it a cache of shape (num_blocks, block_size,           */
+/* head_size); the SM120 backend takes "fp8_ds_mla", the packed record above].          */
+/* Readings: a slot of such a cache is one record of the 576 latent values in dim       */
+/* order (head_size = 512 + 64), the records of a page back to back, so slot s starts   */
+/* at byte s * record_bytes.                                                            */
+/*   bf16: 1152 B, the values' bf16 bits (little-endian); value = that bf16 number.     */
+/*   fp8:  576 B of OCP E4M3 codes and one fp32 scale s for the whole cache (per        */
+/*         tensor); value = e4m3(code) * s.                                             */
+/* ------------------------------------------------------------------------------- */
+
+#define KV_FP8_DS 0
+#define KV_BF16 1
+#define KV_FP8_E4M3 2
+
+int oracle_kv_record_bytes(int kv_dtype) {
+  switch (kv_dtype) {
+    case KV_FP8_DS: return RECORD;
+    case KV_BF16: return LATENT * 2;
+    case KV_FP8_E4M3: return LATENT;
+    default: return 0;
+  }
+}
+
+typedef struct {
+  const uint8_t* cache;
+  int num_pages, P, dtype;
+  double scale; /* fp8 (per tensor) only */
+} kv_view;
+
+/* One slot's 576 values as fp64 (zeros and 0 for an invalid slot). */
+static int read_slot(const kv_view* kv, int64_t slot, double* out) {
+  if (kv->dtype == KV_FP8_DS) return dequant_slot(kv->cache, kv->num_pages, kv->P, slot, out);
+  if (slot < 0 || slot >= (int64_t)kv->num_pages * kv->P) {
+    for (int d = 0; d < LATENT; ++d) out[d] = 0.0;
+    return 0;
+  }
+  const uint8_t* rec = kv->cache + slot * oracle_kv_record_bytes(kv->dtype);
+  for (int d = 0; d < LATENT; ++d)
+    out[d] = kv->dtype == KV_BF16 ? oracle_bf16_to_double(load_u16(rec + 2 * d))
+                                  : oracle_e4m3_decode(rec[d]) * kv->scale;
+  return 1;
+}
+
+/* The gather step's output: each slot's values rounded once to bf16 (exact for the
+ * packed and bf16 caches; for fp8 the exact product code * s rounded once). */
+void oracle_gather_dequant_kv(const uint8_t* cache, int num_pages, int P, int kv_dtype,
+                              double kv_scale, const int32_t* slots, int n,
+                              uint16_t* out_bf16 /* [n][576] */) {
+  const kv_view kv = {cache, num_pages, P, kv_dtype, kv_scale};
   double row[LATENT];
   for (int i = 0; i < n; ++i) {
-    dequant_slot(cache, num_pages, P, slots[i], row);
+    read_slot(&kv, slots[i], row);
     for (int d = 0; d < LATENT; ++d) out_bf16[(int64_t)i * LATENT + d] = oracle_bf16_from_double(row[d]);
   }
+}
+
+void oracle_gather_dequant(const uint8_t* cache, int num_pages, int P, const int32_t* slots,
+                           int n, uint16_t* out_bf16 /* [n][576] */) {
+  oracle_gather_dequant_kv(cache, num_pages, P, KV_FP8_DS, 1.0, slots, n, out_bf16);
 }
 
 /* ------------------------------------------------------------------------------- */
@@ -401,10 +457,15 @@ void oracle_indexer_topk(const float* logits, int logits_stride, const int32_t* 
 /* untouched; slot outside [0, num_pages*P): cache write skipped.                      */
 /* ------------------------------------------------------------------------------- */
 
-void oracle_kv_insert(uint16_t* q, const uint16_t* kv, const int64_t* positions,
-                      const int64_t* slot_mapping, const float* cos_sin, int max_pos,
-                      const uint16_t* weight, double eps, uint8_t* cache, int num_pages, int P,
-                      int T, int H) {
+/* The cache write for the bf16 and fp8 dtypes [p4, as above]: the rope dims rotated and
+ * rounded to bf16 as for the packed record (what the RoPE step hands on); bf16 stores
+ * every value's bits; fp8 stores e4m3(z / s) for every dim z, the quotient rounded to
+ * fp32 first (reading: the pages give no quantiser; both this and the GPU take the
+ * rounding decision on the fp32 quotient), round-to-nearest-even, saturated to +-448. */
+void oracle_kv_insert_kv(uint16_t* q, const uint16_t* kv, const int64_t* positions,
+                         const int64_t* slot_mapping, const float* cos_sin, int max_pos,
+                         const uint16_t* weight, double eps, uint8_t* cache, int num_pages, int P,
+                         int kv_dtype, double kv_scale, int T, int H) {
   double x[LATENT], y[LATENT], c[ROPE / 2], s[ROPE / 2];
   for (int64_t t = 0; t < T; ++t) {
     int64_t p = positions[t];
@@ -433,6 +494,23 @@ void oracle_kv_insert(uint16_t* q, const uint16_t* kv, const int64_t* positions,
     if (slot < 0 || slot >= (int64_t)num_pages * P) continue;
     const uint16_t* kt = kv + t * LATENT;
     for (int d = 0; d < LATENT; ++d) x[d] = oracle_bf16_to_double(kt[d]);
+    if (kv_dtype != KV_FP8_DS) {
+      double z[LATENT];
+      for (int d = 0; d < NOPE; ++d) z[d] = x[d];
+      for (int i = 0; i < ROPE / 2; ++i) {
+        double a = x[NOPE + 2 * i], b = x[NOPE + 2 * i + 1];
+        z[NOPE + 2 * i] = oracle_bf16_to_double(oracle_bf16_from_double(a * c[i] - b * s[i]));
+        z[NOPE + 2 * i + 1] = oracle_bf16_to_double(oracle_bf16_from_double(a * s[i] + b * c[i]));
+      }
+      uint8_t* rec = cache + slot * oracle_kv_record_bytes(kv_dtype);
+      for (int d = 0; d < LATENT; ++d) {
+        if (kv_dtype == KV_BF16)
+          store_u16(rec + 2 * d, oracle_bf16_from_double(z[d]));
+        else
+          rec[d] = (uint8_t)oracle_e4m3_encode((double)(float)(z[d] / kv_scale));
+      }
+      continue;
+    }
     uint8_t* rope = (uint8_t*)rec_rope(cache, P, slot);
     for (int i = 0; i < ROPE / 2; ++i) {
       double a = x[NOPE + 2 * i], b = x[NOPE + 2 * i + 1];
@@ -455,6 +533,14 @@ void oracle_kv_insert(uint16_t* q, const uint16_t* kv, const int64_t* positions,
   }
 }
 
+void oracle_kv_insert(uint16_t* q, const uint16_t* kv, const int64_t* positions,
+                      const int64_t* slot_mapping, const float* cos_sin, int max_pos,
+                      const uint16_t* weight, double eps, uint8_t* cache, int num_pages, int P,
+                      int T, int H) {
+  oracle_kv_insert_kv(q, kv, positions, slot_mapping, cos_sin, max_pos, weight, eps, cache,
+                      num_pages, P, KV_FP8_DS, 1.0, T, H);
+}
+
 /* ------------------------------------------------------------------------------- */
 /* Steps 2+3 (sparse attention over the listed slots) — the plain definition:        */
 /* softmax attention of each head over the valid listed slots, value = first 512 dims, */
@@ -467,8 +553,7 @@ void oracle_kv_insert(uint16_t* q, const uint16_t* kv, const int64_t* positions,
 
 typedef struct {
   const uint16_t* q;
-  const uint8_t* cache;
-  int num_pages, P;
+  kv_view kv;
   const int32_t* idx;
   int idx_stride;
   const int32_t* lens;
@@ -487,7 +572,7 @@ static void attend_token(const attn_job* jb, int t, double* K, double* sc) {
   int n = 0;
   for (int j = 0; j < L; ++j) {
     int64_t slot = jb->idx[(int64_t)t * jb->idx_stride + j];
-    if (dequant_slot(jb->cache, jb->num_pages, jb->P, slot, K + (int64_t)n * LATENT)) ++n;
+    if (read_slot(&jb->kv, slot, K + (int64_t)n * LATENT)) ++n;
   }
   for (int h = 0; h < jb->H; ++h) {
     const uint16_t* qh = jb->q + ((int64_t)t * jb->H + h) * LATENT;
@@ -533,10 +618,12 @@ static void* attn_worker(void* arg) {
 
 /* out fp64 [T][H][512], lse fp64 [T][H] or NULL.  nthreads <= 1 runs on the caller's
  * thread; otherwise query tokens are split into contiguous ranges, one per thread. */
-void oracle_sparse_mla(const uint16_t* q, const uint8_t* cache, int num_pages, int P,
-                       const int32_t* idx, int idx_stride, const int32_t* lens, const float* sinks,
-                       double scale, double* out, double* lse, int T, int H, int nthreads) {
-  attn_job base = {q, cache, num_pages, P, idx, idx_stride, lens, sinks, scale, out, lse, T, H, 0, T};
+void oracle_sparse_mla_kv(const uint16_t* q, const uint8_t* cache, int num_pages, int P,
+                          int kv_dtype, double kv_scale, const int32_t* idx, int idx_stride,
+                          const int32_t* lens, const float* sinks, double scale, double* out,
+                          double* lse, int T, int H, int nthreads) {
+  attn_job base = {q, {cache, num_pages, P, kv_dtype, kv_scale}, idx, idx_stride, lens, sinks,
+                   scale, out, lse, T, H, 0, T};
   if (nthreads <= 1 || T <= 1) {
     attn_worker(&base);
     return;
@@ -553,4 +640,11 @@ void oracle_sparse_mla(const uint16_t* q, const uint8_t* cache, int num_pages, i
   for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
   free(th);
   free(jobs);
+}
+
+void oracle_sparse_mla(const uint16_t* q, const uint8_t* cache, int num_pages, int P,
+                       const int32_t* idx, int idx_stride, const int32_t* lens, const float* sinks,
+                       double scale, double* out, double* lse, int T, int H, int nthreads) {
+  oracle_sparse_mla_kv(q, cache, num_pages, P, KV_FP8_DS, 1.0, idx, idx_stride, lens, sinks,
+                       scale, out, lse, T, H, nthreads);
 }
