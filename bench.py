@@ -38,6 +38,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 METRIC = "sparse MLA decode query-tokens/s + % of HBM/MFMA roofline (B=64,H=128,k=2048)"
+KV_DTYPES = {"fp8_ds_mla": 0, "bf16": 1, "fp8_e4m3": 2}
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (spec)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (spec)
 LATENT, NOPE, RECORD = 576, 512, 648
@@ -68,10 +69,14 @@ def measured_traffic(which="fused"):
     the fused combine + decode launch or the plain decode launch."""
     name = {"step": "sparse_mla_decode_step_b64_h128_traffic.json",
             "fused": "sparse_mla_decode_topk_b64_h128_traffic.json",
+            "decode": "sparse_mla_decode_b64_h128_traffic.json",
+            "step_bf16": "sparse_mla_decode_step_b64_h128_bf16_traffic.json",
+            "step_fp8_e4m3": "sparse_mla_decode_step_b64_h128_fp8_e4m3_traffic.json",
             "insert": "insert_t4096_h128_traffic.json",
             "prefill": "sparse_mla_prefill_l8192_h64_traffic.json",
-            "mtp": "sparse_mla_decode_step_mtp_b256x2_h128_traffic.json"}.get(
-                which, "sparse_mla_decode_b64_h128_traffic.json")
+            "mtp": "sparse_mla_decode_step_mtp_b256x2_h128_traffic.json"}.get(which)
+    if name is None:
+        return None
     path = os.path.join(HERE, "profiles", name)
     try:
         with open(path) as f:
@@ -104,6 +109,11 @@ def parse():
     ap.add_argument("--unfused", action="store_true", help="same as --launches 3")
     ap.add_argument("--page-size", type=int, default=64, choices=[32, 64, 256],
                     help="cache page size of the decode workload (default 64)")
+    ap.add_argument("--kv-dtype", default="fp8_ds_mla", choices=["fp8_ds_mla", "bf16", "fp8_e4m3"],
+                    help="cache dtype of the decode workload: the packed FP8/UE8M0 record "
+                         "(default), bf16 records, or E4M3 records with a per-tensor scale")
+    ap.add_argument("--kv-scale", type=float, default=0.0625,
+                    help="per-tensor scale of the fp8_e4m3 cache")
     ap.add_argument("--workload",
                     choices=["decode", "insert", "mtp", "prefill", "compressed-prefill", "indexer"],
                     default="decode",
@@ -184,12 +194,15 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).to(dev)
 
     # cache filled by the library's own insert (cache-only: no q heads)
-    cache = dsv4.new_cache(npg, page_size=PS)
+    KVD = KV_DTYPES[args.kv_dtype]
+    kvs = args.kv_scale if KVD == 2 else 1.0
+    rec_bytes = dsv4.cache_page_bytes(1, KVD)
+    cache = dsv4.new_cache(npg, page_size=PS, kv_dtype=KVD)
     cos_sin = to_dev(wl["cos_sin"], np.float32)
     weight = to_bf16(wl["q_norm_weight"])
     dsv4.dsv4_kv_insert(None, to_bf16(wl["ctx_kv"]), to_dev(wl["ctx_pos"], np.int64),
                         to_dev(wl["ctx_slot"], np.int64), cos_sin, None, wl["eps"], cache,
-                        page_size=PS)
+                        page_size=PS, kv_dtype=KVD, kv_scale=kvs)
     qsl = to_dev(wl["qsl"], np.int32)
     seq_lens = to_dev(wl["seq_lens"], np.int32)
     bt = to_dev(wl["block_table"], np.int32)
@@ -223,17 +236,20 @@ def main():
     for d in inst:
         ins = (P(d["q"].data_ptr()), P(d["kv"].data_ptr()), P(positions.data_ptr()),
                P(slot_mapping.data_ptr()), P(cos_sin.data_ptr()), cos_sin.shape[0],
-               P(weight.data_ptr()), ctypes.c_float(wl["eps"]), P(cache.data_ptr()), npg, PS, T, H, sp)
+               P(weight.data_ptr()), ctypes.c_float(wl["eps"]), P(cache.data_ptr()), npg, PS, KVD,
+               ctypes.c_float(kvs), T, H, sp)
         comb = (P(d["topk"].data_ptr()), d["topk"].shape[1], d["topk"].shape[1],
                 P(d["topk_lens"].data_ptr()), P(qsl.data_ptr()), P(seq_lens.data_ptr()),
                 P(bt.data_ptr()), bt.shape[1], wl["B"], T, wl["top_k"], wl["window"], PS,
                 P(d["comb"].data_ptr()), W, P(d["lens"].data_ptr()), sp)
-        dec = (P(d["q"].data_ptr()), P(cache.data_ptr()), npg, PS, P(d["comb"].data_ptr()), W,
+        dec = (P(d["q"].data_ptr()), P(cache.data_ptr()), npg, PS, KVD, ctypes.c_float(kvs),
+               P(d["comb"].data_ptr()), W,
                P(d["lens"].data_ptr()), P(d["sinks"].data_ptr()),
                ctypes.c_float(wl["softmax_scale"]), P(d["out"].data_ptr()), None, T, H)
         dec = dec + ((splits, P(workspace.data_ptr()), ctypes.c_size_t(ws_bytes), sp) if splits > 1
                      else (None, ctypes.c_size_t(0), sp))
-        fused = (P(d["q"].data_ptr()), P(cache.data_ptr()), npg, PS, P(d["topk"].data_ptr()),
+        fused = (P(d["q"].data_ptr()), P(cache.data_ptr()), npg, PS, KVD, ctypes.c_float(kvs),
+                 P(d["topk"].data_ptr()),
                  d["topk"].shape[1], d["topk"].shape[1], P(d["topk_lens"].data_ptr()),
                  P(qsl.data_ptr()), P(seq_lens.data_ptr()), P(bt.data_ptr()), bt.shape[1], wl["B"],
                  wl["top_k"], wl["window"], P(d["sinks"].data_ptr()),
@@ -380,9 +396,9 @@ def main():
     nv = float(np.mean([n_valid[i] for i in used]))
     ls = float(np.mean([lens_sum[i] for i in used]))
     flops = 2.0 * H * (LATENT + NOPE) * nv
-    bytes_alg = RECORD * nv + T * H * (LATENT + NOPE) * 2 + 4.0 * ls + 4.0 * T + 4.0 * H
+    bytes_alg = rec_bytes * nv + T * H * (LATENT + NOPE) * 2 + 4.0 * ls + 4.0 * T + 4.0 * H
     if one_launch:  # + the insert's q write-back, kv rows, cache rows, cos/sin, positions
-        bytes_alg += T * H * LATENT * 2 + T * (LATENT * 2 + RECORD + 64 * 4 + 16) + LATENT * 2
+        bytes_alg += T * H * LATENT * 2 + T * (LATENT * 2 + rec_bytes + 64 * 4 + 16) + LATENT * 2
     achieved_tflops = flops / dec_s / 1e12
     achieved_gbs = bytes_alg / dec_s / 1e9
     t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
@@ -425,7 +441,10 @@ def main():
             "batch": T, "heads": H, "top_k": wl["top_k"], "topk_lens": "U{1024..2048}",
             "window": wl["window"], "combined_width": W, "context": int(wl["seq_lens"][0]),
             "page_size": PS, "latent_dim": LATENT, "value_dim": NOPE, "sinks": True,
-            "instances_rotated": n_inst, "cache": "FP8 e4m3 nope + UE8M0 scales + bf16 rope",
+            "instances_rotated": n_inst,
+            "cache": {0: "FP8 e4m3 nope + UE8M0 scales + bf16 rope",
+                      1: "bf16 records (576 values)",
+                      2: f"FP8 e4m3 records (576 codes), per-tensor scale {kvs}"}[KVD],
             **({"decode_splits": splits} if splits > 1 else {}),
         },
         "roofline": {
@@ -435,8 +454,8 @@ def main():
             "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
             "frac": round((achieved_tflops / PEAK_BF16_TFLOPS) if bound == "mfma"
                           else (achieved_gbs / PEAK_HBM_GBS), 4),
-            "traffic": (measured_traffic("step" if one_launch else "fused" if fused_step
-                                         else "decode")
+            "traffic": (measured_traffic(("step" if one_launch else "fused" if fused_step
+                                          else "decode") + ("" if KVD == 0 else "_" + args.kv_dtype))
                         if (splits == 1 and T == 64 and PS == 64) else None),
             "kernel": ("sparse_mla_kernel<2, fused combine, insert> pieces + split_merge_kernel "
                        "(dsv4_sparse_mla_decode_step_split)" if splits > 1 and one_launch else
@@ -465,7 +484,7 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, inst[0], calls, H, T, W, PS)
+        result["cpu_baseline"] = cpu_baseline(wl, inst[0], calls, H, T, W, PS, KVD, kvs)
     print(json.dumps(result), flush=True)
 
 
@@ -994,7 +1013,7 @@ def bench_prefill(args, torch, dsv4):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(wl, d0, calls, H, T, W, PS=64):
+def cpu_baseline(wl, d0, calls, H, T, W, PS=64, kv_dtype=0, kv_scale=1.0):
     """The CPU oracle (fp64, as it stands) timed on this host on one full step of
     instance 0: insert + combine + attention for all 64 query tokens."""
     import oracle
@@ -1008,10 +1027,11 @@ def cpu_baseline(wl, d0, calls, H, T, W, PS=64):
                                  wl["block_table"], T, wl["top_k"], wl["window"], PS, W)
     need = np.unique(idx0[idx0 >= 0])
     sel = np.isin(wl["ctx_slot"], need)
-    cache = np.zeros(npg * PS * RECORD, np.uint8)
+    cache = np.zeros(npg * PS * oracle.kv_record_bytes(kv_dtype), np.uint8)
+    kvk = dict(kv_dtype=kv_dtype, kv_scale=kv_scale)
     oracle.kv_insert(np.zeros((int(sel.sum()), 0, LATENT), np.uint16), wl["ctx_kv"][sel],
                      wl["ctx_pos"][sel], wl["ctx_slot"][sel], wl["cos_sin"],
-                     np.zeros(LATENT, np.uint16), wl["eps"], cache, npg, PS, inplace=True)
+                     np.zeros(LATENT, np.uint16), wl["eps"], cache, npg, PS, inplace=True, **kvk)
     kv_new = d0["kv"].cpu().view(__import__("torch").int16).numpy().view(np.uint16)
     pos = wl["seq_lens"].astype(np.int64) - 1
     slots = wl["block_table"][np.arange(T), pos // PS].astype(np.int64) * PS + pos % PS
@@ -1021,11 +1041,11 @@ def cpu_baseline(wl, d0, calls, H, T, W, PS=64):
         # same rows rewrites the same cache bytes
         q = np.array(it["q"], copy=True)
         oracle.kv_insert(q, kv_new, pos, slots, wl["cos_sin"], wl["q_norm_weight"], wl["eps"],
-                         cache, npg, PS, inplace=True)
+                         cache, npg, PS, inplace=True, **kvk)
         idx, lens = oracle.combine(it["topk"], it["topk_lens"], wl["qsl"], wl["seq_lens"],
                                    wl["block_table"], T, wl["top_k"], wl["window"], PS, W)
         oracle.sparse_mla(q, cache, npg, PS, idx, lens, it["sinks"], wl["softmax_scale"],
-                          nthreads=cores, with_lse=False)
+                          nthreads=cores, with_lse=False, **kvk)
 
     # repeated full steps until about 10 s of host work (at most 30 steps)
     reps, el = 0, 0.0
@@ -1042,7 +1062,7 @@ def cpu_baseline(wl, d0, calls, H, T, W, PS=64):
     q1 = np.array(it["q"][:n1], copy=True)
     t0 = time.perf_counter()
     oracle.sparse_mla(q1, cache, npg, PS, idx[:n1], lens[:n1], it["sinks"], wl["softmax_scale"],
-                      nthreads=1, with_lse=False)
+                      nthreads=1, with_lse=False, **kvk)
     el1 = time.perf_counter() - t0
     return {"value": round(T * reps / el, 3), "unit": "query-tokens/s", "cores": cores,
             "kind": "oracle", "cpu": cpu_model(),

@@ -12,7 +12,8 @@
  *        item 3; Key source excerpts (rocm.py _combine_topk_swa_indices_kernel).
  *   [p4] PR #43477 "Enable DeepSeek V4 and GLM-5.1 on SM120" — Key source excerpts
  *        (flashinfer_mla_sparse_sm120.py forward_mqa; flashinfer_sparse.py supports_sink,
- *        get_kv_cache_shape; supported kernel block sizes).
+ *        get_kv_cache_shape; flashinfer_mla_sparse.py supported_kv_cache_dtypes;
+ *        supported kernel block sizes).
  *
  * Geometry (fixed): latent D = 576 = 512 no-PE ("nope") + 64 RoPE dims; value/output
  * Dv = kv_lora_rank = 512 [p4 forward_mqa output shape (T, H, kv_lora_rank)].
@@ -29,6 +30,20 @@
  * Slot s lives in page s / P at row s % P [p2 dequant kernel: block_idx / pos_in_block].
  * Dequantised nope value d of slot s = e4m3(code) * 2^(scale[d/64] - 127) [p2 dequant
  * kernel], which is exactly representable in bf16.  648 bytes per token record.
+ * This is kv_dtype DSV4_KV_FP8_DS_MLA [p4: the "fp8_ds_mla" cache of the SM120 backend].
+ *
+ * Other kv-cache dtypes [p4 Key source excerpts: the SM100 backend's supported kv-cache
+ * dtypes "auto" / "bfloat16" / "fp8" / "fp8_e4m3", block sizes 32 and 64, and its cache
+ * shape (num_blocks, block_size, head_size)]: a slot holds one record of the 576 values
+ * in dim order, the records of a page back to back, so slot s starts at byte
+ * s * record_bytes (page p at p * P * record_bytes):
+ *   DSV4_KV_BF16      1152 B: the 576 values as bf16 (rope dims stored rotated).
+ *   DSV4_KV_FP8_E4M3   576 B: OCP E4M3 codes of value / kv_scale, one fp32 scale
+ *                     kv_scale for the whole cache (per tensor, a host argument):
+ *                     value = e4m3(code) * kv_scale.
+ * The entry points that read or write a cache take (kv_dtype, kv_scale) right after
+ * page_size; kv_scale is used by DSV4_KV_FP8_E4M3 only and must lie in [2^-64, 2^64]
+ * there (DSV4_ERR_SHAPE otherwise); an unknown kv_dtype is DSV4_ERR_UNSUPPORTED.
  * ---------------------------------------------------------------------------------
  *
  * Conventions for every entry point:
@@ -62,6 +77,9 @@ extern "C" {
 #define DSV4_ROPE_DIM 64
 #define DSV4_SCALE_BLOCK 64
 #define DSV4_RECORD_BYTES 648
+#define DSV4_KV_FP8_DS_MLA 0 /* the packed FP8/UE8M0 record above (648 B)          */
+#define DSV4_KV_BF16 1       /* 576 bf16 values per slot (1152 B)                   */
+#define DSV4_KV_FP8_E4M3 2   /* 576 E4M3 codes per slot (576 B), per-tensor scale   */
 #define DSV4_COMBINE_ALIGN 128 /* [p3 rocm.py: top-k rows padded to a multiple of 128] */
 
 typedef enum {
@@ -81,8 +99,9 @@ const char* dsv4_status_str(int status);
  * The pointer stays valid until the next dsv4_* call on the same thread. */
 const char* dsv4_last_error(void);
 
-/* Bytes of one cache page of `page_size` slots (page_size * 648), 0 if page_size <= 0. */
-size_t dsv4_cache_page_bytes(int page_size);
+/* Bytes of one cache page of `page_size` slots of kv_dtype (page_size * 648, 1152 or 576),
+ * 0 if page_size <= 0 or kv_dtype is unknown. */
+size_t dsv4_cache_page_bytes(int page_size, int kv_dtype);
 
 /*
  * dsv4_kv_insert — fused per-head q RMSNorm + GPT-J RoPE, and FP8/UE8M0 insert of the
@@ -108,13 +127,18 @@ size_t dsv4_cache_page_bytes(int page_size);
  *                  Duplicate slots: one of the writers wins (unspecified which).
  *   q_norm_weight bf16 [576], shared by all heads.
  *   kv_cache     uint8, num_pages pages in the layout above (16-byte aligned).
+ *   kv_dtype, kv_scale  the cache's dtype.  The packed dtype stores the kv row as
+ *                  above; DSV4_KV_BF16 stores dims 0..511 as given and the rotated rope
+ *                  dims as bf16; DSV4_KV_FP8_E4M3 takes those same 576 bf16 values z and
+ *                  stores e4m3(z / kv_scale), the quotient correctly rounded in fp32,
+ *                  saturated to +-448, round to nearest even.
  * Supported: page_size in {32, 64, 256}, H in 1..128, T >= 0 (T == 0 is a no-op).
  * Alignment: q, kv, kv_cache 16-byte aligned.
  */
 int dsv4_kv_insert(void* q, const void* kv, const int64_t* positions,
                    const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                    const void* q_norm_weight, float eps, uint8_t* kv_cache, int num_pages,
-                   int page_size, int T, int H, void* stream);
+                   int page_size, int kv_dtype, float kv_scale, int T, int H, void* stream);
 
 /*
  * dsv4_combine_indices — merge each query token's indexer top-k with its sliding
@@ -234,7 +258,8 @@ int dsv4_gather_workspace(const uint8_t* comp_cache, int comp_num_pages,
  * (T, H, kv_lora_rank) from physical indices; p4 supports_sink].  For token t, head h:
  *   J      = { j < min(lens[t], idx_stride) : 0 <= indices[t][j] < num_pages*page_size }
  *            (a multiset: a repeated slot counts twice),
- *   K_j    = dequantised 576-d record of slot indices[t][j],  V_j = K_j[0:512],
+ *   K_j    = the 576 values of slot indices[t][j] (dequantised for the FP8 dtypes:
+ *            e4m3(code) * 2^(scale-127), or e4m3(code) * kv_scale),  V_j = K_j[0:512],
  *   s_j    = softmax_scale * <q[t][h], K_j>,   z = sinks[h] (absent: -inf),
  *   m      = max(z, max_j s_j),  den = e^(z-m) + sum_j e^(s_j-m),
  *   out[t][h] = sum_j e^(s_j-m) V_j / den  (0 when den == 0),
@@ -243,7 +268,9 @@ int dsv4_gather_workspace(const uint8_t* comp_cache, int comp_num_pages,
  *   q        bf16 [T][H][576];  out bf16 [T][H][512];  lse fp32 [T][H] or NULL
  *   indices  int32 [T][idx_stride];  lens int32 [T];  sinks fp32 [H] or NULL
  * Arithmetic: bf16 operands, fp32 accumulation, probabilities rounded to bf16 for the
- * value product.  Supported: H in {16, 32, 64, 128}, page_size in {32, 64, 256}.
+ * value product (the per-tensor fp8 scale multiplies the scores' scale and the output
+ * instead of each value).  Supported: H in {16, 32, 64, 128}, page_size in {32, 64, 256},
+ * every kv_dtype.
  * Alignment: q, out, kv_cache 16-byte aligned; indices 4-byte aligned.
  *
  * Workspace [p2 Review highlights: no allocation on the decode path, so scratch memory
@@ -258,10 +285,10 @@ int dsv4_gather_workspace(const uint8_t* comp_cache, int comp_num_pages,
  * DSV4_ERR_WORKSPACE.
  */
 int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages,
-                           int page_size, const int32_t* indices, int idx_stride,
-                           const int32_t* lens, const float* sinks, float softmax_scale,
-                           void* out, float* lse, int T, int H, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           int page_size, int kv_dtype, float kv_scale, const int32_t* indices,
+                           int idx_stride, const int32_t* lens, const float* sinks,
+                           float softmax_scale, void* out, float* lse, int T, int H,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dsv4_sparse_mla_workspace_bytes — device workspace bytes that dsv4_sparse_mla_decode
@@ -287,7 +314,8 @@ size_t dsv4_sparse_mla_workspace_bytes(int T, int H, int width, int is_prefill);
  * (DSV4_ERR_UNSUPPORTED otherwise) and what both entry points require.
  */
 int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
-                                const int32_t* topk, int topk_stride, int topk_width,
+                                int kv_dtype, float kv_scale, const int32_t* topk,
+                                int topk_stride, int topk_width,
                                 const int32_t* topk_lens, const int32_t* query_start_loc,
                                 const int32_t* seq_lens, const int32_t* block_table,
                                 int block_table_stride, int B, int top_k, int window,
@@ -317,8 +345,9 @@ int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_
 int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* positions,
                                 const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                                 const void* q_norm_weight, float eps, uint8_t* kv_cache,
-                                int num_pages, int page_size, const int32_t* topk, int topk_stride,
-                                int topk_width, const int32_t* topk_lens,
+                                int num_pages, int page_size, int kv_dtype, float kv_scale,
+                                const int32_t* topk, int topk_stride, int topk_width,
+                                const int32_t* topk_lens,
                                 const int32_t* query_start_loc, const int32_t* seq_lens,
                                 const int32_t* block_table, int block_table_stride, int B,
                                 int top_k, int window, const float* sinks, float softmax_scale,
@@ -345,11 +374,11 @@ int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* position
 int dsv4_sparse_mla_decode_step_split(
     void* q, const void* kv, const int64_t* positions, const int64_t* slot_mapping,
     const float* cos_sin, int max_pos, const void* q_norm_weight, float eps, uint8_t* kv_cache,
-    int num_pages, int page_size, const int32_t* topk, int topk_stride, int topk_width,
-    const int32_t* topk_lens, const int32_t* query_start_loc, const int32_t* seq_lens,
-    const int32_t* block_table, int block_table_stride, int B, int top_k, int window,
-    const float* sinks, float softmax_scale, void* out, float* lse, int T, int H, int splits,
-    void* workspace, size_t workspace_bytes, void* stream);
+    int num_pages, int page_size, int kv_dtype, float kv_scale, const int32_t* topk,
+    int topk_stride, int topk_width, const int32_t* topk_lens, const int32_t* query_start_loc,
+    const int32_t* seq_lens, const int32_t* block_table, int block_table_stride, int B, int top_k,
+    int window, const float* sinks, float softmax_scale, void* out, float* lse, int T, int H,
+    int splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dsv4_sparse_mla_prefill — the same result as dsv4_sparse_mla_decode, scheduled for
@@ -360,10 +389,10 @@ int dsv4_sparse_mla_decode_step_split(
  * so NULL / 0 is the usual argument.
  */
 int dsv4_sparse_mla_prefill(const void* q, const uint8_t* kv_cache, int num_pages,
-                            int page_size, const int32_t* indices, int idx_stride,
-                            const int32_t* lens, const float* sinks, float softmax_scale,
-                            void* out, float* lse, int T, int H, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            int page_size, int kv_dtype, float kv_scale, const int32_t* indices,
+                            int idx_stride, const int32_t* lens, const float* sinks,
+                            float softmax_scale, void* out, float* lse, int T, int H,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dsv4_sparse_mla_split_workspace_bytes — bytes of device workspace that
@@ -394,10 +423,11 @@ size_t dsv4_sparse_mla_split_workspace_bytes(int T, int H, int splits);
  * misaligned or too small workspace, and everything dsv4_sparse_mla_decode checks.
  */
 int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num_pages,
-                                 int page_size, const int32_t* indices, int idx_stride,
-                                 const int32_t* lens, const float* sinks, float softmax_scale,
-                                 void* out, float* lse, int T, int H, int splits,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 int page_size, int kv_dtype, float kv_scale,
+                                 const int32_t* indices, int idx_stride, const int32_t* lens,
+                                 const float* sinks, float softmax_scale, void* out, float* lse,
+                                 int T, int H, int splits, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * dsv4_sparse_mla_decode_split_noalloc — dsv4_sparse_mla_decode_split for callers that
@@ -418,7 +448,8 @@ int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num
  */
 #define DSV4_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 int dsv4_sparse_mla_decode_split_noalloc(const void* q, const uint8_t* kv_cache, int num_pages,
-                                         int page_size, const int32_t* indices, int idx_stride,
+                                         int page_size, int kv_dtype, float kv_scale,
+                                         const int32_t* indices, int idx_stride,
                                          const int32_t* lens, const float* sinks,
                                          float softmax_scale, void* out, float* lse, int T, int H,
                                          int splits, void* stream);
@@ -428,11 +459,12 @@ int dsv4_sparse_mla_decode_split_noalloc(const void* q, const uint8_t* kv_cache,
  * excerpts: _dequant_gather_slots_kernel, one program per slot; a negative slot gives
  * a zero row; FP8 -> fp32 times 2^(byte-127) -> bf16; the bf16 RoPE part is copied].
  * Slots >= num_pages*page_size also give zero rows.  The attention entry points fuse
- * this step; it is exported as a separately testable step.
+ * this step; it is exported as a separately testable step.  DSV4_KV_BF16 records are
+ * copied; DSV4_KV_FP8_E4M3 values are e4m3(code) * kv_scale rounded once to bf16.
  *   slots int32 [n];  out bf16 [n][576]
  */
-int dsv4_gather_dequant(const uint8_t* kv_cache, int num_pages, int page_size,
-                        const int32_t* slots, int n, void* out, void* stream);
+int dsv4_gather_dequant(const uint8_t* kv_cache, int num_pages, int page_size, int kv_dtype,
+                        float kv_scale, const int32_t* slots, int n, void* out, void* stream);
 
 #ifdef __cplusplus
 }

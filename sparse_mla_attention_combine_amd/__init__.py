@@ -18,6 +18,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libdsv4.so")
 
 LATENT_DIM, NOPE_DIM, ROPE_DIM, RECORD_BYTES, COMBINE_ALIGN = 576, 512, 64, 648, 128
+# kv-cache dtypes (DSV4_KV_* of the C header): the packed FP8/UE8M0 record, bf16 records,
+# E4M3 records with one per-tensor scale (kv_scale)
+KV_FP8_DS_MLA, KV_BF16, KV_FP8_E4M3 = 0, 1, 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -28,26 +31,27 @@ _vp, _i32, _f32, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_
 
 _lib.dsv4_status_str.argtypes, _lib.dsv4_status_str.restype = [_i32], ctypes.c_char_p
 _lib.dsv4_last_error.argtypes, _lib.dsv4_last_error.restype = [], ctypes.c_char_p
-_lib.dsv4_cache_page_bytes.argtypes, _lib.dsv4_cache_page_bytes.restype = [_i32], ctypes.c_size_t
+_lib.dsv4_cache_page_bytes.argtypes = [_i32, _i32]
+_lib.dsv4_cache_page_bytes.restype = ctypes.c_size_t
 _lib.dsv4_kv_insert.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _vp, _i32, _i32, _i32,
-                                _i32, _vp]
+                                _f32, _i32, _i32, _vp]
 _lib.dsv4_combine_indices.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _vp, _i32, _vp, _vp]
-_attn_head = [_vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _i32, _i32]
+_attn_head = [_vp, _vp, _i32, _i32, _i32, _f32, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _i32, _i32]
 _lib.dsv4_sparse_mla_decode.argtypes = _attn_head + [_vp, ctypes.c_size_t, _vp]
 _lib.dsv4_sparse_mla_prefill.argtypes = _attn_head + [_vp, ctypes.c_size_t, _vp]
 _lib.dsv4_sparse_mla_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
 _lib.dsv4_sparse_mla_workspace_bytes.restype = ctypes.c_size_t
-_lib.dsv4_gather_dequant.argtypes = [_vp, _i32, _i32, _vp, _i32, _vp, _vp]
+_lib.dsv4_gather_dequant.argtypes = [_vp, _i32, _i32, _i32, _f32, _vp, _i32, _vp, _vp]
 _lib.dsv4_sparse_mla_split_workspace_bytes.argtypes = [_i32, _i32, _i32]
 _lib.dsv4_sparse_mla_split_workspace_bytes.restype = ctypes.c_size_t
 _lib.dsv4_sparse_mla_decode_split.argtypes = _attn_head + [_i32, _vp, ctypes.c_size_t, _vp]
 _lib.dsv4_sparse_mla_decode_split_noalloc.argtypes = _attn_head + [_i32, _vp]
 _lib.dsv4_combine_indices_compressed.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]
-_lib.dsv4_sparse_mla_decode_topk.argtypes = [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp,
-                                             _vp, _i32, _i32, _i32, _i32, _vp, _f32, _vp, _vp,
-                                             _i32, _i32, _vp]
+_lib.dsv4_sparse_mla_decode_topk.argtypes = [_vp, _vp, _i32, _i32, _i32, _f32, _vp, _i32, _i32,
+                                             _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _f32,
+                                             _vp, _vp, _i32, _i32, _vp]
 _lib.dsv4_sparse_mla_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _vp, _i32,
                                              _i32] + _lib.dsv4_sparse_mla_decode_topk.argtypes[4:]
 _lib.dsv4_sparse_mla_decode_step_split.argtypes = (_lib.dsv4_sparse_mla_decode_step.argtypes[:-1]
@@ -111,29 +115,38 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def cache_page_bytes(page_size: int = 64) -> int:
-    return int(_lib.dsv4_cache_page_bytes(page_size))
+def cache_page_bytes(page_size: int = 64, kv_dtype: int = KV_FP8_DS_MLA) -> int:
+    return int(_lib.dsv4_cache_page_bytes(page_size, kv_dtype))
 
 
-def new_cache(num_pages: int, page_size: int = 64, device="cuda") -> torch.Tensor:
+def new_cache(num_pages: int, page_size: int = 64, device="cuda",
+              kv_dtype: int = KV_FP8_DS_MLA) -> torch.Tensor:
     """Zero-filled uint8 cache of ``num_pages`` pages (caller-owned device memory)."""
-    return torch.zeros(num_pages * cache_page_bytes(page_size), dtype=torch.uint8, device=device)
+    return torch.zeros(num_pages * cache_page_bytes(page_size, kv_dtype), dtype=torch.uint8,
+                       device=device)
+
+
+def _num_pages(kv_cache, page_size, kv_dtype):
+    pb = cache_page_bytes(page_size, kv_dtype)
+    return kv_cache.numel() // pb if pb else 0
 
 
 def dsv4_kv_insert(q, kv, positions, slot_mapping, cos_sin, q_norm_weight, eps, kv_cache,
-                   page_size=64, stream=None):
+                   page_size=64, stream=None, kv_dtype=KV_FP8_DS_MLA, kv_scale=1.0):
     """q bf16 [T, H, 576] (in place), kv bf16 [T, 576], positions/slot_mapping int64 [T],
-    cos_sin fp32 [max_pos, 64], q_norm_weight bf16 [576], kv_cache uint8 pages."""
+    cos_sin fp32 [max_pos, 64], q_norm_weight bf16 [576], kv_cache uint8 pages of
+    kv_dtype (kv_scale: the per-tensor scale of a KV_FP8_E4M3 cache)."""
     _want(q, torch.bfloat16, "q"), _want(kv, torch.bfloat16, "kv")
     _want(positions, torch.int64, "positions"), _want(slot_mapping, torch.int64, "slot_mapping")
     _want(cos_sin, torch.float32, "cos_sin"), _want(q_norm_weight, torch.bfloat16, "q_norm_weight")
     _want(kv_cache, torch.uint8, "kv_cache")
     T, H = (q.shape[0], q.shape[1]) if q is not None else (kv.shape[0], 0)
-    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    num_pages = _num_pages(kv_cache, page_size, kv_dtype)
     _check(_lib.dsv4_kv_insert(_ptr(q) if H else None, _ptr(kv), _ptr(positions),
                                _ptr(slot_mapping), _ptr(cos_sin), cos_sin.shape[0],
                                _ptr(q_norm_weight) if H else None, float(eps), _ptr(kv_cache),
-                               num_pages, page_size, T, H, _stream(stream)))
+                               num_pages, page_size, int(kv_dtype), float(kv_scale), T, H,
+                               _stream(stream)))
     return q
 
 
@@ -212,14 +225,15 @@ def _nbytes(t):
 
 
 def _attention(fn, q, kv_cache, indices, lens, sinks, softmax_scale, out, lse, page_size,
-               workspace, stream):
+               workspace, stream, kv_dtype, kv_scale):
     _want(q, torch.bfloat16, "q"), _want(kv_cache, torch.uint8, "kv_cache")
     _want(indices, torch.int32, "indices"), _want(lens, torch.int32, "lens")
     _want(sinks, torch.float32, "sinks"), _want(out, torch.bfloat16, "out")
     _want(lse, torch.float32, "lse")
     T, H = q.shape[0], q.shape[1]
-    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
-    _check(fn(_ptr(q), _ptr(kv_cache), num_pages, page_size, _ptr(indices), indices.shape[1],
+    num_pages = _num_pages(kv_cache, page_size, kv_dtype)
+    _check(fn(_ptr(q), _ptr(kv_cache), num_pages, page_size, int(kv_dtype), float(kv_scale),
+              _ptr(indices), indices.shape[1],
               _ptr(lens), _ptr(sinks), float(softmax_scale), _ptr(out), _ptr(lse), T, H,
               _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return out
@@ -231,25 +245,28 @@ def workspace_bytes(T, H, width, prefill=False):
 
 
 def dsv4_sparse_mla_decode(q, kv_cache, indices, lens, sinks, softmax_scale, out, lse=None,
-                           page_size=64, workspace=None, stream=None):
+                           page_size=64, workspace=None, stream=None, kv_dtype=KV_FP8_DS_MLA,
+                           kv_scale=1.0):
     """q bf16 [T, H, 576], indices int32 [T, stride] physical slots, lens int32 [T],
     sinks fp32 [H] or None -> out bf16 [T, H, 512] (and lse fp32 [T, H] if given).
     workspace: None, or a device tensor of at least workspace_bytes(T, H, stride) bytes
     (lets a small batch run its rows in pieces)."""
     return _attention(_lib.dsv4_sparse_mla_decode, q, kv_cache, indices, lens, sinks,
-                      softmax_scale, out, lse, page_size, workspace, stream)
+                      softmax_scale, out, lse, page_size, workspace, stream, kv_dtype, kv_scale)
 
 
 def dsv4_sparse_mla_prefill(q, kv_cache, indices, lens, sinks, softmax_scale, out, lse=None,
-                            page_size=64, workspace=None, stream=None):
+                            page_size=64, workspace=None, stream=None, kv_dtype=KV_FP8_DS_MLA,
+                            kv_scale=1.0):
     """Same contract as dsv4_sparse_mla_decode, scheduled for many query tokens."""
     return _attention(_lib.dsv4_sparse_mla_prefill, q, kv_cache, indices, lens, sinks,
-                      softmax_scale, out, lse, page_size, workspace, stream)
+                      softmax_scale, out, lse, page_size, workspace, stream, kv_dtype, kv_scale)
 
 
 def dsv4_sparse_mla_decode_topk(q, kv_cache, topk, topk_lens, query_start_loc, seq_lens,
                                 block_table, top_k, window, sinks, softmax_scale, out, lse=None,
-                                page_size=64, topk_width=None, stream=None):
+                                page_size=64, topk_width=None, stream=None,
+                                kv_dtype=KV_FP8_DS_MLA, kv_scale=1.0):
     """dsv4_combine_indices + dsv4_sparse_mla_decode in one launch (the combined rows are
     built in LDS): q bf16 [T, H, 576], topk int32 [T, width], topk_lens int32 [T] or None,
     query_start_loc int32 [B+1], seq_lens int32 [B], block_table int32 [B, pages] ->
@@ -261,10 +278,11 @@ def dsv4_sparse_mla_decode_topk(q, kv_cache, topk, topk_lens, query_start_loc, s
     _want(sinks, torch.float32, "sinks"), _want(out, torch.bfloat16, "out")
     _want(lse, torch.float32, "lse")
     T, H = q.shape[0], q.shape[1]
-    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    num_pages = _num_pages(kv_cache, page_size, kv_dtype)
     width = topk.shape[1] if topk_width is None else topk_width
     _check(_lib.dsv4_sparse_mla_decode_topk(
-        _ptr(q), _ptr(kv_cache), num_pages, page_size, _ptr(topk), topk.shape[1], width,
+        _ptr(q), _ptr(kv_cache), num_pages, page_size, int(kv_dtype), float(kv_scale), _ptr(topk),
+        topk.shape[1], width,
         _ptr(topk_lens), _ptr(query_start_loc), _ptr(seq_lens), _ptr(block_table),
         block_table.shape[1], seq_lens.shape[0], top_k, window, _ptr(sinks), float(softmax_scale),
         _ptr(out), _ptr(lse), T, H, _stream(stream)))
@@ -274,7 +292,8 @@ def dsv4_sparse_mla_decode_topk(q, kv_cache, topk, topk_lens, query_start_loc, s
 def dsv4_sparse_mla_decode_step(q, kv, positions, slot_mapping, cos_sin, q_norm_weight, eps,
                                 kv_cache, topk, topk_lens, query_start_loc, seq_lens, block_table,
                                 top_k, window, sinks, softmax_scale, out, lse=None, page_size=64,
-                                topk_width=None, splits=1, workspace=None, stream=None):
+                                topk_width=None, splits=1, workspace=None, stream=None,
+                                kv_dtype=KV_FP8_DS_MLA, kv_scale=1.0):
     """dsv4_kv_insert + dsv4_sparse_mla_decode_topk in one launch: the arguments of the
     two (q normalised in place, the new kv rows inserted into kv_cache) -> out bf16
     [T, H, 512] (and lse fp32 [T, H] if given).  splits > 1: rows cut into pieces merged
@@ -290,11 +309,11 @@ def dsv4_sparse_mla_decode_step(q, kv, positions, slot_mapping, cos_sin, q_norm_
     _want(sinks, torch.float32, "sinks"), _want(out, torch.bfloat16, "out")
     _want(lse, torch.float32, "lse")
     T, H = q.shape[0], q.shape[1]
-    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    num_pages = _num_pages(kv_cache, page_size, kv_dtype)
     width = topk.shape[1] if topk_width is None else topk_width
     args = (_ptr(q), _ptr(kv), _ptr(positions), _ptr(slot_mapping), _ptr(cos_sin),
             cos_sin.shape[0], _ptr(q_norm_weight), float(eps), _ptr(kv_cache), num_pages,
-            page_size, _ptr(topk), topk.shape[1], width, _ptr(topk_lens), _ptr(query_start_loc),
+            page_size, int(kv_dtype), float(kv_scale), _ptr(topk), topk.shape[1], width, _ptr(topk_lens), _ptr(query_start_loc),
             _ptr(seq_lens), _ptr(block_table), block_table.shape[1], seq_lens.shape[0], top_k,
             window, _ptr(sinks), float(softmax_scale), _ptr(out), _ptr(lse), T, H)
     if splits == 1:
@@ -312,7 +331,8 @@ def split_workspace_bytes(T, H, splits):
 
 
 def dsv4_sparse_mla_decode_split(q, kv_cache, indices, lens, sinks, softmax_scale, out, splits,
-                                 workspace, lse=None, page_size=64, stream=None):
+                                 workspace, lse=None, page_size=64, stream=None,
+                                 kv_dtype=KV_FP8_DS_MLA, kv_scale=1.0):
     """dsv4_sparse_mla_decode with each token's row cut into `splits` pieces merged by
     their lse; workspace: a caller-owned device tensor of at least
     split_workspace_bytes(T, H, splits) bytes (16-byte aligned)."""
@@ -321,17 +341,18 @@ def dsv4_sparse_mla_decode_split(q, kv_cache, indices, lens, sinks, softmax_scal
     _want(sinks, torch.float32, "sinks"), _want(out, torch.bfloat16, "out")
     _want(lse, torch.float32, "lse")
     T, H = q.shape[0], q.shape[1]
-    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    num_pages = _num_pages(kv_cache, page_size, kv_dtype)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.dsv4_sparse_mla_decode_split(
-        _ptr(q), _ptr(kv_cache), num_pages, page_size, _ptr(indices), indices.shape[1], _ptr(lens),
+        _ptr(q), _ptr(kv_cache), num_pages, page_size, int(kv_dtype), float(kv_scale), _ptr(indices), indices.shape[1], _ptr(lens),
         _ptr(sinks), float(softmax_scale), _ptr(out), _ptr(lse), T, H, int(splits), _ptr(workspace),
         ws_bytes, _stream(stream)))
     return out
 
 
 def dsv4_sparse_mla_decode_split_noalloc(q, kv_cache, indices, lens, sinks, softmax_scale, out,
-                                         splits, lse=None, page_size=64, stream=None):
+                                         splits, lse=None, page_size=64, stream=None,
+                                         kv_dtype=KV_FP8_DS_MLA, kv_scale=1.0):
     """dsv4_sparse_mla_decode_split with its workspace in the library's static per-GPU
     scratch array (no allocation; split_workspace_bytes(T, H, splits) must fit
     NOALLOC_SCRATCH_BYTES).  Calls that overlap on one GPU race."""
@@ -340,19 +361,21 @@ def dsv4_sparse_mla_decode_split_noalloc(q, kv_cache, indices, lens, sinks, soft
     _want(sinks, torch.float32, "sinks"), _want(out, torch.bfloat16, "out")
     _want(lse, torch.float32, "lse")
     T, H = q.shape[0], q.shape[1]
-    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
+    num_pages = _num_pages(kv_cache, page_size, kv_dtype)
     _check(_lib.dsv4_sparse_mla_decode_split_noalloc(
-        _ptr(q), _ptr(kv_cache), num_pages, page_size, _ptr(indices), indices.shape[1], _ptr(lens),
+        _ptr(q), _ptr(kv_cache), num_pages, page_size, int(kv_dtype), float(kv_scale), _ptr(indices), indices.shape[1], _ptr(lens),
         _ptr(sinks), float(softmax_scale), _ptr(out), _ptr(lse), T, H, int(splits),
         _stream(stream)))
     return out
 
 
-def dsv4_gather_dequant(kv_cache, slots, out, page_size=64, stream=None):
+def dsv4_gather_dequant(kv_cache, slots, out, page_size=64, stream=None, kv_dtype=KV_FP8_DS_MLA,
+                        kv_scale=1.0):
     """slots int32 [n] -> out bf16 [n, 576] (dequantised rows; zeros for invalid slots)."""
     _want(kv_cache, torch.uint8, "kv_cache"), _want(slots, torch.int32, "slots")
     _want(out, torch.bfloat16, "out")
-    num_pages = kv_cache.numel() // cache_page_bytes(page_size)
-    _check(_lib.dsv4_gather_dequant(_ptr(kv_cache), num_pages, page_size, _ptr(slots),
-                                    slots.shape[0], _ptr(out), _stream(stream)))
+    num_pages = _num_pages(kv_cache, page_size, kv_dtype)
+    _check(_lib.dsv4_gather_dequant(_ptr(kv_cache), num_pages, page_size, int(kv_dtype),
+                                    float(kv_scale), _ptr(slots), slots.shape[0], _ptr(out),
+                                    _stream(stream)))
     return out

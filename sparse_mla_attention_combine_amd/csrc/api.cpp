@@ -46,13 +46,26 @@ int check_page(const char* fn, int page_size, int num_pages) {
   return DSV4_OK;
 }
 
+// The cache dtype and, for the per-tensor fp8 cache, its scale (kept where every
+// E4M3 value times it, and 448 / it, stay normal fp32 numbers).
+int check_kv(const char* fn, int kv_dtype, float kv_scale) {
+  if (kv_dtype != DSV4_KV_FP8_DS_MLA && kv_dtype != DSV4_KV_BF16 && kv_dtype != DSV4_KV_FP8_E4M3)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: kv_dtype %d not supported (0 fp8_ds_mla, 1 bf16, 2 fp8_e4m3)",
+                fn, kv_dtype);
+  if (kv_dtype == DSV4_KV_FP8_E4M3 && !(kv_scale >= 0x1p-64f && kv_scale <= 0x1p64f))
+    return fail(DSV4_ERR_SHAPE, "%s: kv_scale %g of the fp8 cache not in [2^-64, 2^64]", fn,
+                (double)kv_scale);
+  return DSV4_OK;
+}
+
 int check_attention(const char* fn, const void* q, const uint8_t* kv_cache, int num_pages,
-                    int page_size, const int32_t* indices, int idx_stride, const int32_t* lens,
+                    int page_size, int kv_dtype, float kv_scale, const int32_t* indices, int idx_stride, const int32_t* lens,
                     const float* /*sinks*/, float softmax_scale, const void* out, int T, int H) {
   if (T < 0) return fail(DSV4_ERR_SHAPE, "%s: T = %d < 0", fn, T);
   if (H != 16 && H != 32 && H != 64 && H != 128)
     return fail(DSV4_ERR_UNSUPPORTED, "%s: H = %d not in {16, 32, 64, 128}", fn, H);
   int st = check_page(fn, page_size, num_pages);
+  if (!st) st = check_kv(fn, kv_dtype, kv_scale);
   if (st) return st;
   if (idx_stride < 0) return fail(DSV4_ERR_SHAPE, "%s: idx_stride %d < 0", fn, idx_stride);
   if (!(softmax_scale == softmax_scale)) return fail(DSV4_ERR_SHAPE, "%s: softmax_scale is NaN", fn);
@@ -85,16 +98,18 @@ const char* dsv4_status_str(int status) {
 
 const char* dsv4_last_error(void) { return g_err; }
 
-size_t dsv4_cache_page_bytes(int page_size) {
-  return page_size > 0 ? (size_t)page_size * DSV4_RECORD_BYTES : 0;
+size_t dsv4_cache_page_bytes(int page_size, int kv_dtype) {
+  return page_size > 0 ? (size_t)page_size * (size_t)dsv4::kv_record_bytes_of(kv_dtype) : 0;
 }
 
 int dsv4_kv_insert(void* q, const void* kv, const int64_t* positions, const int64_t* slot_mapping,
                    const float* cos_sin, int max_pos, const void* q_norm_weight, float eps,
-                   uint8_t* kv_cache, int num_pages, int page_size, int T, int H, void* stream) {
+                   uint8_t* kv_cache, int num_pages, int page_size, int kv_dtype, float kv_scale,
+                   int T, int H, void* stream) {
   const char* fn = "dsv4_kv_insert";
   if (T < 0 || H < 0 || H > 128) return fail(DSV4_ERR_SHAPE, "%s: T = %d, H = %d out of range (T >= 0, 0 <= H <= 128)", fn, T, H);
   int st = check_page(fn, page_size, num_pages);
+  if (!st) st = check_kv(fn, kv_dtype, kv_scale);
   if (st) return st;
   if (max_pos < 0) return fail(DSV4_ERR_SHAPE, "%s: max_pos %d < 0", fn, max_pos);
   if (!(eps >= 0.f)) return fail(DSV4_ERR_SHAPE, "%s: eps must be >= 0", fn);
@@ -108,7 +123,7 @@ int dsv4_kv_insert(void* q, const void* kv, const int64_t* positions, const int6
     return fail(DSV4_ERR_ALIGN, "%s: q, kv, q_norm_weight, cos_sin, kv_cache must be 16-byte aligned; positions, slot_mapping 8-byte", fn);
   return hip_status(dsv4::launch_insert(q, kv, positions, slot_mapping, cos_sin, max_pos,
                                         q_norm_weight, eps, kv_cache, num_pages,
-                                        dsv4::page_shift_of(page_size), T, H,
+                                        dsv4::page_shift_of(page_size), kv_dtype, kv_scale, T, H,
                                         static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -234,12 +249,13 @@ int dsv4_gather_workspace(const uint8_t* comp_cache, int comp_num_pages,
 
 // decode and prefill: the same checks, the workspace contract, then the launch
 static int attention_checked(const char* fn, bool prefill, const void* q, const uint8_t* kv_cache,
-                             int num_pages, int page_size, const int32_t* indices, int idx_stride,
+                             int num_pages, int page_size, int kv_dtype, float kv_scale,
+                             const int32_t* indices, int idx_stride,
                              const int32_t* lens, const float* sinks, float softmax_scale,
                              void* out, float* lse, int T, int H, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  int st = check_attention(fn, q, kv_cache, num_pages, page_size, indices, idx_stride, lens, sinks,
-                           softmax_scale, out, T, H);
+  int st = check_attention(fn, q, kv_cache, num_pages, page_size, kv_dtype, kv_scale, indices,
+                           idx_stride, lens, sinks, softmax_scale, out, T, H);
   if (st) return st;
   if (!workspace && workspace_bytes != 0)
     return fail(DSV4_ERR_WORKSPACE, "%s: workspace is NULL but workspace_bytes is %zu", fn,
@@ -253,18 +269,20 @@ static int attention_checked(const char* fn, bool prefill, const void* q, const 
   }
   if (T == 0) return ok();
   return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size),
-                                           indices, idx_stride, lens, sinks, softmax_scale, out,
-                                           lse, T, H, prefill, workspace, workspace_bytes,
+                                           kv_dtype, kv_scale, indices, idx_stride, lens, sinks,
+                                           softmax_scale, out, lse, T, H, prefill, workspace,
+                                           workspace_bytes,
                                            static_cast<hipStream_t>(stream)),
                     fn);
 }
 
 int dsv4_sparse_mla_decode(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
-                           const int32_t* indices, int idx_stride, const int32_t* lens,
-                           const float* sinks, float softmax_scale, void* out, float* lse, int T,
-                           int H, void* workspace, size_t workspace_bytes, void* stream) {
+                           int kv_dtype, float kv_scale, const int32_t* indices, int idx_stride,
+                           const int32_t* lens, const float* sinks, float softmax_scale, void* out,
+                           float* lse, int T, int H, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   return attention_checked("dsv4_sparse_mla_decode", false, q, kv_cache, num_pages, page_size,
-                           indices, idx_stride, lens, sinks, softmax_scale, out, lse, T, H,
+                           kv_dtype, kv_scale, indices, idx_stride, lens, sinks, softmax_scale, out, lse, T, H,
                            workspace, workspace_bytes, stream);
 }
 
@@ -279,20 +297,22 @@ size_t dsv4_sparse_mla_split_workspace_bytes(int T, int H, int splits) {
 }
 
 int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num_pages,
-                                 int page_size, const int32_t* indices, int idx_stride,
-                                 const int32_t* lens, const float* sinks, float softmax_scale,
-                                 void* out, float* lse, int T, int H, int splits,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+                                 int page_size, int kv_dtype, float kv_scale,
+                                 const int32_t* indices, int idx_stride, const int32_t* lens,
+                                 const float* sinks, float softmax_scale, void* out, float* lse,
+                                 int T, int H, int splits, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   const char* fn = "dsv4_sparse_mla_decode_split";
-  int st = check_attention(fn, q, kv_cache, num_pages, page_size, indices, idx_stride, lens, sinks,
-                           softmax_scale, out, T, H);
+  int st = check_attention(fn, q, kv_cache, num_pages, page_size, kv_dtype, kv_scale, indices,
+                           idx_stride, lens, sinks, softmax_scale, out, T, H);
   if (st) return st;
   if (splits < 1 || splits > 64) return fail(DSV4_ERR_SHAPE, "%s: splits %d not in 1..64", fn, splits);
   if (T == 0) return ok();
   if (splits == 1)
-    return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size), indices, idx_stride, lens,
-                                             sinks, softmax_scale, out, lse, T, H, false, nullptr,
-                                             0, static_cast<hipStream_t>(stream)),
+    return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size),
+                                             kv_dtype, kv_scale, indices, idx_stride, lens, sinks,
+                                             softmax_scale, out, lse, T, H, false, nullptr, 0,
+                                             static_cast<hipStream_t>(stream)),
                       fn);
   if ((int64_t)T * splits >= ((int64_t)1 << 31) / 8)
     return fail(DSV4_ERR_SHAPE, "%s: T * splits = %lld too large", fn, (long long)T * splits);
@@ -300,27 +320,30 @@ int dsv4_sparse_mla_decode_split(const void* q, const uint8_t* kv_cache, int num
   if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
     return fail(DSV4_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned and hold %zu bytes (got %zu%s)",
                 fn, need, workspace_bytes, workspace ? "" : ", NULL");
-  return hip_status(dsv4::launch_attention_split(q, kv_cache, num_pages, dsv4::page_shift_of(page_size), indices, idx_stride, lens,
-                                                 sinks, softmax_scale, out, lse, T, H, splits,
-                                                 workspace, static_cast<hipStream_t>(stream)),
+  return hip_status(dsv4::launch_attention_split(q, kv_cache, num_pages,
+                                                 dsv4::page_shift_of(page_size), kv_dtype,
+                                                 kv_scale, indices, idx_stride, lens, sinks,
+                                                 softmax_scale, out, lse, T, H, splits, workspace,
+                                                 static_cast<hipStream_t>(stream)),
                     fn);
 }
 
 int dsv4_sparse_mla_decode_split_noalloc(const void* q, const uint8_t* kv_cache, int num_pages,
-                                         int page_size, const int32_t* indices, int idx_stride,
+                                         int page_size, int kv_dtype, float kv_scale,
+                                         const int32_t* indices, int idx_stride,
                                          const int32_t* lens, const float* sinks,
                                          float softmax_scale, void* out, float* lse, int T, int H,
                                          int splits, void* stream) {
   const char* fn = "dsv4_sparse_mla_decode_split_noalloc";
-  int st = check_attention(fn, q, kv_cache, num_pages, page_size, indices, idx_stride, lens, sinks,
-                           softmax_scale, out, T, H);
+  int st = check_attention(fn, q, kv_cache, num_pages, page_size, kv_dtype, kv_scale, indices,
+                           idx_stride, lens, sinks, softmax_scale, out, T, H);
   if (st) return st;
   if (splits < 1 || splits > 64) return fail(DSV4_ERR_SHAPE, "%s: splits %d not in 1..64", fn, splits);
   if (T == 0) return ok();
   if (splits == 1)
     return hip_status(dsv4::launch_attention(q, kv_cache, num_pages, dsv4::page_shift_of(page_size),
-                                             indices, idx_stride, lens, sinks, softmax_scale, out,
-                                             lse, T, H, false, nullptr, 0,
+                                             kv_dtype, kv_scale, indices, idx_stride, lens, sinks,
+                                             softmax_scale, out, lse, T, H, false, nullptr, 0,
                                              static_cast<hipStream_t>(stream)),
                       fn);
   if ((int64_t)T * splits >= ((int64_t)1 << 31) / 8)
@@ -338,14 +361,15 @@ int dsv4_sparse_mla_decode_split_noalloc(const void* q, const uint8_t* kv_cache,
     return fail(DSV4_ERR_HIP, "%s: the address of the static scratch array: %s", fn,
                 hipGetErrorString(e));
   return hip_status(dsv4::launch_attention_split(q, kv_cache, num_pages,
-                                                 dsv4::page_shift_of(page_size), indices,
-                                                 idx_stride, lens, sinks, softmax_scale, out, lse,
-                                                 T, H, splits, ws, static_cast<hipStream_t>(stream)),
+                                                 dsv4::page_shift_of(page_size), kv_dtype,
+                                                 kv_scale, indices, idx_stride, lens, sinks,
+                                                 softmax_scale, out, lse, T, H, splits, ws,
+                                                 static_cast<hipStream_t>(stream)),
                     fn);
 }
 
 int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
-                                const int32_t* topk, int topk_stride, int topk_width,
+                                int kv_dtype, float kv_scale, const int32_t* topk, int topk_stride, int topk_width,
                                 const int32_t* topk_lens, const int32_t* query_start_loc,
                                 const int32_t* seq_lens, const int32_t* block_table,
                                 int block_table_stride, int B, int top_k, int window,
@@ -358,6 +382,7 @@ int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_
   if (H != 16 && H != 32 && H != 64 && H != 128)
     return fail(DSV4_ERR_UNSUPPORTED, "%s: H = %d not in {16, 32, 64, 128}", fn, H);
   int st = check_page(fn, page_size, num_pages);
+  if (!st) st = check_kv(fn, kv_dtype, kv_scale);
   if (st) return st;
   if (top_k > topk_width) return fail(DSV4_ERR_SHAPE, "%s: top_k %d > topk_width %d", fn, top_k, topk_width);
   if ((int64_t)top_k + window > 4096)
@@ -372,7 +397,7 @@ int dsv4_sparse_mla_decode_topk(const void* q, const uint8_t* kv_cache, int num_
   if ((topk && !aligned(topk, 4)) || !aligned(query_start_loc, 4) || !aligned(seq_lens, 4))
     return fail(DSV4_ERR_ALIGN, "%s: int32 arrays must be 4-byte aligned", fn);
   return hip_status(dsv4::launch_attention_topk(q, kv_cache, num_pages, dsv4::page_shift_of(page_size),
-                                                topk, topk_stride, topk_width, topk_lens,
+                                                kv_dtype, kv_scale, topk, topk_stride, topk_width, topk_lens,
                                                 query_start_loc, seq_lens, block_table,
                                                 block_table_stride, B, top_k, window, sinks,
                                                 softmax_scale, out, lse, T, H,
@@ -385,19 +410,21 @@ constexpr int kMaxStepQueriesPerRequest = 64;
 static int decode_step_checked(const char* fn, void* q, const void* kv, const int64_t* positions,
                                const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                                const void* q_norm_weight, float eps, uint8_t* kv_cache,
-                               int num_pages, int page_size, const int32_t* topk, int topk_stride,
-                               int topk_width, const int32_t* topk_lens,
-                               const int32_t* query_start_loc, const int32_t* seq_lens,
-                               const int32_t* block_table, int block_table_stride, int B,
-                               int top_k, int window, const float* sinks, float softmax_scale,
-                               void* out, float* lse, int T, int H, int splits, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               int num_pages, int page_size, int kv_dtype, float kv_scale,
+                               const int32_t* topk, int topk_stride, int topk_width,
+                               const int32_t* topk_lens, const int32_t* query_start_loc,
+                               const int32_t* seq_lens, const int32_t* block_table,
+                               int block_table_stride, int B, int top_k, int window,
+                               const float* sinks, float softmax_scale, void* out, float* lse,
+                               int T, int H, int splits, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   if (T < 0 || B < 0 || top_k < 0 || window < 0 || topk_width < 0 || topk_stride < topk_width ||
       block_table_stride < 0 || max_pos < 0)
     return fail(DSV4_ERR_SHAPE, "%s: negative size or topk_stride < topk_width", fn);
   if (H != 16 && H != 32 && H != 64 && H != 128)
     return fail(DSV4_ERR_UNSUPPORTED, "%s: H = %d not in {16, 32, 64, 128}", fn, H);
   int st = check_page(fn, page_size, num_pages);
+  if (!st) st = check_kv(fn, kv_dtype, kv_scale);
   if (st) return st;
   if (top_k > topk_width) return fail(DSV4_ERR_SHAPE, "%s: top_k %d > topk_width %d", fn, top_k, topk_width);
   if ((int64_t)top_k + window > 4096)
@@ -432,7 +459,8 @@ static int decode_step_checked(const char* fn, void* q, const void* kv, const in
   }
   return hip_status(dsv4::launch_attention_step(q, kv, positions, slot_mapping, cos_sin, max_pos,
                                                 q_norm_weight, eps, kv_cache, num_pages,
-                                                dsv4::page_shift_of(page_size), topk, topk_stride,
+                                                dsv4::page_shift_of(page_size), kv_dtype,
+                                                kv_scale, topk, topk_stride,
                                                 topk_width, topk_lens, query_start_loc, seq_lens,
                                                 block_table, block_table_stride, B, top_k, window,
                                                 sinks, softmax_scale, out, lse, T, H, splits,
@@ -443,15 +471,16 @@ static int decode_step_checked(const char* fn, void* q, const void* kv, const in
 int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* positions,
                                 const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                                 const void* q_norm_weight, float eps, uint8_t* kv_cache,
-                                int num_pages, int page_size, const int32_t* topk, int topk_stride,
-                                int topk_width, const int32_t* topk_lens,
-                                const int32_t* query_start_loc, const int32_t* seq_lens,
-                                const int32_t* block_table, int block_table_stride, int B,
-                                int top_k, int window, const float* sinks, float softmax_scale,
-                                void* out, float* lse, int T, int H, void* stream) {
+                                int num_pages, int page_size, int kv_dtype, float kv_scale,
+                                const int32_t* topk, int topk_stride, int topk_width,
+                                const int32_t* topk_lens, const int32_t* query_start_loc,
+                                const int32_t* seq_lens, const int32_t* block_table,
+                                int block_table_stride, int B, int top_k, int window,
+                                const float* sinks, float softmax_scale, void* out, float* lse,
+                                int T, int H, void* stream) {
   return decode_step_checked("dsv4_sparse_mla_decode_step", q, kv, positions, slot_mapping,
                              cos_sin, max_pos, q_norm_weight, eps, kv_cache, num_pages, page_size,
-                             topk, topk_stride, topk_width, topk_lens, query_start_loc, seq_lens,
+                             kv_dtype, kv_scale, topk, topk_stride, topk_width, topk_lens, query_start_loc, seq_lens,
                              block_table, block_table_stride, B, top_k, window, sinks,
                              softmax_scale, out, lse, T, H, 1, nullptr, 0, stream);
 }
@@ -459,40 +488,43 @@ int dsv4_sparse_mla_decode_step(void* q, const void* kv, const int64_t* position
 int dsv4_sparse_mla_decode_step_split(
     void* q, const void* kv, const int64_t* positions, const int64_t* slot_mapping,
     const float* cos_sin, int max_pos, const void* q_norm_weight, float eps, uint8_t* kv_cache,
-    int num_pages, int page_size, const int32_t* topk, int topk_stride, int topk_width,
-    const int32_t* topk_lens, const int32_t* query_start_loc, const int32_t* seq_lens,
-    const int32_t* block_table, int block_table_stride, int B, int top_k, int window,
-    const float* sinks, float softmax_scale, void* out, float* lse, int T, int H, int splits,
-    void* workspace, size_t workspace_bytes, void* stream) {
+    int num_pages, int page_size, int kv_dtype, float kv_scale, const int32_t* topk,
+    int topk_stride, int topk_width, const int32_t* topk_lens, const int32_t* query_start_loc,
+    const int32_t* seq_lens, const int32_t* block_table, int block_table_stride, int B, int top_k,
+    int window, const float* sinks, float softmax_scale, void* out, float* lse, int T, int H,
+    int splits, void* workspace, size_t workspace_bytes, void* stream) {
   return decode_step_checked("dsv4_sparse_mla_decode_step_split", q, kv, positions, slot_mapping,
                              cos_sin, max_pos, q_norm_weight, eps, kv_cache, num_pages, page_size,
-                             topk, topk_stride, topk_width, topk_lens, query_start_loc, seq_lens,
+                             kv_dtype, kv_scale, topk, topk_stride, topk_width, topk_lens, query_start_loc, seq_lens,
                              block_table, block_table_stride, B, top_k, window, sinks,
                              softmax_scale, out, lse, T, H, splits, workspace, workspace_bytes,
                              stream);
 }
 
 int dsv4_sparse_mla_prefill(const void* q, const uint8_t* kv_cache, int num_pages, int page_size,
-                            const int32_t* indices, int idx_stride, const int32_t* lens,
-                            const float* sinks, float softmax_scale, void* out, float* lse, int T,
-                            int H, void* workspace, size_t workspace_bytes, void* stream) {
+                            int kv_dtype, float kv_scale, const int32_t* indices, int idx_stride,
+                            const int32_t* lens, const float* sinks, float softmax_scale, void* out,
+                            float* lse, int T, int H, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   return attention_checked("dsv4_sparse_mla_prefill", true, q, kv_cache, num_pages, page_size,
-                           indices, idx_stride, lens, sinks, softmax_scale, out, lse, T, H,
+                           kv_dtype, kv_scale, indices, idx_stride, lens, sinks, softmax_scale, out, lse, T, H,
                            workspace, workspace_bytes, stream);
 }
 
-int dsv4_gather_dequant(const uint8_t* kv_cache, int num_pages, int page_size, const int32_t* slots,
-                        int n, void* out, void* stream) {
+int dsv4_gather_dequant(const uint8_t* kv_cache, int num_pages, int page_size, int kv_dtype,
+                        float kv_scale, const int32_t* slots, int n, void* out, void* stream) {
   const char* fn = "dsv4_gather_dequant";
   if (n < 0) return fail(DSV4_ERR_SHAPE, "%s: n = %d < 0", fn, n);
   int st = check_page(fn, page_size, num_pages);
+  if (!st) st = check_kv(fn, kv_dtype, kv_scale);
   if (st) return st;
   if (n == 0) return ok();
   if (!slots || !out || (!kv_cache && num_pages > 0))
     return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
   if (!aligned(out, 16) || (kv_cache && !aligned(kv_cache, 16)) || !aligned(slots, 4))
     return fail(DSV4_ERR_ALIGN, "%s: out and kv_cache must be 16-byte aligned, slots 4-byte", fn);
-  return hip_status(dsv4::launch_gather(kv_cache, num_pages, dsv4::page_shift_of(page_size), slots, n, out,
+  return hip_status(dsv4::launch_gather(kv_cache, num_pages, dsv4::page_shift_of(page_size),
+                                        kv_dtype, kv_scale, slots, n, out,
                                         static_cast<hipStream_t>(stream)),
                     fn);
 }

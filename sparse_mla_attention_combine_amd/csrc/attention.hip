@@ -38,6 +38,11 @@
 // opaque copy of the thread id so that nothing stays live, or spilled, across the loop.
 // Numerics: bf16 operands, fp32 accumulation and softmax, P rounded to bf16 for P.V;
 // the per-head sink enters only the final denominator.
+// Cache dtypes (template KV): the packed FP8/UE8M0 record above; bf16 records (the
+// fragments are the loaded bits, nothing to convert); E4M3 records with one scale s per
+// cache (PR #43477 Key source excerpts: the SM100 backend's "bfloat16" / "fp8" caches):
+// the codes convert exactly to bf16 unscaled, s multiplies the softmax scale of the
+// scores and the output (o_scale), the same values as scaling every K and V entry.
 // Variants of one kernel: the index rows come from memory (decode, prefill, and pieces of
 // rows for the split decode), or each workgroup builds its token's row in LDS from the
 // combine step's inputs (PR #43385 combine kernel: top-k, window, block table), or it
@@ -60,13 +65,14 @@ namespace dsv4 {
 // the cache is read through sti.cache.  Only this workgroup reads what it wrote (other
 // workgroups that write the same rows write the same bytes), so the barrier's
 // workgroup-scope ordering suffices.
-template <int NHB, bool FUSED, bool STEP>
+template <int NHB, bool FUSED, bool STEP, int KV>
 __global__ void __launch_bounds__(256) sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int64_t num_slots, int ps,
     const int32_t* __restrict__ indices, int idx_stride, const int32_t* __restrict__ lens,
     const float* __restrict__ sinks, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, int T, int H, int groups, int splits, int split_len,
-    float* __restrict__ part_o, float* __restrict__ part_ml, TopkIn tin, StepIn sti) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, TopkIn tin, StepIn sti,
+    float o_scale) {
   static_assert(FUSED || !STEP, "the step variant builds its index rows itself");
   __shared__ AttnSmem<NHB> sm;
 
@@ -208,14 +214,13 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     const int64_t first = sm.req[0] >= 0 ? (int64_t)max(sm.req[1], 0) : (int64_t)t;
     int64_t tt = (int64_t)t - w;
     if (tt >= first && kvp >= 0 && kvp < sti.max_pos && kvs >= 0 && kvs < num_slots)
-      kv_quant_store(kvv, kvrot, sti.cache + page_base(kvs >> ps, ps),
-                     (int)(kvs & ((1 << ps) - 1)), ps, lane);
+      kv_store_row<KV>(kvv, kvrot, sti.cache, kvs, ps, sti.kv_scale, lane);
     for (tt -= 4; tt >= first; tt -= 4) {
       const KvLane v = kv_lane_load(sti.kv + tt * kLatent, lane);
       const int64_t p = sti.positions[tt], sl = sti.slot_mapping[tt];
       if (p >= 0 && p < sti.max_pos && sl >= 0 && sl < num_slots)
-        kv_quant_store(v, rope_cs_load(sti.cos_sin + p * kRope, lane),
-                       sti.cache + page_base(sl >> ps, ps), (int)(sl & ((1 << ps) - 1)), ps, lane);
+        kv_store_row<KV>(v, rope_cs_load(sti.cos_sin + p * kRope, lane), sti.cache, sl, ps,
+                         sti.kv_scale, lane);
     }
   } else if constexpr (FUSED) {
     end = stage_combined(sm, tin, t, ps, tid);
@@ -271,18 +276,18 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
       __syncthreads();
     }
     const int nch = (n_blk + kChunk - 1) / kChunk;
-    RawSlot A, B;
-    load_raw_slot(A, cr, idx_at(sm.idx, row, n_blk), g);
-    load_raw_slot(B, cr, idx_at(sm.idx, kChunk + row, n_blk), g);
+    RawT<KV> A, B;
+    load_raw<KV>(A, cr, idx_at(sm.idx, row, n_blk), g);
+    load_raw<KV>(B, cr, idx_at(sm.idx, kChunk + row, n_blk), g);
     {  // prologue: stage chunk 0 and settle its probabilities
       f32x4 sacc[NHB];
       const uint64_t vmask = __ballot(A.valid);
       if constexpr (NHB == 2) {
-        const RecPtr nxt = rec_ptr(cr, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
-        stage2<true>(&sm.v[0][0][0], A, nxt, st, sacc, w, lane);
+        const RecPtr nxt = rec_ptr<KV>(cr, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
+        stage2<true, KV>(&sm.v[0][0][0], A, nxt, st, sacc, w, lane);
       } else {
-        stage_chunk<NHB>(&sm.v[0][0][0], A, st, sacc, w, l16, g);
-        load_raw_slot(A, cr, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
+        stage_chunk<NHB, KV>(&sm.v[0][0][0], A, st, sacc, w, l16, g);
+        load_raw<KV>(A, cr, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
       }
       float s[NHB][4], psum[NHB];
       softmax_local<NHB>(sm.p[0], sm.red[0], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
@@ -291,14 +296,14 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     }
     int i = 0;
     for (; i + 2 < nch; i += 2) {
-      pipelined_step<NHB>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cr, w, lane,
-                          scale_log2);
-      pipelined_step<NHB>(sm, 1, st, A, (i + 4) * kChunk + row, n_blk, cr, w, lane,
-                          scale_log2);
+      pipelined_step<NHB, KV>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cr, w, lane,
+                              scale_log2);
+      pipelined_step<NHB, KV>(sm, 1, st, A, (i + 4) * kChunk + row, n_blk, cr, w, lane,
+                              scale_log2);
     }
     if (i + 1 < nch) {
-      pipelined_step<NHB>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cr, w, lane,
-                          scale_log2);
+      pipelined_step<NHB, KV>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cr, w, lane,
+                              scale_log2);
       pv_last<NHB>(sm, 1, st, w, lane);
     } else {
       pv_last<NHB>(sm, 0, st, w, lane);
@@ -323,6 +328,14 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   const int h = h0 + hl;
   const float lt = sm.lsum[0][hl] + sm.lsum[1][hl] + sm.lsum[2][hl] + sm.lsum[3][hl];
   const float mr = (NHB == 2 && (g & 1)) ? st.m_run[NHB - 1] : st.m_run[0];
+  if constexpr (KV == kKvFp8E4m3) {
+    if (part_o) {  // the per-tensor scale of the values, before the partial leaves
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) st.o16[mb] *= o_scale;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) st.o32[mb] *= o_scale;
+    }
+  }
   if (part_o) {
     // one split of a row: the unnormalised O (relative to the reference mr), mr and the
     // denominator go to the workspace; the merge pass adds the sink and normalises
@@ -367,7 +380,8 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   const float M = fmaxf(mr, z2);
   const float f = exp2f(mr - M);
   const float den = lt * f + ((z2 == -INFINITY) ? 0.f : exp2f(z2 - M));
-  const float inv = den > 0.f ? f / den : 0.f;
+  float inv = den > 0.f ? f / den : 0.f;
+  if constexpr (KV == kKvFp8E4m3) inv *= o_scale;  // the per-tensor scale of the values
   uint16_t* orow = out + ((int64_t)t * H + h) * kNope;
   if constexpr (NHB == 2) {
     // A lane holds 4 consecutive output dims of one head per register group, so direct
@@ -485,34 +499,70 @@ size_t split_workspace_bytes(int T, int H, int splits) {
   return (size_t)T * splits * H * (kNope + 2) * sizeof(float);
 }
 
-template <bool FUSED, bool STEP>
-static hipError_t launch_items(const void* q, const uint8_t* cache, int num_pages, int ps,
-                               const int32_t* indices, int idx_stride, const int32_t* lens,
-                               const float* sinks, float softmax_scale, void* out, float* lse,
-                               int T, int H, int splits, int split_len, float* part_o,
-                               float* part_ml, const TopkIn& tin, const StepIn& sti,
-                               hipStream_t stream) {
+template <bool FUSED, bool STEP, int KV>
+static hipError_t launch_items_kv(const void* q, const uint8_t* cache, int num_pages, int ps,
+                                  const int32_t* indices, int idx_stride, const int32_t* lens,
+                                  const float* sinks, float scale_log2, float o_scale, void* out,
+                                  float* lse, int T, int H, int splits, int split_len,
+                                  float* part_o, float* part_ml, const TopkIn& tin,
+                                  const StepIn& sti, hipStream_t stream) {
   const int64_t num_slots = (int64_t)num_pages << ps;
-  const float scale_log2 = softmax_scale * kLog2e;
   const int items = T * splits;
-  if (H == 16) {
-    hipLaunchKernelGGL((sparse_mla_kernel<1, FUSED, STEP>), dim3(items), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), cache, num_slots, ps, indices, idx_stride, lens,
-                       sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, 1, splits,
-                       split_len, part_o, part_ml, tin, sti);
-  } else {
-    const int groups = H / 32;
+  // bf16 records take 72 registers a lane per chunk in flight (the FP8 ones 42): two
+  // chunks in flight beside Q for 32 heads would spill, so a workgroup takes 16 heads and
+  // the head groups of a token share the gathered records through their XCD's L2.
+  if (H == 16 || KV == kKvBf16) {
+    const int groups = H / 16;
     const int grid = groups == 1 ? items : 8 * groups * ((items + 7) / 8);
-    hipLaunchKernelGGL((sparse_mla_kernel<2, FUSED, STEP>), dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL((sparse_mla_kernel<1, FUSED, STEP, KV>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), cache, num_slots, ps, indices, idx_stride, lens,
                        sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, groups, splits,
-                       split_len, part_o, part_ml, tin, sti);
+                       split_len, part_o, part_ml, tin, sti, o_scale);
+  } else if constexpr (KV != kKvBf16) {
+    const int groups = H / 32;
+    const int grid = groups == 1 ? items : 8 * groups * ((items + 7) / 8);
+    hipLaunchKernelGGL((sparse_mla_kernel<2, FUSED, STEP, KV>), dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), cache, num_slots, ps, indices, idx_stride, lens,
+                       sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, groups, splits,
+                       split_len, part_o, part_ml, tin, sti, o_scale);
   }
   return hipGetLastError();
 }
 
+// The per-tensor fp8 cache folds its scale s into the scores' softmax scale and the
+// output: the codes are K and V up to that factor.
+template <bool FUSED, bool STEP>
+static hipError_t launch_items(const void* q, const uint8_t* cache, int num_pages, int ps,
+                               int kv_dtype, float kv_scale, const int32_t* indices,
+                               int idx_stride, const int32_t* lens, const float* sinks,
+                               float softmax_scale, void* out, float* lse, int T, int H,
+                               int splits, int split_len, float* part_o, float* part_ml,
+                               const TopkIn& tin, StepIn sti, hipStream_t stream) {
+  const float scale_log2 = softmax_scale * kLog2e;
+  sti.kv_scale = kv_scale;
+  switch (kv_dtype) {
+    case kKvFp8Ds:
+      return launch_items_kv<FUSED, STEP, kKvFp8Ds>(q, cache, num_pages, ps, indices, idx_stride,
+                                                    lens, sinks, scale_log2, 1.f, out, lse, T, H,
+                                                    splits, split_len, part_o, part_ml, tin, sti,
+                                                    stream);
+    case kKvBf16:
+      return launch_items_kv<FUSED, STEP, kKvBf16>(q, cache, num_pages, ps, indices, idx_stride,
+                                                   lens, sinks, scale_log2, 1.f, out, lse, T, H,
+                                                   splits, split_len, part_o, part_ml, tin, sti,
+                                                   stream);
+    case kKvFp8E4m3:
+      return launch_items_kv<FUSED, STEP, kKvFp8E4m3>(
+          q, cache, num_pages, ps, indices, idx_stride, lens, sinks, softmax_scale * kv_scale * kLog2e,
+          kv_scale, out, lse, T, H, splits, split_len, part_o, part_ml, tin, sti, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_attention_topk(const void* q, const uint8_t* cache, int num_pages,
-                                 int page_shift, const int32_t* topk, int topk_stride,
+                                 int page_shift, int kv_dtype, float kv_scale,
+                                 const int32_t* topk, int topk_stride,
                                  int topk_width, const int32_t* topk_lens, const int32_t* qsl,
                                  const int32_t* seq_lens, const int32_t* block_table, int bt_stride,
                                  int B, int top_k, int window, const float* sinks,
@@ -521,7 +571,8 @@ hipError_t launch_attention_topk(const void* q, const uint8_t* cache, int num_pa
   if (T == 0) return hipSuccess;
   const TopkIn tin{topk, topk_stride, topk_width, topk_lens, qsl, seq_lens, block_table,
                    bt_stride, B, top_k, window};
-  return launch_items<true, false>(q, cache, num_pages, page_shift, nullptr, 0, nullptr, sinks,
+  return launch_items<true, false>(q, cache, num_pages, page_shift, kv_dtype, kv_scale, nullptr,
+                                   0, nullptr, sinks,
                                    softmax_scale, out, lse, T, H, 1, kIdxBlock, nullptr, nullptr,
                                    tin, StepIn{}, stream);
 }
@@ -529,7 +580,8 @@ hipError_t launch_attention_topk(const void* q, const uint8_t* cache, int num_pa
 hipError_t launch_attention_step(void* q, const void* kv, const int64_t* positions,
                                  const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                                  const void* q_norm_weight, float eps, uint8_t* cache,
-                                 int num_pages, int page_shift, const int32_t* topk,
+                                 int num_pages, int page_shift, int kv_dtype, float kv_scale,
+                                 const int32_t* topk,
                                  int topk_stride, int topk_width, const int32_t* topk_lens,
                                  const int32_t* qsl, const int32_t* seq_lens,
                                  const int32_t* block_table, int bt_stride, int B, int top_k,
@@ -543,7 +595,8 @@ hipError_t launch_attention_step(void* q, const void* kv, const int64_t* positio
                    slot_mapping, cos_sin, max_pos, static_cast<const uint16_t*>(q_norm_weight),
                    eps, cache};
   if (splits <= 1)
-    return launch_items<true, true>(nullptr, nullptr, num_pages, page_shift, nullptr, 0, nullptr,
+    return launch_items<true, true>(nullptr, nullptr, num_pages, page_shift, kv_dtype, kv_scale,
+                                    nullptr, 0, nullptr,
                                     sinks, softmax_scale, out, lse, T, H, 1, kIdxBlock, nullptr,
                                     nullptr, tin, sti, stream);
   // pieces of the row as the split decode cuts a combined row of width
@@ -553,7 +606,8 @@ hipError_t launch_attention_step(void* q, const void* kv, const int64_t* positio
   const int split_len = per > 0 ? ((per + kChunk - 1) / kChunk) * kChunk : kChunk;
   float* part_o = static_cast<float*>(workspace);
   float* part_ml = part_o + (size_t)T * splits * H * kNope;
-  hipError_t e = launch_items<true, true>(nullptr, nullptr, num_pages, page_shift, nullptr, 0,
+  hipError_t e = launch_items<true, true>(nullptr, nullptr, num_pages, page_shift, kv_dtype,
+                                          kv_scale, nullptr, 0,
                                           nullptr, sinks, softmax_scale, out, lse, T, H, splits,
                                           split_len, part_o, part_ml, tin, sti, stream);
   if (e != hipSuccess) return e;
@@ -585,17 +639,19 @@ size_t attention_workspace_bytes(int T, int H, int width, bool prefill) {
 }
 
 hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, int page_shift,
-                            const int32_t* indices, int idx_stride, const int32_t* lens,
+                            int kv_dtype, float kv_scale, const int32_t* indices, int idx_stride, const int32_t* lens,
                             const float* sinks, float softmax_scale, void* out, float* lse, int T,
                             int H, bool prefill, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int splits = auto_splits(T, H, idx_stride, prefill);
   if (splits > 1 && workspace && workspace_bytes >= split_workspace_bytes(T, H, splits))
-    return launch_attention_split(q, cache, num_pages, page_shift, indices, idx_stride, lens,
+    return launch_attention_split(q, cache, num_pages, page_shift, kv_dtype, kv_scale, indices,
+                                  idx_stride, lens,
                                   sinks, softmax_scale, out, lse, T, H, splits, workspace, stream);
   const int whole = idx_stride > 0 ? idx_stride : 1;
-  return launch_items<false, false>(q, cache, num_pages, page_shift, indices, idx_stride, lens,
+  return launch_items<false, false>(q, cache, num_pages, page_shift, kv_dtype, kv_scale, indices,
+                                    idx_stride, lens,
                                     sinks, softmax_scale, out, lse, T, H, 1, whole, nullptr,
                                     nullptr, TopkIn{}, StepIn{}, stream);
 }
@@ -627,7 +683,8 @@ hipError_t noalloc_scratch(void** ptr) {
 }
 
 hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_pages,
-                                  int page_shift, const int32_t* indices, int idx_stride, const int32_t* lens,
+                                  int page_shift, int kv_dtype, float kv_scale,
+                                  const int32_t* indices, int idx_stride, const int32_t* lens,
                                   const float* sinks, float softmax_scale, void* out, float* lse,
                                   int T, int H, int splits, void* workspace, hipStream_t stream) {
   if (T == 0) return hipSuccess;
@@ -636,7 +693,8 @@ hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_p
   const int split_len = per > 0 ? ((per + kChunk - 1) / kChunk) * kChunk : kChunk;
   float* part_o = static_cast<float*>(workspace);
   float* part_ml = part_o + (size_t)T * splits * H * kNope;
-  hipError_t e = launch_items<false, false>(q, cache, num_pages, page_shift, indices, idx_stride,
+  hipError_t e = launch_items<false, false>(q, cache, num_pages, page_shift, kv_dtype, kv_scale,
+                                            indices, idx_stride,
                                             lens, sinks, softmax_scale, out, lse, T, H, splits,
                                             split_len, part_o, part_ml, TopkIn{}, StepIn{}, stream);
   if (e != hipSuccess) return e;

@@ -58,6 +58,7 @@ struct StepIn {
   const uint16_t* weight;
   float eps;
   uint8_t* cache;
+  float kv_scale;  // the fp8 cache's per-tensor scale (other dtypes: unused)
 };
 
 // Source of the (all-zero) record read for an invalid or absent slot, so that every
@@ -72,24 +73,139 @@ struct CacheRef {
   int ps;
 };
 
-struct RawSlot {
+template <int KV>
+constexpr int kv_record_bytes() {
+  return kv_record_bytes_of(KV);
+}
+
+// One lane's share of a slot's record (row l16 of its wave's 16, k-group g): the dims
+// 64u + 16g .. +15 (u = 0..7) and the rope dims 8g..8g+7, 32+8g..32+8g+7, the pieces the
+// MFMA fragments of the QK product take.
+template <int KV>
+struct RawT;
+template <>
+struct RawT<kKvFp8Ds> {
   uint4 nope[8];  // 128 codes: dims 64u + 16g .. 64u + 16g + 15 for u = 0..7
   uint4 rope[2];  // rope dims 8g..8g+7 and 32+8g..32+8g+7 (bf16)
   uint2 sc;       // the slot's 8 scale bytes
   int valid;
 };
+template <>
+struct RawT<kKvBf16> {
+  uint4 nope[16];  // dims 64u + 16g .. +7 in nope[2u], +8 .. +15 in nope[2u + 1] (bf16)
+  uint4 rope[2];   // rope dims 8g..8g+7 and 32+8g..32+8g+7 (bf16)
+  int valid;
+};
+template <>
+struct RawT<kKvFp8E4m3> {
+  uint4 nope[8];  // 128 codes: dims 64u + 16g .. 64u + 16g + 15 for u = 0..7
+  uint2 rope[2];  // codes of rope dims 8g..8g+7 and 32+8g..32+8g+7
+  int valid;
+};
+using RawSlot = RawT<kKvFp8Ds>;
 
-__device__ __forceinline__ void load_raw_slot(RawSlot& r, const CacheRef& c, int64_t slot, int g) {
-  r.valid = (slot >= 0 && slot < c.num_slots) ? 1 : 0;
-  const uint8_t* base = r.valid ? c.base + page_base(slot >> c.ps, c.ps) : g_zero_page;
-  const int off = r.valid ? (int)(slot & ((1 << c.ps) - 1)) : 0;
-  const uint8_t* np = base + nope_off(off) + 16 * g;
+// Where this lane's pieces of a slot's record live (the zero page for an invalid slot).
+struct RecPtr {
+  const uint8_t* np;  // value dims 16g.. of the record (u = 0 piece)
+  const uint8_t* rp;  // rope dims 8g.. of the record
+  const uint8_t* sp;  // scale bytes (packed record only)
+  int valid;
+};
+template <int KV = kKvFp8Ds>
+__device__ __forceinline__ RecPtr rec_ptr(const CacheRef& c, int64_t slot, int g) {
+  RecPtr p;
+  p.valid = (slot >= 0 && slot < c.num_slots) ? 1 : 0;
+  if constexpr (KV == kKvFp8Ds) {
+    const uint8_t* base = p.valid ? c.base + page_base(slot >> c.ps, c.ps) : g_zero_page;
+    const int off = p.valid ? (int)(slot & ((1 << c.ps) - 1)) : 0;
+    p.np = base + nope_off(off) + 16 * g;
+    p.rp = base + rope_off(off, c.ps) + 16 * g;
+    p.sp = base + scale_off(off, c.ps);
+  } else {
+    const uint8_t* base = p.valid ? c.base + slot * kv_record_bytes<KV>() : g_zero_page;
+    constexpr int esz = KV == kKvBf16 ? 2 : 1;  // bytes per value
+    p.np = base + esz * 16 * g;
+    p.rp = base + esz * (kNope + 8 * g);
+    p.sp = base;
+  }
+  return p;
+}
+
+// Loads of piece u of the value dims, and of the rope dims (and scales), from p.
+template <int KV>
+__device__ __forceinline__ void load_nope_piece(RawT<KV>& r, const RecPtr& p, int u) {
+  if constexpr (KV == kKvBf16) {
+    r.nope[2 * u] = *reinterpret_cast<const uint4*>(p.np + 128 * u);
+    r.nope[2 * u + 1] = *reinterpret_cast<const uint4*>(p.np + 128 * u + 16);
+  } else {
+    r.nope[u] = *reinterpret_cast<const uint4*>(p.np + 64 * u);
+  }
+}
+template <int KV>
+__device__ __forceinline__ void load_rope_piece(RawT<KV>& r, const RecPtr& p) {
+  if constexpr (KV == kKvFp8E4m3) {
+    r.rope[0] = *reinterpret_cast<const uint2*>(p.rp);
+    r.rope[1] = *reinterpret_cast<const uint2*>(p.rp + 32);
+  } else {
+    r.rope[0] = *reinterpret_cast<const uint4*>(p.rp);
+    r.rope[1] = *reinterpret_cast<const uint4*>(p.rp + 64);
+  }
+  if constexpr (KV == kKvFp8Ds) r.sc = *reinterpret_cast<const uint2*>(p.sp);
+  r.valid = p.valid;
+}
+
+template <int KV>
+__device__ __forceinline__ void load_raw(RawT<KV>& r, const CacheRef& c, int64_t slot, int g) {
+  if constexpr (KV == kKvFp8Ds) {
+    r.valid = (slot >= 0 && slot < c.num_slots) ? 1 : 0;
+    const uint8_t* base = r.valid ? c.base + page_base(slot >> c.ps, c.ps) : g_zero_page;
+    const int off = r.valid ? (int)(slot & ((1 << c.ps) - 1)) : 0;
+    const uint8_t* np = base + nope_off(off) + 16 * g;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) r.nope[u] = *reinterpret_cast<const uint4*>(np + 64 * u);
-  const uint8_t* rp = base + rope_off(off, c.ps) + 16 * g;
-  r.rope[0] = *reinterpret_cast<const uint4*>(rp);
-  r.rope[1] = *reinterpret_cast<const uint4*>(rp + 64);
-  r.sc = *reinterpret_cast<const uint2*>(base + scale_off(off, c.ps));
+    for (int u = 0; u < 8; ++u) r.nope[u] = *reinterpret_cast<const uint4*>(np + 64 * u);
+    const uint8_t* rp = base + rope_off(off, c.ps) + 16 * g;
+    r.rope[0] = *reinterpret_cast<const uint4*>(rp);
+    r.rope[1] = *reinterpret_cast<const uint4*>(rp + 64);
+    r.sc = *reinterpret_cast<const uint2*>(base + scale_off(off, c.ps));
+  } else {
+    const RecPtr p = rec_ptr<KV>(c, slot, g);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) load_nope_piece<KV>(r, p, u);
+    load_rope_piece<KV>(r, p);
+  }
+}
+__device__ __forceinline__ void load_raw_slot(RawSlot& r, const CacheRef& c, int64_t slot, int g) {
+  load_raw<kKvFp8Ds>(r, c, slot, g);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// The bf16 K fragments of piece u (dims 64u + 16g .. +7 and +8 .. +15) and of the rope
+// dims.  The packed record's codes are scaled by their block's 2^(byte-127) in the
+// conversion (exact); the per-tensor fp8 codes convert unscaled (exact: E4M3 values are
+// bf16 values) and the scale is applied to the scores and the output instead.
+template <int KV>
+__device__ __forceinline__ void k_frags(const RawT<KV>& r, int u, bf16x8& k0, bf16x8& k1) {
+  if constexpr (KV == kKvBf16) {
+    k0 = as_bf16x8(r.nope[2 * u]);
+    k1 = as_bf16x8(r.nope[2 * u + 1]);
+  } else {
+    float scale = 1.0f;
+    if constexpr (KV == kKvFp8Ds)
+      scale = e8m0_as_scale(((u < 4 ? r.sc.x : r.sc.y) >> (8 * (u & 3))) & 0xFF);
+    k0 = dequant8(r.nope[u].x, r.nope[u].y, scale);
+    k1 = dequant8(r.nope[u].z, r.nope[u].w, scale);
+  }
+}
+template <int KV>
+__device__ __forceinline__ void k_frags_rope(const RawT<KV>& r, bf16x8& k16, bf16x8& k17) {
+  if constexpr (KV == kKvFp8E4m3) {
+    k16 = dequant8(r.rope[0].x, r.rope[0].y, 1.0f);
+    k17 = dequant8(r.rope[1].x, r.rope[1].y, 1.0f);
+  } else {
+    k16 = as_bf16x8(r.rope[0]);
+    k17 = as_bf16x8(r.rope[1]);
+  }
 }
 
 // Entry jj of the staged index block (-1 past its end).  The read is unconditional (at a
@@ -207,25 +323,6 @@ __device__ __forceinline__ int stage_combined(SM& sm, const TopkIn& c, int64_t t
   return combine_rows<NT>(sm, c, t, ps, tid, xv, tl);
 }
 
-// Where this lane's pieces of a slot's record live (the zero page for an invalid slot).
-struct RecPtr {
-  const uint8_t* np;  // value codes, already offset by 16g
-  const uint8_t* rp;  // rope, already offset by 16g
-  const uint8_t* sp;  // scale bytes
-  int valid;
-};
-__device__ __forceinline__ RecPtr rec_ptr(const CacheRef& c, int64_t slot, int g) {
-  RecPtr p;
-  p.valid = (slot >= 0 && slot < c.num_slots) ? 1 : 0;
-  const uint8_t* base = p.valid ? c.base + page_base(slot >> c.ps, c.ps) : g_zero_page;
-  const int off = p.valid ? (int)(slot & ((1 << c.ps) - 1)) : 0;
-  p.np = base + nope_off(off) + 16 * g;
-  p.rp = base + rope_off(off, c.ps) + 16 * g;
-  p.sp = base + scale_off(off, c.ps);
-  return p;
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -294,8 +391,8 @@ struct AttnState {
 // Dequantise this lane's slot of a chunk (row 16w + l16, k-group g), stage its value
 // dims as bf16 into `vtile` and return S^T fragments: sacc[hb][i] = q.k of chunk row
 // 16w + 4g + i and head 16hb + l16.  Two accumulator chains per head block.
-template <int NHB>
-__device__ __forceinline__ void stage_chunk(__bf16* __restrict__ vtile, const RawSlot& cur,
+template <int NHB, int KV = kKvFp8Ds>
+__device__ __forceinline__ void stage_chunk(__bf16* __restrict__ vtile, const RawT<KV>& cur,
                                             const AttnState<NHB>& st, f32x4 (&sacc)[NHB], int w,
                                             int l16, int g) {
   f32x4 sa[NHB], sb[NHB];
@@ -307,10 +404,8 @@ __device__ __forceinline__ void stage_chunk(__bf16* __restrict__ vtile, const Ra
   const int vr = 16 * w + l16;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const uint32_t sbyte = ((u < 4 ? cur.sc.x : cur.sc.y) >> (8 * (u & 3))) & 0xFF;
-    const float scale = e8m0_as_scale(sbyte);
-    const bf16x8 k0 = dequant8(cur.nope[u].x, cur.nope[u].y, scale);
-    const bf16x8 k1 = dequant8(cur.nope[u].z, cur.nope[u].w, scale);
+    bf16x8 k0, k1;
+    k_frags<KV>(cur, u, k0, k1);
     *reinterpret_cast<bf16x8*>(vtile + v_off(vr, 8 * u + 2 * g)) = k0;
     *reinterpret_cast<bf16x8*>(vtile + v_off(vr, 8 * u + 2 * g + 1)) = k1;
 #pragma unroll
@@ -319,8 +414,8 @@ __device__ __forceinline__ void stage_chunk(__bf16* __restrict__ vtile, const Ra
       sb[hb] = mfma16(k1, st.qf[hb][2 * u + 1], sb[hb]);
     }
   }
-  const bf16x8 k16 = as_bf16x8(cur.rope[0]);
-  const bf16x8 k17 = as_bf16x8(cur.rope[1]);
+  bf16x8 k16, k17;
+  k_frags_rope<KV>(cur, k16, k17);
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     sa[hb] = mfma16(k16, st.qf[hb][16], sa[hb]);
@@ -377,8 +472,8 @@ __device__ __forceinline__ void pv_chunk(const __bf16* __restrict__ vtile,
 // been converted, so the record loads of a chunk go out one by one across the staging
 // work instead of as one burst: a burst fills the memory pipeline's queue and stalls
 // the wave's in-order issue until it drains.
-template <bool REFILL>
-__device__ __forceinline__ void stage2(__bf16* __restrict__ vn, RawSlot& cur, const RecPtr& nxt,
+template <bool REFILL, int KV = kKvFp8Ds>
+__device__ __forceinline__ void stage2(__bf16* __restrict__ vn, RawT<KV>& cur, const RecPtr& nxt,
                                        const AttnState<2>& st, f32x4 (&sacc)[2], int w,
                                        int lane) {
   const int l16 = lane & 15, g = lane >> 4;
@@ -399,11 +494,9 @@ __device__ __forceinline__ void stage2(__bf16* __restrict__ vn, RawSlot& cur, co
   }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const uint32_t sbyte = ((u < 4 ? cur.sc.x : cur.sc.y) >> (8 * (u & 3))) & 0xFF;
-    const float scale = e8m0_as_scale(sbyte);
-    const bf16x8 k0 = dequant8(cur.nope[u].x, cur.nope[u].y, scale);
-    const bf16x8 k1 = dequant8(cur.nope[u].z, cur.nope[u].w, scale);
-    if constexpr (REFILL) cur.nope[u] = *reinterpret_cast<const uint4*>(nxt.np + 64 * u);
+    bf16x8 k0, k1;
+    k_frags<KV>(cur, u, k0, k1);
+    if constexpr (REFILL) load_nope_piece<KV>(cur, nxt, u);
     *reinterpret_cast<bf16x8*>(wb[u & 1][0] + 64 * u) = k0;
     *reinterpret_cast<bf16x8*>(wb[u & 1][1] + 64 * u) = k1;
 #pragma unroll
@@ -412,14 +505,9 @@ __device__ __forceinline__ void stage2(__bf16* __restrict__ vn, RawSlot& cur, co
       sb[hb] = mfma16(k1, st.qf[hb][2 * u + 1], sb[hb]);
     }
   }
-  const bf16x8 k16 = as_bf16x8(cur.rope[0]);
-  const bf16x8 k17 = as_bf16x8(cur.rope[1]);
-  if constexpr (REFILL) {
-    cur.rope[0] = *reinterpret_cast<const uint4*>(nxt.rp);
-    cur.rope[1] = *reinterpret_cast<const uint4*>(nxt.rp + 64);
-    cur.sc = *reinterpret_cast<const uint2*>(nxt.sp);
-    cur.valid = nxt.valid;
-  }
+  bf16x8 k16, k17;
+  k_frags_rope<KV>(cur, k16, k17);
+  if constexpr (REFILL) load_rope_piece<KV>(cur, nxt);
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     sa[hb] = mfma16(k16, st.qf[hb][16], sa[hb]);
@@ -555,9 +643,9 @@ __device__ __forceinline__ void resolve_chunk(__bf16 (*__restrict__ ptile)[kPStr
 // chunk i+1's staging (raw -> vn, scores), so the matrix cores, the LDS and the VALU
 // work on both at once; then chunk i+1's softmax, the chunk's only barrier, and its
 // reference check.
-template <int NHB>
+template <int NHB, int KV = kKvFp8Ds>
 __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnState<NHB>& st,
-                                               RawSlot& raw, int pf_jj, int n_blk,
+                                               RawT<KV>& raw, int pf_jj, int n_blk,
                                                const CacheRef& cr, int w, int lane,
                                                float scale_log2) {
   const int l16 = lane & 15, g = lane >> 4;
@@ -569,8 +657,8 @@ __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnSt
     // staging + S first, so the scores are ready by the softmax; the P.V operands are
     // requested next and consumed last, so their MFMAs run across the barrier.
     const uint64_t vmask = __ballot(raw.valid);  // bit j (j < 16) = row 16w + j valid
-    const RecPtr nxt = rec_ptr(cr, next_slot, g);
-    stage2<true>(&sm.v[nb][0][0], raw, nxt, st, sacc, w, lane);
+    const RecPtr nxt = rec_ptr<KV>(cr, next_slot, g);
+    stage2<true, KV>(&sm.v[nb][0][0], raw, nxt, st, sacc, w, lane);
     PvFrags f;
     pv_reads2(&sm.v[cb][0][0], sm.p[cb], f, w, lane);
     // With one wave per SIMD the wave issues in order, so left to itself the softmax
@@ -589,10 +677,10 @@ __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnSt
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then up to eight VALU
     }
   } else {
-    stage_chunk<NHB>(&sm.v[nb][0][0], raw, st, sacc, w, l16, g);
+    stage_chunk<NHB, KV>(&sm.v[nb][0][0], raw, st, sacc, w, l16, g);
     pv_chunk<NHB>(&sm.v[cb][0][0], sm.p[cb], st, w, lane);
     const uint64_t vmask = __ballot(raw.valid);
-    load_raw_slot(raw, cr, next_slot, g);
+    load_raw<KV>(raw, cr, next_slot, g);
     softmax_local<NHB>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
   }
   __syncthreads();

@@ -21,6 +21,19 @@ constexpr int kBlocks = 8;
 constexpr int kRecord = 648;
 constexpr int kMaxPage = 256;  // page sizes accepted by the launchers: 32, 64 and 256 slots
 
+// kv-cache dtypes (the DSV4_KV_* values of the C header).  kKvFp8Ds: the packed record
+// below (E4M3 codes, UE8M0 block scales, bf16 rope; pages split by field).  kKvBf16 and
+// kKvFp8E4m3: one record of the 576 values per slot in dim order, records back to back
+// (slot s at byte s * record bytes): bf16 values (1152 B), or E4M3 codes (576 B) with one
+// scale for the whole cache (PR #43477 Key source excerpts: the SM100 backend's kv-cache
+// dtypes "bfloat16" / "fp8" and its (num_blocks, block_size, head_size) cache shape).
+constexpr int kKvFp8Ds = 0;
+constexpr int kKvBf16 = 1;
+constexpr int kKvFp8E4m3 = 2;
+constexpr int kv_record_bytes_of(int kv_dtype) {
+  return kv_dtype == kKvFp8Ds ? 648 : kv_dtype == kKvBf16 ? 2 * 576 : kv_dtype == kKvFp8E4m3 ? 576 : 0;
+}
+
 // A page of P = 2^ps slots holds the E4M3 codes [P][512] at byte 0, the bf16 rope rows
 // [P][64] at P*512 and the UE8M0 scales [P][8] at P*640.  Byte offsets of a page and of
 // the three fields of its slot `off`:

@@ -92,6 +92,21 @@ __device__ __forceinline__ KvLane kv_lane_load(const uint16_t* __restrict__ kr, 
   return v;
 }
 
+// Rope dims 512 + 8j .. +7 (a lane's KvLane::rope, j = lane & 7) rotated by the GPT-J pairs
+// of its position (rope_cs_load) and rounded to bf16.
+__device__ __forceinline__ uint4 rope_rotate8(uint4 r, const RopeCs& rot) {
+  const uint32_t ru[4] = {r.x, r.y, r.z, r.w};
+  const float cc[4] = {rot.c.x, rot.c.y, rot.c.z, rot.c.w};
+  const float sn[4] = {rot.s.x, rot.s.y, rot.s.z, rot.s.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    const float a = bf16_bits_to_f32(ru[e2] & 0xFFFF), b = bf16_bits_to_f32(ru[e2] >> 16);
+    o[e2] = pack_bf16x2(a * cc[e2] - b * sn[e2], a * sn[e2] + b * cc[e2]);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Quantises the row held by a wave (kv_lane_load) into the record of slot `off` of the
 // page at `base` (pages of 2^ps slots); `rot` holds the cos/sin values of the row's
 // position (rope_cs_load).
@@ -136,17 +151,59 @@ __device__ __forceinline__ void kv_quant_store(const KvLane& v, const RopeCs& ro
   if ((lane & 7) == 0) base[scale_off(off, ps) + (lane >> 3)] = (uint8_t)(e + 127);
 
   // rope dims 512 + 8*lane .. +7 for lanes 0..7, stored rotated (bf16)
-  if (lane < 8) {
-    const uint32_t ru[4] = {v.rope.x, v.rope.y, v.rope.z, v.rope.w};
-    const float cc[4] = {rot.c.x, rot.c.y, rot.c.z, rot.c.w};
-    const float sn[4] = {rot.s.x, rot.s.y, rot.s.z, rot.s.w};
-    uint32_t o[4];
+  if (lane < 8) *reinterpret_cast<uint4*>(base + rope_off(off, ps) + 16 * lane) = rope_rotate8(v.rope, rot);
+}
+
+// The other kv-cache dtypes (PR #43477 Key source excerpts: the SM100 backend's
+// "bfloat16" and "fp8" caches of shape (num_blocks, block_size, head_size)): one record
+// of the 576 values per slot in dim order, `rec` pointing at the slot's record.  The
+// rope dims are rotated and rounded to bf16 exactly as for the packed record.  bf16:
+// the values' bits.  fp8 (one scale s per cache): e4m3(z / s) for every dim, the
+// quotient correctly rounded in fp32, saturated to +-448, converted with gfx950's
+// round-to-nearest-even.  All 64 lanes must take part (lanes 0..7 store the rope dims).
+__device__ __forceinline__ void kv_store_bf16(const KvLane& v, const RopeCs& rot,
+                                              uint8_t* __restrict__ rec, int lane) {
+  *reinterpret_cast<uint4*>(rec + 16 * lane) = v.nope;
+  if (lane < 8) *reinterpret_cast<uint4*>(rec + 2 * kNope + 16 * lane) = rope_rotate8(v.rope, rot);
+}
+
+// 8 bf16 values (memory order) -> 8 E4M3 codes of z / s.
+__device__ __forceinline__ uint2 e4m3_quot8(uint4 z, float s) {
+  const uint32_t u[4] = {z.x, z.y, z.z, z.w};
+  float k[8];
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const float a = bf16_bits_to_f32(ru[e2] & 0xFFFF), b = bf16_bits_to_f32(ru[e2] >> 16);
-      o[e2] = pack_bf16x2(a * cc[e2] - b * sn[e2], a * sn[e2] + b * cc[e2]);
-    }
-    *reinterpret_cast<uint4*>(base + rope_off(off, ps) + 16 * lane) = make_uint4(o[0], o[1], o[2], o[3]);
+  for (int e = 0; e < 4; ++e) {
+    k[2 * e] = fminf(fmaxf(bf16_bits_to_f32(u[e] & 0xFFFF) / s, -448.f), 448.f);
+    k[2 * e + 1] = fminf(fmaxf(bf16_bits_to_f32(u[e] >> 16) / s, -448.f), 448.f);
+  }
+  uint32_t codes[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int c = 0;
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(k[4 * h + 0], k[4 * h + 1], c, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(k[4 * h + 2], k[4 * h + 3], c, true);
+    codes[h] = (uint32_t)c;
+  }
+  return make_uint2(codes[0], codes[1]);
+}
+
+__device__ __forceinline__ void kv_store_fp8(const KvLane& v, const RopeCs& rot, float s,
+                                             uint8_t* __restrict__ rec, int lane) {
+  *reinterpret_cast<uint2*>(rec + 8 * lane) = e4m3_quot8(v.nope, s);
+  if (lane < 8) *reinterpret_cast<uint2*>(rec + kNope + 8 * lane) = e4m3_quot8(rope_rotate8(v.rope, rot), s);
+}
+
+// The row writer of a cache dtype (packed FP8/UE8M0, bf16, or fp8 with scale s)
+// for slot `slot` of a cache of pages of 2^ps slots.
+template <int KV>
+__device__ __forceinline__ void kv_store_row(const KvLane& v, const RopeCs& rot, uint8_t* cache,
+                                             int64_t slot, int ps, float s, int lane) {
+  if constexpr (KV == kKvFp8Ds) {
+    kv_quant_store(v, rot, cache + page_base(slot >> ps, ps), (int)(slot & ((1 << ps) - 1)), ps, lane);
+  } else if constexpr (KV == kKvBf16) {
+    kv_store_bf16(v, rot, cache + slot * (2 * kLatent), lane);
+  } else {
+    kv_store_fp8(v, rot, s, cache + slot * kLatent, lane);
   }
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device.hpp"
+
 namespace dsv4 {
 
 // log2 of a supported page size (32, 64 or 256 slots), -1 for any other.
@@ -43,17 +45,22 @@ hipError_t launch_indexer_topk(const float* logits, int logits_stride, const int
 hipError_t launch_insert(void* q, const void* kv, const int64_t* positions,
                          const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                          const void* weight, float eps, uint8_t* cache, int num_pages,
-                         int page_shift, int T, int H, hipStream_t stream);
+                         int page_shift, int kv_dtype, float kv_scale, int T, int H,
+                         hipStream_t stream);
 
-hipError_t launch_gather(const uint8_t* cache, int num_pages, int page_shift, const int32_t* slots,
-                         int n, void* out, hipStream_t stream);
+hipError_t launch_gather(const uint8_t* cache, int num_pages, int page_shift, int kv_dtype,
+                         float kv_scale, const int32_t* slots, int n, void* out,
+                         hipStream_t stream);
+
+// The attention launchers below read a cache of dtype kv_dtype (kKvFp8Ds, kKvBf16 or
+// kKvFp8E4m3; kv_scale is the fp8 cache's per-tensor scale, ignored otherwise).
 
 // Decode / prefill over index rows from memory.  With a workspace of at least
 // attention_workspace_bytes(T, H, idx_stride, prefill) bytes the call may cut rows into
 // pieces (a decode batch too small to fill the compute units); workspace may be NULL.
 hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, int page_shift,
-                            const int32_t* indices, int idx_stride, const int32_t* lens,
-                            const float* sinks, float softmax_scale, void* out, float* lse,
+                            int kv_dtype, float kv_scale, const int32_t* indices, int idx_stride,
+                            const int32_t* lens, const float* sinks, float softmax_scale, void* out, float* lse,
                             int T, int H, bool prefill, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 // Pieces per row the decode picks for T tokens, H heads and rows of `width` entries
@@ -64,7 +71,8 @@ size_t attention_workspace_bytes(int T, int H, int width, bool prefill);
 // Split-slot decode: the row of each token is cut into `splits` 64-aligned pieces whose
 // partials go to `workspace` (split_workspace_bytes(T, H, splits) bytes) and are merged.
 hipError_t launch_attention_split(const void* q, const uint8_t* cache, int num_pages,
-                                  int page_shift, const int32_t* indices, int idx_stride, const int32_t* lens,
+                                  int page_shift, int kv_dtype, float kv_scale,
+                                  const int32_t* indices, int idx_stride, const int32_t* lens,
                                   const float* sinks, float softmax_scale, void* out, float* lse,
                                   int T, int H, int splits, void* workspace, hipStream_t stream);
 size_t split_workspace_bytes(int T, int H, int splits);
@@ -78,8 +86,8 @@ hipError_t noalloc_scratch(void** ptr);
 // Decode that builds each token's combined index row itself from the combine step's
 // inputs (top_k + window <= 4096).
 hipError_t launch_attention_topk(const void* q, const uint8_t* cache, int num_pages,
-                                 int page_shift, const int32_t* topk, int topk_stride,
-                                 int topk_width, const int32_t* topk_lens, const int32_t* qsl,
+                                 int page_shift, int kv_dtype, float kv_scale, const int32_t* topk,
+                                 int topk_stride, int topk_width, const int32_t* topk_lens, const int32_t* qsl,
                                  const int32_t* seq_lens, const int32_t* block_table, int bt_stride,
                                  int B, int top_k, int window, const float* sinks,
                                  float softmax_scale, void* out, float* lse, int T, int H,
@@ -91,8 +99,9 @@ hipError_t launch_attention_topk(const void* q, const uint8_t* cache, int num_pa
 hipError_t launch_attention_step(void* q, const void* kv, const int64_t* positions,
                                  const int64_t* slot_mapping, const float* cos_sin, int max_pos,
                                  const void* q_norm_weight, float eps, uint8_t* cache,
-                                 int num_pages, int page_shift, const int32_t* topk,
-                                 int topk_stride, int topk_width, const int32_t* topk_lens,
+                                 int num_pages, int page_shift, int kv_dtype, float kv_scale,
+                                 const int32_t* topk, int topk_stride, int topk_width,
+                                 const int32_t* topk_lens,
                                  const int32_t* qsl, const int32_t* seq_lens,
                                  const int32_t* block_table, int bt_stride, int B, int top_k,
                                  int window, const float* sinks, float softmax_scale, void* out,

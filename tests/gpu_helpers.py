@@ -32,14 +32,16 @@ def bits_to_f64(bits):
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def oracle_cache(wl, num_pages=None):
-    """Host cache holding the workload's context rows, inserted by the oracle."""
+def oracle_cache(wl, num_pages=None, kv_dtype=0, kv_scale=1.0):
+    """Host cache (pages of 64 slots, dtype kv_dtype) holding the workload's context rows,
+    inserted by the oracle."""
     npg = wl["num_pages"] if num_pages is None else num_pages
-    cache = np.zeros(npg * 64 * 648, np.uint8)
+    cache = np.zeros(npg * 64 * oracle.kv_record_bytes(kv_dtype), np.uint8)
     T = wl["ctx_kv"].shape[0]
     q0 = np.zeros((T, 0, 576), np.uint16)
     oracle.kv_insert(q0, wl["ctx_kv"], wl["ctx_pos"], wl["ctx_slot"], wl["cos_sin"],
-                     np.zeros(576, np.uint16), 1e-6, cache, npg, 64, inplace=True)
+                     np.zeros(576, np.uint16), 1e-6, cache, npg, 64, inplace=True,
+                     kv_dtype=kv_dtype, kv_scale=kv_scale)
     return cache
 
 

@@ -28,8 +28,11 @@ def test_status_strings_and_page_bytes(dsv4):
     lib = dsv4.library()
     assert lib.dsv4_status_str(0) == b"DSV4_OK"
     assert lib.dsv4_status_str(4) == b"DSV4_ERR_UNSUPPORTED"
-    assert lib.dsv4_cache_page_bytes(64) == 64 * 648
-    assert lib.dsv4_cache_page_bytes(0) == 0
+    assert lib.dsv4_cache_page_bytes(64, 0) == 64 * 648
+    assert lib.dsv4_cache_page_bytes(32, 1) == 32 * 1152
+    assert lib.dsv4_cache_page_bytes(256, 2) == 256 * 576
+    assert lib.dsv4_cache_page_bytes(0, 0) == 0
+    assert lib.dsv4_cache_page_bytes(64, 3) == 0
 
 
 def _fake(n=1 << 20):
@@ -43,14 +46,14 @@ def _fake(n=1 << 20):
 def test_attention_validation(dsv4):
     lib = dsv4.library()
     keep, p = _fake()
-    args = dict(q=p, cache=p, num_pages=4, page_size=64, idx=p, stride=128, lens=p, sinks=None,
-                scale=0.04, out=p, lse=None, T=2, H=16)
+    args = dict(q=p, cache=p, num_pages=4, page_size=64, kvd=0, kvs=1.0, idx=p, stride=128,
+                lens=p, sinks=None, scale=0.04, out=p, lse=None, T=2, H=16)
 
     def call(fn, **kw):
         a = dict(args, ws=None, wsb=0, **kw)
-        return fn(a["q"], a["cache"], a["num_pages"], a["page_size"], a["idx"], a["stride"],
-                  a["lens"], a["sinks"], a["scale"], a["out"], a["lse"], a["T"], a["H"], a["ws"],
-                  a["wsb"], None)
+        return fn(a["q"], a["cache"], a["num_pages"], a["page_size"], a["kvd"], a["kvs"],
+                  a["idx"], a["stride"], a["lens"], a["sinks"], a["scale"], a["out"], a["lse"],
+                  a["T"], a["H"], a["ws"], a["wsb"], None)
 
     for fn in (lib.dsv4_sparse_mla_decode, lib.dsv4_sparse_mla_prefill):
         assert call(fn, H=24) == 4 and b"H = 24" in lib.dsv4_last_error()
@@ -62,6 +65,13 @@ def test_attention_validation(dsv4):
         assert call(fn, num_pages=-3) == 2
         assert call(fn, out=ctypes.c_void_p(p.value + 2)) == 3
         assert call(fn, T=0, q=None) == 0 and lib.dsv4_last_error() == b""
+        # cache dtypes: unknown -> unsupported; the fp8 cache's scale must be in range
+        assert call(fn, kvd=3) == 4 and b"kv_dtype" in lib.dsv4_last_error()
+        assert call(fn, kvd=-1) == 4
+        for bad in (0.0, -1.0, float("nan"), float("inf"), 2.0 ** -70, 2.0 ** 70):
+            assert call(fn, kvd=2, kvs=bad) == 2 and b"kv_scale" in lib.dsv4_last_error()
+        assert call(fn, kvd=1, kvs=0.0, T=0, q=None) == 0   # the scale is the fp8 cache's only
+        assert call(fn, kvd=2, kvs=0.5, T=0, q=None) == 0
 
 
 def test_attention_workspace_contract(dsv4):
@@ -87,9 +97,9 @@ def test_attention_workspace_contract(dsv4):
         a = dict(q=p, cache=p, num_pages=4, page_size=64, idx=p, stride=4096, lens=p, sinks=None,
                  scale=0.04, out=p, lse=None, T=2, H=16, ws=p, wsb=need)
         a.update(kw)
-        return fn(a["q"], a["cache"], a["num_pages"], a["page_size"], a["idx"], a["stride"],
-                  a["lens"], a["sinks"], a["scale"], a["out"], a["lse"], a["T"], a["H"], a["ws"],
-                  a["wsb"], None)
+        return fn(a["q"], a["cache"], a["num_pages"], a["page_size"], 0, 1.0, a["idx"],
+                  a["stride"], a["lens"], a["sinks"], a["scale"], a["out"], a["lse"], a["T"],
+                  a["H"], a["ws"], a["wsb"], None)
 
     for fn in (lib.dsv4_sparse_mla_decode, lib.dsv4_sparse_mla_prefill):
         assert call(fn, T=0, q=None) == 0
@@ -108,17 +118,18 @@ def test_noalloc_split_decode_validation(dsv4):
     keep, p = _fake()
 
     def call(**kw):
-        a = dict(T=2, H=16, splits=4, stride=128)
+        a = dict(T=2, H=16, splits=4, stride=128, kvd=0, kvs=1.0)
         a.update(kw)
         return lib.dsv4_sparse_mla_decode_split_noalloc(
-            p, p, 4, 64, p, a["stride"], p, None, 0.04, p, None, a["T"], a["H"], a["splits"],
-            None)
+            p, p, 4, 64, a["kvd"], a["kvs"], p, a["stride"], p, None, 0.04, p, None, a["T"],
+            a["H"], a["splits"], None)
 
     assert dsv4.NOALLOC_SCRATCH_BYTES == 32 << 20
     assert lib.dsv4_sparse_mla_split_workspace_bytes(64, 128, 8) > dsv4.NOALLOC_SCRATCH_BYTES
     assert call(T=64, H=128, splits=8) == 5 and b"static scratch" in lib.dsv4_last_error()
     assert call(splits=0) == 2 and call(splits=65) == 2
     assert call(H=24) == 4
+    assert call(kvd=5) == 4 and call(kvd=2, kvs=-2.0) == 2
     assert call(T=0) == 0
 
 
@@ -131,9 +142,10 @@ def test_split_decode_validation(dsv4):
 
     def call(**kw):
         a = dict(q=p, cache=p, num_pages=4, page_size=64, idx=p, stride=128, lens=p, sinks=None,
-                 scale=0.04, out=p, lse=None, T=2, H=16, splits=4, ws=p, wsb=need)
+                 scale=0.04, out=p, lse=None, T=2, H=16, splits=4, ws=p, wsb=need, kvd=0, kvs=1.0)
         a.update(kw)
         return lib.dsv4_sparse_mla_decode_split(a["q"], a["cache"], a["num_pages"], a["page_size"],
+                                                a["kvd"], a["kvs"],
                                                 a["idx"], a["stride"], a["lens"], a["sinks"],
                                                 a["scale"], a["out"], a["lse"], a["T"], a["H"],
                                                 a["splits"], a["ws"], a["wsb"], None)
@@ -145,6 +157,7 @@ def test_split_decode_validation(dsv4):
     assert call(ws=ctypes.c_void_p(p.value + 4)) == 5
     assert call(H=24) == 4
     assert call(q=None) == 1
+    assert call(kvd=7) == 4 and call(kvd=2, kvs=float("nan")) == 2
     assert call(T=0, q=None) == 0
     assert lib.dsv4_status_str(5) == b"DSV4_ERR_WORKSPACE"
 
@@ -235,10 +248,10 @@ def test_decode_topk_validation(dsv4):
     def call(**kw):
         a = dict(q=p, cache=p, npg=4, P=64, topk=p, ts=2048, tw=2048, tl=None, qsl=p, sl=p, bt=p,
                  bts=8, B=2, top_k=2048, window=128, sinks=None, scale=0.04, out=p, lse=None, T=2,
-                 H=128)
+                 H=128, kvd=0, kvs=1.0)
         a.update(kw)
         return lib.dsv4_sparse_mla_decode_topk(
-            a["q"], a["cache"], a["npg"], a["P"], a["topk"], a["ts"], a["tw"], a["tl"], a["qsl"],
+            a["q"], a["cache"], a["npg"], a["P"], a["kvd"], a["kvs"], a["topk"], a["ts"], a["tw"], a["tl"], a["qsl"],
             a["sl"], a["bt"], a["bts"], a["B"], a["top_k"], a["window"], a["sinks"], a["scale"],
             a["out"], a["lse"], a["T"], a["H"], None)
 
@@ -248,6 +261,7 @@ def test_decode_topk_validation(dsv4):
     assert call(top_k=3000) == 2
     assert call(qsl=None) == 1
     assert call(out=ctypes.c_void_p(p.value + 2)) == 3
+    assert call(kvd=3) == 4 and call(kvd=2, kvs=0.0) == 2
     assert call(T=0) == 0
 
 
@@ -258,11 +272,11 @@ def test_decode_step_validation(dsv4):
     def call(**kw):
         a = dict(q=p, kv=p, pos=p, sm=p, cs=p, maxp=100, w=p, eps=1e-6, cache=p, npg=4, P=64,
                  topk=p, ts=2048, tw=2048, tl=None, qsl=p, sl=p, bt=p, bts=8, B=2, top_k=2048,
-                 window=128, sinks=None, scale=0.04, out=p, lse=None, T=2, H=128)
+                 window=128, sinks=None, scale=0.04, out=p, lse=None, T=2, H=128, kvd=0, kvs=1.0)
         a.update(kw)
         return lib.dsv4_sparse_mla_decode_step(
             a["q"], a["kv"], a["pos"], a["sm"], a["cs"], a["maxp"], a["w"], a["eps"], a["cache"],
-            a["npg"], a["P"], a["topk"], a["ts"], a["tw"], a["tl"], a["qsl"], a["sl"], a["bt"],
+            a["npg"], a["P"], a["kvd"], a["kvs"], a["topk"], a["ts"], a["tw"], a["tl"], a["qsl"], a["sl"], a["bt"],
             a["bts"], a["B"], a["top_k"], a["window"], a["sinks"], a["scale"], a["out"], a["lse"],
             a["T"], a["H"], None)
 
@@ -277,6 +291,7 @@ def test_decode_step_validation(dsv4):
     assert call(cs=None) == 1
     assert call(q=ctypes.c_void_p(p.value + 8)) == 3
     assert call(pos=ctypes.c_void_p(p.value + 4)) == 3
+    assert call(kvd=3) == 4 and call(kvd=2, kvs=float("inf")) == 2
     assert call(T=0) == 0
 
 
@@ -289,7 +304,7 @@ def test_decode_step_split_validation(dsv4):
         a = dict(S=4, ws=p, wsb=need, T=2, H=128, window=128, P=64)
         a.update(kw)
         return lib.dsv4_sparse_mla_decode_step_split(
-            p, p, p, p, p, 100, p, 1e-6, p, 4, a["P"], p, 2048, 2048, None, p, p, p, 8, 2, 2048,
+            p, p, p, p, p, 100, p, 1e-6, p, 4, a["P"], 0, 1.0, p, 2048, 2048, None, p, p, p, 8, 2, 2048,
             a["window"], None, 0.04, p, None, a["T"], a["H"], a["S"], a["ws"], a["wsb"], None)
 
     assert call(S=0) == 4 and call(S=65) == 4
@@ -311,10 +326,12 @@ def test_insert_and_gather_validation(dsv4):
     keep, p = _fake()
 
     def ins(**kw):
-        a = dict(q=p, kv=p, pos=p, sm=p, cs=p, maxp=100, w=p, eps=1e-6, cache=p, npg=4, P=64, T=4, H=8)
+        a = dict(q=p, kv=p, pos=p, sm=p, cs=p, maxp=100, w=p, eps=1e-6, cache=p, npg=4, P=64, T=4,
+                 H=8, kvd=0, kvs=1.0)
         a.update(kw)
         return lib.dsv4_kv_insert(a["q"], a["kv"], a["pos"], a["sm"], a["cs"], a["maxp"], a["w"],
-                                  a["eps"], a["cache"], a["npg"], a["P"], a["T"], a["H"], None)
+                                  a["eps"], a["cache"], a["npg"], a["P"], a["kvd"], a["kvs"],
+                                  a["T"], a["H"], None)
 
     assert ins(H=129) == 2
     assert ins(P=16) == 4
@@ -323,11 +340,14 @@ def test_insert_and_gather_validation(dsv4):
     assert ins(q=None, w=None, H=0, kv=None) == 1
     assert ins(eps=-1.0) == 2
     assert ins(q=ctypes.c_void_p(p.value + 8)) == 3
-    assert ins(T=0) == 0
-    assert lib.dsv4_gather_dequant(p, 4, 64, None, 5, p, None) == 1
-    assert lib.dsv4_gather_dequant(p, 4, 64, p, -1, p, None) == 2
-    assert lib.dsv4_gather_dequant(p, 4, 48, p, 5, p, None) == 4
-    assert lib.dsv4_gather_dequant(p, 4, 64, p, 0, p, None) == 0
+    assert ins(kvd=4) == 4 and ins(kvd=2, kvs=0.0) == 2 and b"kv_scale" in lib.dsv4_last_error()
+    assert ins(T=0) == 0 and ins(T=0, kvd=1) == 0
+    assert lib.dsv4_gather_dequant(p, 4, 64, 0, 1.0, None, 5, p, None) == 1
+    assert lib.dsv4_gather_dequant(p, 4, 64, 0, 1.0, p, -1, p, None) == 2
+    assert lib.dsv4_gather_dequant(p, 4, 48, 0, 1.0, p, 5, p, None) == 4
+    assert lib.dsv4_gather_dequant(p, 4, 64, 9, 1.0, p, 5, p, None) == 4
+    assert lib.dsv4_gather_dequant(p, 4, 64, 2, -1.0, p, 5, p, None) == 2
+    assert lib.dsv4_gather_dequant(p, 4, 64, 0, 1.0, p, 0, p, None) == 0
 
 
 def test_binding_rejects_host_tensors(dsv4):

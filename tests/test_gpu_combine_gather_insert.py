@@ -205,7 +205,8 @@ def test_insert_without_rope_rows_touches_nothing(dsv4):
     st = dsv4.library().dsv4_kv_insert(vp(qd.data_ptr()), vp(kv.data_ptr()), vp(pos.data_ptr()),
                                        vp(slots.data_ptr()), vp(table.data_ptr()), 0,
                                        vp(w.data_ptr()), ctypes.c_float(1e-6),
-                                       vp(cache.data_ptr()), num_pages, P, T, H, None)
+                                       vp(cache.data_ptr()), num_pages, P, 0, ctypes.c_float(1.0),
+                                       T, H, None)
     torch.cuda.synchronize()
     assert st == 0
     assert np.array_equal(host_bits(qd), q0) and np.array_equal(cache.cpu().numpy(), cache0)

@@ -26,16 +26,20 @@ def _same(a, b):
     return torch.equal(a, b)
 
 
+def _kv(c):
+    return dict(kv_dtype=c.get("kvd", 0), kv_scale=c.get("kvs", 1.0))
+
+
 def _run_two(dsv4, c, q0, cache0):
     q, cache = q0.clone(), cache0.clone()
     T, H = q.shape[0], q.shape[1]
     dsv4.dsv4_kv_insert(q, c["kv"], c["pos"], c["slots"], c["cos_sin"], c["w"], 1e-6, cache,
-                        page_size=c["P"])
+                        page_size=c["P"], **_kv(c))
     out = torch.full((T, H, 512), 3.0, dtype=torch.bfloat16, device="cuda")
     lse = torch.full((T, H), 3.0, dtype=torch.float32, device="cuda")
     dsv4.dsv4_sparse_mla_decode_topk(q, cache, c["topk"], c["tl"], c["qsl"], c["sl"], c["bt"],
                                      c["top_k"], c["window"], c["sinks"], c["scale"], out, lse,
-                                     page_size=c["P"])
+                                     page_size=c["P"], **_kv(c))
     return q, cache, out, lse
 
 
@@ -48,12 +52,12 @@ def _run_step(dsv4, c, q0, cache0, out=None, lse=None):
     dsv4.dsv4_sparse_mla_decode_step(q, c["kv"], c["pos"], c["slots"], c["cos_sin"], c["w"], 1e-6,
                                      cache, c["topk"], c["tl"], c["qsl"], c["sl"], c["bt"],
                                      c["top_k"], c["window"], c["sinks"], c["scale"], out, lse,
-                                     page_size=c["P"])
+                                     page_size=c["P"], **_kv(c))
     return q, cache, out, lse
 
 
 def _random_case(rng, P, H, qmax, B=None, top_k=None, window=None, max_len=2500,
-                 full_rows=False):
+                 full_rows=False, kv_dtype=0, kv_scale=1.0):
     B = int(rng.integers(1, 5)) if B is None else B
     top_k = int(rng.choice([16, 300, 2048])) if top_k is None else top_k
     window = int(rng.choice([0, 1, 4, 128])) if window is None else window
@@ -85,7 +89,7 @@ def _random_case(rng, P, H, qmax, B=None, top_k=None, window=None, max_len=2500,
     pos[T - 2], slots[T - 2] = 7, (npg - 1) * P + 3
     pos[T - 1], slots[T - 1] = -1, (npg - 1) * P + 4  # skipped: q and cache untouched
     # garbage everywhere, then the context rows (positions before the new tokens)
-    cache = rng.integers(0, 256, size=npg * P * 648, dtype=np.uint8)
+    cache = rng.integers(0, 256, size=npg * P * oracle.kv_record_bytes(kv_dtype), dtype=np.uint8)
     ctx_b = np.concatenate([np.full(L - ql, b) for b, (L, ql) in enumerate(zip(seq_lens, qlens))])
     ctx_p = np.concatenate([np.arange(L - ql) for L, ql in zip(seq_lens, qlens)]).astype(np.int64)
     keep = bt[ctx_b, ctx_p // P] >= 0
@@ -93,7 +97,8 @@ def _random_case(rng, P, H, qmax, B=None, top_k=None, window=None, max_len=2500,
     cos_sin = rope_table(max_len + 100)
     oracle.kv_insert(np.zeros((ctx_s.size, 0, 576), np.uint16),
                      bf16_normal(rng, (ctx_s.size, 576)), ctx_p[keep], ctx_s, cos_sin,
-                     np.zeros(576, np.uint16), 1e-6, cache, npg, P, inplace=True)
+                     np.zeros(576, np.uint16), 1e-6, cache, npg, P, inplace=True,
+                     kv_dtype=kv_dtype, kv_scale=kv_scale)
     if full_rows:  # distinct valid picks: every row as long as top_k allows
         topk = np.stack([rng.permutation(max_len - 200 - 1)[:top_k] for _ in range(T)]).astype(np.int32)
     else:
@@ -106,7 +111,9 @@ def _random_case(rng, P, H, qmax, B=None, top_k=None, window=None, max_len=2500,
              pos=pos, slots=slots, cos_sin=cos_sin, w=bf16_normal(rng, (576,), mean=1.0, std=0.1),
              topk=topk, tl=tl, qsl=qsl, sl=seq_lens, bt=bt, sinks=sinks,
              q=bf16_normal(rng, (T, H, 576)), cache=cache)
+    h.update(kvd=kv_dtype, kvs=kv_scale)
     c = dict(P=P, top_k=top_k, window=window, scale=1 / 24, B=B, T=T, kv=dev_bf16(h["kv"]),
+             kvd=kv_dtype, kvs=kv_scale,
              pos=dev(pos), slots=dev(slots), cos_sin=dev(cos_sin, np.float32), w=dev_bf16(h["w"]),
              topk=dev(topk), tl=None if tl is None else dev(tl), qsl=dev(qsl), sl=dev(seq_lens),
              bt=dev(bt), sinks=None if sinks is None else dev(sinks))
