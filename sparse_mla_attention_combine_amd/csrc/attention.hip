@@ -276,18 +276,22 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
       __syncthreads();
     }
     const int nch = (n_blk + kChunk - 1) / kChunk;
+    // Chunks of records in flight per lane: two (buffers A and B, odd chunks in B), or
+    // one for bf16 records at 32 heads (72 registers a chunk beside Q for 32 heads).
+    constexpr int kAhead = (KV == kKvBf16 && NHB == 2) ? 1 : 2;
     RawT<KV> A, B;
+    RawT<KV>& odd = kAhead == 2 ? B : A;
     load_raw<KV>(A, cr, idx_at(sm.idx, row, n_blk), g);
-    load_raw<KV>(B, cr, idx_at(sm.idx, kChunk + row, n_blk), g);
+    if constexpr (kAhead == 2) load_raw<KV>(B, cr, idx_at(sm.idx, kChunk + row, n_blk), g);
     {  // prologue: stage chunk 0 and settle its probabilities
       f32x4 sacc[NHB];
       const uint64_t vmask = __ballot(A.valid);
       if constexpr (NHB == 2) {
-        const RecPtr nxt = rec_ptr<KV>(cr, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
+        const RecPtr nxt = rec_ptr<KV>(cr, idx_at(sm.idx, kAhead * kChunk + row, n_blk), g);
         stage2<true, KV>(&sm.v[0][0][0], A, nxt, st, sacc, w, lane);
       } else {
         stage_chunk<NHB, KV>(&sm.v[0][0][0], A, st, sacc, w, l16, g);
-        load_raw<KV>(A, cr, idx_at(sm.idx, 2 * kChunk + row, n_blk), g);
+        load_raw<KV>(A, cr, idx_at(sm.idx, kAhead * kChunk + row, n_blk), g);
       }
       float s[NHB][4], psum[NHB];
       softmax_local<NHB>(sm.p[0], sm.red[0], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
@@ -296,14 +300,14 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     }
     int i = 0;
     for (; i + 2 < nch; i += 2) {
-      pipelined_step<NHB, KV>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cr, w, lane,
-                              scale_log2);
-      pipelined_step<NHB, KV>(sm, 1, st, A, (i + 4) * kChunk + row, n_blk, cr, w, lane,
+      pipelined_step<NHB, KV>(sm, 0, st, odd, (i + 1 + kAhead) * kChunk + row, n_blk, cr, w,
+                              lane, scale_log2);
+      pipelined_step<NHB, KV>(sm, 1, st, A, (i + 2 + kAhead) * kChunk + row, n_blk, cr, w, lane,
                               scale_log2);
     }
     if (i + 1 < nch) {
-      pipelined_step<NHB, KV>(sm, 0, st, B, (i + 3) * kChunk + row, n_blk, cr, w, lane,
-                              scale_log2);
+      pipelined_step<NHB, KV>(sm, 0, st, odd, (i + 1 + kAhead) * kChunk + row, n_blk, cr, w,
+                              lane, scale_log2);
       pv_last<NHB>(sm, 1, st, w, lane);
     } else {
       pv_last<NHB>(sm, 0, st, w, lane);
@@ -508,17 +512,12 @@ static hipError_t launch_items_kv(const void* q, const uint8_t* cache, int num_p
                                   const StepIn& sti, hipStream_t stream) {
   const int64_t num_slots = (int64_t)num_pages << ps;
   const int items = T * splits;
-  // bf16 records take 72 registers a lane per chunk in flight (the FP8 ones 42): two
-  // chunks in flight beside Q for 32 heads would spill, so a workgroup takes 16 heads and
-  // the head groups of a token share the gathered records through their XCD's L2.
-  if (H == 16 || KV == kKvBf16) {
-    const int groups = H / 16;
-    const int grid = groups == 1 ? items : 8 * groups * ((items + 7) / 8);
-    hipLaunchKernelGGL((sparse_mla_kernel<1, FUSED, STEP, KV>), dim3(grid), dim3(256), 0, stream,
+  if (H == 16) {
+    hipLaunchKernelGGL((sparse_mla_kernel<1, FUSED, STEP, KV>), dim3(items), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), cache, num_slots, ps, indices, idx_stride, lens,
-                       sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, groups, splits,
+                       sinks, scale_log2, static_cast<uint16_t*>(out), lse, T, H, 1, splits,
                        split_len, part_o, part_ml, tin, sti, o_scale);
-  } else if constexpr (KV != kKvBf16) {
+  } else {
     const int groups = H / 32;
     const int grid = groups == 1 ? items : 8 * groups * ((items + 7) / 8);
     hipLaunchKernelGGL((sparse_mla_kernel<2, FUSED, STEP, KV>), dim3(grid), dim3(256), 0, stream,
