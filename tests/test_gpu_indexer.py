@@ -140,3 +140,24 @@ def test_indexer_topk_zero_width_output(dsv4):
     dsv4.dsv4_indexer_topk(dev(np.zeros((2, 64), np.float32)), dev(qsl), dev(seq), 0, out, lens)
     torch.cuda.synchronize()
     assert lens.cpu().tolist() == [0, 0]
+
+
+@pytest.mark.parametrize("ties", [1, 1023, 1024, 1025, 5000])
+def test_indexer_threshold_bin_sizes(dsv4, ties):
+    """Rows staged in LDS resolve the threshold bin by ranking its keys when it holds at
+    most 1024 of them, and by a radix select otherwise: a row of 99 logits 10.0, `ties`
+    logits 5.0 (the k-th largest, all in one bin) and -1.0 elsewhere, k = 100, on both
+    sides of that limit; ids must match the oracle bit for bit (ties to the smaller id)."""
+    rng = np.random.default_rng(1400 + ties)
+    T, L, top_k = 3, 8192, 100
+    logits = np.full((T, L), -1.0, np.float32)
+    for t in range(T):
+        perm = rng.permutation(L)
+        logits[t, perm[:99]] = 10.0
+        logits[t, perm[99:99 + ties]] = 5.0
+    qsl = np.arange(T + 1, dtype=np.int32)
+    seq_lens = np.full(T, L, np.int32)
+    log(f"indexer threshold bin of {ties} equal keys")
+    ref, rlen = oracle.indexer_topk(logits, qsl, seq_lens, T, 1, top_k, top_k)
+    got, glen = _gpu_topk(dsv4, logits, qsl, seq_lens, T, 1, top_k, top_k)
+    assert np.array_equal(glen, rlen) and np.array_equal(got, ref)
