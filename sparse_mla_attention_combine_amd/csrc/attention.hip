@@ -428,6 +428,209 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   }
 }
 
+// Persistent prefill (dsv4_sparse_mla_prefill with many rows): one workgroup per compute
+// unit loops over the (token, 32-head group) items of the one-shot launch, in the same
+// order and XCD placement (item i runs on the XCD of block id i; tokens in reverse, so
+// the longest causal rows come first).  What the loop buys is the prologue: while an
+// item's chunks run, the next item's index row is copied from memory straight into the
+// other of two LDS row buffers (no registers), and its Q fragments are requested as soon
+// as the item's last chunk has been staged (Q is dead then), so the next item starts
+// with its row in LDS and its Q in flight instead of paying two memory round trips.
+// Rows of up to kPIdx entries.  Same arithmetic as the one-shot kernel, bit for bit.
+constexpr int kPIdx = 2304;
+
+struct AttnSmemP {
+  __bf16 v[2][kChunk][kVStride];
+  __bf16 p[2][32][kPStride];
+  float red[2][4][32];
+  float lsum[4][32];
+  int32_t idx[2][kPIdx];
+};
+static_assert(sizeof(AttnSmemP) <= 160 * 1024, "fits the LDS of a compute unit");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Entry jj of a row buffer of kPIdx entries (-1 at or past n).
+__device__ __forceinline__ int64_t idx_at_p(const int32_t* idx, int jj, int n) {
+  const int32_t v = idx[min(jj, kPIdx - 1)];
+  return jj < n ? (int64_t)v : -1;
+}
+
+// Entries [0, n) of a row into `dst` (kPIdx entries), memory to LDS without registers:
+// wave w copies entries 256u + 64w .. +63 with one 4-byte load per lane (lanes past n
+// copy entry n - 1 into slots that are never read).  Complete after s_waitcnt vmcnt(0).
+__device__ __forceinline__ void copy_row_to_lds(int32_t* dst, const int32_t* __restrict__ src,
+                                                int n, int w, int lane) {
+  for (int e0 = 64 * w; e0 < n; e0 += 256) {
+    const int e = min(e0 + lane, n - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(src + e), (lds_void*)(dst + e0), 4, 0, 0);
+  }
+}
+
+// The normalised output rows and lse of a (token, 32 heads) item: the waves' partial
+// denominators summed, the sink added, O scaled and staged through LDS (first value
+// tile) so that each store writes one 1 KB row.
+template <int KV, class SM>
+__device__ __forceinline__ void store_rows2(SM& sm, const AttnState<2>& st,
+                                            const float* __restrict__ sinks,
+                                            uint16_t* __restrict__ out, float* __restrict__ lse,
+                                            int64_t t, int H, int h0, float o_scale) {
+  int tid_e = threadIdx.x;
+  asm volatile("" : "+v"(tid_e));
+  const int lane = tid_e & 63, w = tid_e >> 6, l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const float lp = sum_xor32(sum_xor16(st.l_part[hb]));
+    if (g == 0) sm.lsum[w][16 * hb + l16] = lp;
+  }
+  __syncthreads();
+  const int hl = lane & 31;
+  const int h = h0 + hl;
+  const float lt = sm.lsum[0][hl] + sm.lsum[1][hl] + sm.lsum[2][hl] + sm.lsum[3][hl];
+  const float mr = (g & 1) ? st.m_run[1] : st.m_run[0];
+  const float z2 = sinks ? sinks[h] * kLog2e : -INFINITY;
+  const float M = fmaxf(mr, z2);
+  const float f = exp2f(mr - M);
+  const float den = lt * f + ((z2 == -INFINITY) ? 0.f : exp2f(z2 - M));
+  float inv = den > 0.f ? f / den : 0.f;
+  if constexpr (KV == kKvFp8E4m3) inv *= o_scale;
+  const int hi = lane >> 5;
+  __bf16* const ot = &sm.v[0][0][0];
+  constexpr int kOStride = kNope + 8;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const f32x16& o = st.o32[mb];
+      *reinterpret_cast<uint2*>(ot + hl * kOStride + 128 * mb + 32 * w + 8 * qd + 4 * hi) =
+          make_uint2(pack_bf16x2(o[4 * qd] * inv, o[4 * qd + 1] * inv),
+                     pack_bf16x2(o[4 * qd + 2] * inv, o[4 * qd + 3] * inv));
+    }
+  if (lse && w == 0 && hi == 0)
+    lse[t * H + h] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+  __syncthreads();
+  uint16_t* const ob = out + (t * H + h0) * kNope;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int hr = 8 * w + r;
+    *reinterpret_cast<uint4*>(ob + (int64_t)hr * kNope + 8 * lane) =
+        *reinterpret_cast<const uint4*>(ot + hr * kOStride + 8 * lane);
+  }
+}
+
+template <int KV>
+__global__ void __launch_bounds__(256) sparse_mla_prefill_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int64_t num_slots, int ps,
+    const int32_t* __restrict__ indices, int idx_stride, const int32_t* __restrict__ lens,
+    const float* __restrict__ sinks, float scale_log2, float o_scale, uint16_t* __restrict__ out,
+    float* __restrict__ lse, int T, int H, int groups, int n_items) {
+  __shared__ AttnSmemP sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int row = 16 * w + l16;
+  const CacheRef cr{cache, num_slots, ps};
+  // item -> (token, head group), as the one-shot launch maps its block ids
+  auto item = [&](int it, int64_t& t, int& h0, int& len) -> bool {
+    const int x = it & 7, k = it >> 3;
+    const int vt = (k / groups) * 8 + x;
+    if (vt >= T) return false;
+    t = T - 1 - vt;
+    h0 = (k % groups) * 32;
+    len = min(max(lens[t], 0), idx_stride);
+    return true;
+  };
+  int it = blockIdx.x;
+  int64_t t = 0;
+  int h0 = 0, len = 0;
+  while (it < n_items && !item(it, t, h0, len)) it += gridDim.x;
+  if (it >= n_items) return;
+  int buf = 0;
+  AttnState<2> st;
+  copy_row_to_lds(sm.idx[0], indices + t * idx_stride, len, w, lane);
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+    load_q_frags(st.qf[hb], q + (t * H + h0 + 16 * hb + l16) * kLatent, g);
+  __builtin_amdgcn_s_waitcnt(0);  // (includes the row's copy into LDS)
+  __syncthreads();
+  for (;;) {
+    int nit = it + gridDim.x;
+    int64_t nt = 0;
+    int nh0 = 0, nlen = 0;
+    while (nit < n_items && !item(nit, nt, nh0, nlen)) nit += gridDim.x;
+    const bool has_next = nit < n_items;
+    if (has_next) copy_row_to_lds(sm.idx[buf ^ 1], indices + nt * idx_stride, nlen, w, lane);
+    // (the lane's indices from an opaque copy of the thread id: kept from the prologue,
+    // their address terms would stay live across the chunk loop and be spilled)
+    auto load_next_q = [&]() {
+      if (has_next) {
+        int tid_q = threadIdx.x;
+        asm volatile("" : "+v"(tid_q));
+        const int l16q = tid_q & 15, gq = (tid_q >> 4) & 3;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          load_q_frags(st.qf[hb], q + (nt * H + nh0 + 16 * hb + l16q) * kLatent, gq);
+      }
+    };
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      st.m_run[hb] = kMFloor;
+      st.l_part[hb] = 0.f;
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o32[mb][r] = 0.f;
+    const int32_t* cidx = sm.idx[buf];
+    const int n_blk = len;
+    const int nch = (n_blk + kChunk - 1) / kChunk;
+    if (nch > 0) {
+      constexpr int kAhead = KV == kKvBf16 ? 1 : 2;
+      RawT<KV> A, B;
+      RawT<KV>& odd = kAhead == 2 ? B : A;
+      load_raw<KV>(A, cr, idx_at_p(cidx, row, n_blk), g);
+      if constexpr (kAhead == 2) load_raw<KV>(B, cr, idx_at_p(cidx, kChunk + row, n_blk), g);
+      {
+        f32x4 sacc[2];
+        const uint64_t vmask = __ballot(A.valid);
+        const RecPtr nxt = rec_ptr<KV>(cr, idx_at_p(cidx, kAhead * kChunk + row, n_blk), g);
+        stage2<true, KV>(&sm.v[0][0][0], A, nxt, st, sacc, w, lane);
+        float s[2][4], psum[2];
+        softmax_local<2, true>(sm.p[0], sm.red[0], sacc, vmask, st, scale_log2, s, psum, w, l16,
+                               g);
+        __syncthreads();
+        resolve_chunk<2>(sm.p[0], sm.red[0], st, s, scale_log2, psum, w, l16, g);
+      }
+      int i = 0;
+      for (; i + 2 < nch; i += 2) {
+        pipelined_step_slot<2, KV, true>(sm, 0, st, odd,
+                                   idx_at_p(cidx, (i + 1 + kAhead) * kChunk + row, n_blk), cr,
+                                   w, lane, scale_log2);
+        pipelined_step_slot<2, KV, true>(sm, 1, st, A,
+                                   idx_at_p(cidx, (i + 2 + kAhead) * kChunk + row, n_blk), cr,
+                                   w, lane, scale_log2);
+      }
+      if (i + 1 < nch) {
+        pipelined_step_slot<2, KV, true>(sm, 0, st, odd,
+                                   idx_at_p(cidx, (i + 1 + kAhead) * kChunk + row, n_blk), cr,
+                                   w, lane, scale_log2);
+        pv_last<2>(sm, 1, st, w, lane);
+      } else {
+        pv_last<2>(sm, 0, st, w, lane);
+      }
+    }
+    load_next_q();  // in flight during the output rows' staging and stores
+    store_rows2<KV>(sm, st, sinks, out, lse, t, H, h0, o_scale);
+    __builtin_amdgcn_s_waitcnt(0);  // the next row's copy into LDS has landed
+    __syncthreads();                // ... for every wave; the value tiles are free again
+    if (!has_next) break;
+    it = nit;
+    t = nt;
+    h0 = nh0;
+    len = nlen;
+    buf ^= 1;
+  }
+}
+
 // Merge of the split partials of a row (LSE merge): with per-split reference maxima m_s
 // (log2 domain), denominators l_s and unnormalised outputs O_s, and the sink z,
 //   M = max(z, max_s m_s),  den = 2^(z-M) + sum_s l_s 2^(m_s-M),
@@ -622,6 +825,29 @@ hipError_t launch_attention_step(void* q, const void* kv, const int64_t* positio
   return hipGetLastError();
 }
 
+static hipError_t launch_prefill_persistent(const void* q, const uint8_t* cache, int num_pages,
+                                            int ps, int kv_dtype, float kv_scale,
+                                            const int32_t* indices, int idx_stride,
+                                            const int32_t* lens, const float* sinks,
+                                            float softmax_scale, void* out, float* lse, int T,
+                                            int H, int n_items, int grid, hipStream_t stream) {
+  const int64_t num_slots = (int64_t)num_pages << ps;
+  const float scale_log2 = softmax_scale * kLog2e * (kv_dtype == kKvFp8E4m3 ? kv_scale : 1.f);
+  const float o_scale = kv_dtype == kKvFp8E4m3 ? kv_scale : 1.f;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), cache, num_slots, ps, indices, idx_stride,
+                       lens, sinks, scale_log2, o_scale, static_cast<uint16_t*>(out), lse, T, H,
+                       H / 32, n_items);
+    return hipGetLastError();
+  };
+  switch (kv_dtype) {
+    case kKvFp8Ds: return go(sparse_mla_prefill_kernel<kKvFp8Ds>);
+    case kKvBf16: return go(sparse_mla_prefill_kernel<kKvBf16>);
+    default: return go(sparse_mla_prefill_kernel<kKvFp8E4m3>);
+  }
+}
+
 int auto_splits(int T, int H, int width, bool prefill) {
   // workgroups of the unsplit schedule: (token, 32 heads), or (token, 16 heads) at H = 16
   const int64_t wgs = (int64_t)T * (H == 16 ? 1 : H / 32);
@@ -648,6 +874,23 @@ hipError_t launch_attention(const void* q, const uint8_t* cache, int num_pages, 
     return launch_attention_split(q, cache, num_pages, page_shift, kv_dtype, kv_scale, indices,
                                   idx_stride, lens,
                                   sinks, softmax_scale, out, lse, T, H, splits, workspace, stream);
+  if (prefill && H >= 32 && idx_stride <= kPIdx && kv_dtype >= 0 && kv_dtype <= 2) {
+    // the persistent schedule, when the one-shot grid would run in several rounds
+    static int n_cu = 0;
+    if (n_cu == 0) {
+      int dev = 0, v = 0;
+      if (hipGetDevice(&dev) == hipSuccess &&
+          hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        n_cu = v;
+    }
+    const int groups = H / 32;
+    const int64_t n_items = 8LL * groups * ((T + 7) / 8);
+    const int grid = (n_cu / 8) * 8;  // a multiple of 8: an item keeps its block id's XCD
+    if (grid >= 8 && n_items > 2LL * grid && n_items < (1LL << 31))
+      return launch_prefill_persistent(q, cache, num_pages, page_shift, kv_dtype, kv_scale,
+                                       indices, idx_stride, lens, sinks, softmax_scale, out, lse,
+                                       T, H, (int)n_items, grid, stream);
+  }
   const int whole = idx_stride > 0 ? idx_stride : 1;
   return launch_items<false, false>(q, cache, num_pages, page_shift, kv_dtype, kv_scale, indices,
                                     idx_stride, lens,

@@ -562,17 +562,26 @@ __device__ __forceinline__ void pv_mfma2(const PvFrags& f, AttnState<2>& st) {
 // per-head maxima (log2 domain) into `red`, probabilities against the current reference into
 // `ptile` (clamped at 2^kPLimit; a chunk that needs more is recomputed after the
 // barrier), and their per-lane sums into psum.
-template <int NHB>
+// SHIFT_MASK: the lane's four validity bits are taken from vmask >> 4g (one 64-bit shift
+// a chunk) instead of being tested against four per-lane 64-bit masks, which a kernel
+// short of registers would otherwise keep (or spill) across its loop.
+template <int NHB, bool SHIFT_MASK = false>
 __device__ __forceinline__ void softmax_local(__bf16 (*__restrict__ ptile)[kPStride],
                                               float (*__restrict__ red)[16 * NHB],
                                               const f32x4 (&sacc)[NHB], uint64_t vmask,
                                               const AttnState<NHB>& st, float scale_log2,
                                               float (&s)[NHB][4], float (&psum)[NHB], int w,
                                               int l16, int g) {
+  const uint32_t vm = SHIFT_MASK ? (uint32_t)(vmask >> (4 * g)) : 0u;
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[hb][i] = ((vmask >> (4 * g + i)) & 1) ? sacc[hb][i] : -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (SHIFT_MASK)
+        s[hb][i] = ((vm >> i) & 1u) ? sacc[hb][i] : -INFINITY;
+      else
+        s[hb][i] = ((vmask >> (4 * g + i)) & 1) ? sacc[hb][i] : -INFINITY;
+    }
     float mx = fmaxf(fmaxf(s[hb][0], s[hb][1]), fmaxf(s[hb][2], s[hb][3]));
     mx = max_xor32(max_xor16(mx));
     // every lane stores (the 4 lanes of a head hold the same value): a lane condition here
@@ -643,14 +652,16 @@ __device__ __forceinline__ void resolve_chunk(__bf16 (*__restrict__ ptile)[kPStr
 // chunk i+1's staging (raw -> vn, scores), so the matrix cores, the LDS and the VALU
 // work on both at once; then chunk i+1's softmax, the chunk's only barrier, and its
 // reference check.
-template <int NHB, int KV = kKvFp8Ds>
-__device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnState<NHB>& st,
-                                               RawT<KV>& raw, int pf_jj, int n_blk,
-                                               const CacheRef& cr, int w, int lane,
-                                               float scale_log2) {
+// One step of the chunk pipeline (see above), the next record to request given as a slot
+// (read from the LDS index block by the caller; -1 for none).  SM: any LDS layout with
+// the value tiles v, the probability tiles p and the maxima red.
+template <int NHB, int KV = kKvFp8Ds, bool SHIFT_MASK = false, class SM>
+__device__ __forceinline__ void pipelined_step_slot(SM& sm, int cb, AttnState<NHB>& st,
+                                                    RawT<KV>& raw, int64_t next_slot,
+                                                    const CacheRef& cr, int w, int lane,
+                                                    float scale_log2) {
   const int l16 = lane & 15, g = lane >> 4;
   const int nb = cb ^ 1;
-  const int64_t next_slot = idx_at(sm.idx, pf_jj, n_blk);  // read early: off the LDS queue
   f32x4 sacc[NHB];
   float s[NHB][4], psum[NHB];
   if constexpr (NHB == 2) {
@@ -669,7 +680,8 @@ __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnSt
     // scheduling barrier keeps the staging, whose own MFMAs and conversions are already
     // interleaved, out of that pattern.
     __builtin_amdgcn_sched_barrier(0);
-    softmax_local<NHB>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
+    softmax_local<NHB, SHIFT_MASK>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w,
+                                   l16, g);
     pv_mfma2(f, st);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -681,12 +693,20 @@ __device__ __forceinline__ void pipelined_step(AttnSmem<NHB>& sm, int cb, AttnSt
     pv_chunk<NHB>(&sm.v[cb][0][0], sm.p[cb], st, w, lane);
     const uint64_t vmask = __ballot(raw.valid);
     load_raw<KV>(raw, cr, next_slot, g);
-    softmax_local<NHB>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w, l16, g);
+    softmax_local<NHB, SHIFT_MASK>(sm.p[nb], sm.red[nb], sacc, vmask, st, scale_log2, s, psum, w,
+                                   l16, g);
   }
   __syncthreads();
   resolve_chunk<NHB>(sm.p[nb], sm.red[nb], st, s, scale_log2, psum, w, l16, g);
 }
-
+template <int NHB, int KV = kKvFp8Ds, class SM>
+__device__ __forceinline__ void pipelined_step(SM& sm, int cb, AttnState<NHB>& st,
+                                               RawT<KV>& raw, int pf_jj, int n_blk,
+                                               const CacheRef& cr, int w, int lane,
+                                               float scale_log2) {
+  pipelined_step_slot<NHB, KV>(sm, cb, st, raw, idx_at(sm.idx, pf_jj, n_blk), cr, w, lane,
+                               scale_log2);
+}
 static_assert(32 * kLatent <= kChunk * kVStride, "32 q rows fit one value-tile buffer");
 static_assert(32 * (kNope + 8) <= kChunk * kVStride, "32 staged output rows fit one value-tile buffer");
 static_assert(32 * (kNope + 4) * 4 <= 2 * kChunk * kVStride * 2, "32 staged fp32 partial rows fit both value-tile buffers");
@@ -705,8 +725,8 @@ __device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[18], const uint16_t* q
 }
 
 // The block's last chunk: P.V only.
-template <int NHB>
-__device__ __forceinline__ void pv_last(AttnSmem<NHB>& sm, int cb, AttnState<NHB>& st,
+template <int NHB, class SM>
+__device__ __forceinline__ void pv_last(SM& sm, int cb, AttnState<NHB>& st,
                                         int w, int lane) {
   if constexpr (NHB == 2) {
     PvFrags f;

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from synth_inputs import attention_workload, bf16_normal
+from synth_inputs import attention_workload, bf16_normal, rope_table
 from tests.gpu_helpers import (assert_attention_close, bits_to_f64, dev, dev_bf16, host_bits,
                                log, oracle_cache)
 
@@ -253,3 +253,49 @@ def test_rows_past_one_index_block(dsv4, stride, H):
     assert torch.equal(lse_a.view(torch.int32), lse_s.view(torch.int32))
     check(f"decode+workspace ({auto} pieces) stride={stride}", host_bits(out_a),
           lse_a.cpu().numpy())
+
+
+@pytest.mark.parametrize("kvd,kvs", [(0, 1.0), (1, 1.0), (2, 0.0371)], ids=["packed", "bf16", "fp8"])
+@pytest.mark.parametrize("H", [32, 64, 128])
+def test_prefill_persistent_equals_decode(dsv4, H, kvd, kvs):
+    """Prefill batches of many rows run on persistent workgroups that loop over (token,
+    head group) items, copying each next row into LDS and requesting its Q while the
+    current item finishes: out and lse bit for bit equal to the one-workgroup-per-item
+    decode, on 600 tokens (several items per workgroup) with ragged, empty and full rows
+    of up to 2304 entries, -1 holes and out-of-range slots; sampled tokens against the
+    oracle."""
+    rng = np.random.default_rng(5000 + H + 7 * kvd)
+    P, num_pages, T, stride = 64, 80, 600, 2304
+    rb = oracle.kv_record_bytes(kvd)
+    slots = rng.choice(num_pages * P, size=4000, replace=False).astype(np.int64)
+    cache = np.zeros(num_pages * P * rb, np.uint8)
+    _, cache = oracle.kv_insert(np.zeros((slots.size, 0, 576), np.uint16),
+                                bf16_normal(rng, (slots.size, 576)), rng.integers(0, 900, slots.size),
+                                slots, rope_table(900), np.zeros(576, np.uint16), 1e-6, cache,
+                                num_pages, P, kv_dtype=kvd, kv_scale=kvs)
+    lens = rng.integers(0, stride + 1, T).astype(np.int32)
+    lens[:5] = [0, 1, 64, stride, stride]
+    idx = rng.choice(slots, size=(T, stride)).astype(np.int32)
+    idx[rng.random((T, stride)) < 0.05] = -1
+    idx[rng.random((T, stride)) < 0.01] = num_pages * P + 3
+    q = bf16_normal(rng, (T, H, 576))
+    sinks = rng.standard_normal(H).astype(np.float32)
+    cache_dev, qd, idd, ld, sd = dev(cache), dev_bf16(q), dev(idx), dev(lens), dev(sinks)
+    res = []
+    for fn in (dsv4.dsv4_sparse_mla_prefill, dsv4.dsv4_sparse_mla_decode):
+        out = torch.full((T, H, 512), 7.0, dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((T, H), 7.0, dtype=torch.float32, device="cuda")
+        fn(qd, cache_dev, idd, ld, sd, 1.0 / 24, out, lse, kv_dtype=kvd, kv_scale=kvs)
+        torch.cuda.synchronize()
+        res.append((out, lse))
+    log(f"prefill persistent H={H} kv_dtype={kvd} T={T}")
+    (op, lp), (od, ldd) = res
+    assert torch.equal(op.view(torch.int16), od.view(torch.int16))
+    assert torch.equal(lp.view(torch.int32), ldd.view(torch.int32))
+    toks = np.array([0, 1, 2, 3, 4, 299, T - 1])
+    ref, rlse = oracle.sparse_mla(q[toks], cache, num_pages, P, idx[toks], lens[toks], sinks,
+                                  1.0 / 24, nthreads=8, kv_dtype=kvd, kv_scale=kvs)
+    assert_attention_close(host_bits(op)[toks], ref, f"prefill persistent H={H}")
+    gl = lp.cpu().numpy()[toks]
+    fin = np.isfinite(rlse)
+    assert np.array_equal(fin, np.isfinite(gl)) and np.max(np.abs(gl[fin] - rlse[fin])) <= 2e-3
