@@ -667,7 +667,7 @@ def bench_compressed_prefill(args, torch, dsv4):
                      "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS, 4),
                      "traffic": None,
-                     "kernel": "sparse_mla_kernel<2> (dsv4_sparse_mla_prefill over the workspace)",
+                     "kernel": "sparse_mla_prefill_kernel (dsv4_sparse_mla_prefill over the workspace)",
                      "launch_us": round(attn_s * 1e6, 2), "alg_flops": flops, "alg_bytes": bytes_alg},
         "kernels_us": {"kv_insert": round(float(kt[:, 0].mean()), 2),
                        "combine_indices_compressed": round(float(kt[:, 1].mean()), 2),
@@ -994,7 +994,7 @@ def bench_prefill(args, torch, dsv4):
     attn_s = float(kt[:, 2].mean()) * 1e-6
     flops = 2.0 * H * (LATENT + NOPE) * nv
     nbytes = RECORD * T + T * H * (LATENT + NOPE) * 2 + 4.0 * l_np.sum() + 4.0 * T + 4.0 * H
-    roof = _roofline(flops, nbytes, attn_s, "sparse_mla_kernel<2> (dsv4_sparse_mla_prefill)",
+    roof = _roofline(flops, nbytes, attn_s, "sparse_mla_prefill_kernel (dsv4_sparse_mla_prefill)",
                      measured_traffic("prefill"))
     log(f"[bench] prefill step: {reps[0] / args.steps * 1e3:.3f} ms/step (graph); insert "
         f"{kt[:, 0].mean():.1f} us, combine {kt[:, 1].mean():.1f} us, attention {kt[:, 2].mean():.1f} us "
