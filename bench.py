@@ -132,6 +132,9 @@ def parse():
                          "reported value; default 5)")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cache-flushed pass (512 MB written between steps)")
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="skip the measured peaks (a bf16 GEMM and 1 GiB copy / reduction after "
+                         "the timed region) that the roofline is also reported against")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device-to-device copy 3 times (the known-size "
                          "kernel that scales FETCH_SIZE / WRITE_SIZE counter readings)")
@@ -485,7 +488,7 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inst[0], calls, H, T, W, PS, KVD, kvs)
-    print(json.dumps(result), flush=True)
+    emit(args, torch, result)
 
 
 def bench_indexer(args, torch, dsv4):
@@ -551,7 +554,7 @@ def bench_indexer(args, torch, dsv4):
                      "launch_us": round(float(us.mean()), 2), "alg_bytes": bytes_alg},
         "prefill_shape_us": round(pre_us, 1),
     }
-    print(json.dumps(result), flush=True)
+    emit(args, torch, result)
 
 
 def bench_compressed_prefill(args, torch, dsv4):
@@ -674,7 +677,7 @@ def bench_compressed_prefill(args, torch, dsv4):
                        "gather_workspace": round(float(kt[:, 2].mean()), 2),
                        "sparse_mla_prefill": round(float(kt[:, 3].mean()), 2)},
     }
-    print(json.dumps(result), flush=True)
+    emit(args, torch, result)
 
 
 def _graph_of(torch, fn):
@@ -802,7 +805,7 @@ def bench_insert(args, torch, dsv4):
         res["cpu_baseline"] = {"value": round(n / el, 3), "unit": "tokens/s", "cores": 1,
                                "kind": "oracle", "cpu": cpu_model(),
                                "sample": f"the first {n} tokens (all {H} heads), fp64, {el:.1f} s"}
-    print(json.dumps(res), flush=True)
+    emit(args, torch, res)
 
 
 def _compact_cache(wl, idx, lens, tokens):
@@ -933,7 +936,7 @@ def bench_mtp(args, torch, dsv4):
                   roof, {"sparse_mla_decode_step": round(float(us.mean()), 2)})
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = _attention_cpu_baseline(wl, it, c_np, l_np, H, "query-tokens/s")
-    print(json.dumps(res), flush=True)
+    emit(args, torch, res)
 
 
 def attention_workload_mtp(args):
@@ -1010,7 +1013,7 @@ def bench_prefill(args, torch, dsv4):
                    "sparse_mla_prefill": round(float(kt[:, 2].mean()), 2)})
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = _attention_cpu_baseline(wl, it, c_np, l_np, H, "query-tokens/s")
-    print(json.dumps(res), flush=True)
+    emit(args, torch, res)
 
 
 def cpu_baseline(wl, d0, calls, H, T, W, PS=64, kv_dtype=0, kv_scale=1.0):
@@ -1081,6 +1084,73 @@ def cpu_model():
     except OSError:
         pass
     return "unknown"
+
+
+_PEAKS = None
+
+
+def measured_peaks(torch):
+    """Peaks this GPU reaches in the library's own probes (dsv4_peak_mfma,
+    dsv4_peak_stream), measured once per run after the timed region: dense bf16 MFMAs of
+    both shapes the attention kernels use (1024 workgroups, 8 independent accumulators a
+    wave), and a 1 GiB streaming read (8192 workgroups) and a 1 GiB copy (16384
+    workgroups; bytes read + written) for HBM.
+    The roofline's measured fraction uses the larger MFMA rate and the larger HBM rate."""
+    global _PEAKS
+    if _PEAKS is not None:
+        return _PEAKS
+    import sparse_mla_attention_combine_amd as dsv4
+    dev = torch.device("cuda:0")
+
+    def per_call(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n
+
+    wg = 1024
+    fsink = torch.empty(wg * 256, dtype=torch.float32, device=dev)
+    mfma = {}
+    for shape, name in ((0, "32x32x16"), (1, "16x16x32")):
+        flops = dsv4.dsv4_peak_mfma(shape, 2000, fsink)
+        mfma[name] = flops / per_call(lambda: dsv4.dsv4_peak_mfma(shape, 2000, fsink), 10) / 1e12
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    rsink = torch.empty(8192 * 256, dtype=torch.int32, device=dev)
+    csink = torch.empty(16384 * 256, dtype=torch.int32, device=dev)
+    read_gbs = nbytes / per_call(lambda: dsv4.dsv4_peak_stream(src, rsink), 20) / 1e9
+    copy_gbs = 2.0 * nbytes / per_call(lambda: dsv4.dsv4_peak_stream(src, csink, dst=dst), 20) / 1e9
+    del src, dst, rsink, csink, fsink
+    torch.cuda.synchronize()
+    _PEAKS = {"mfma_tflops": round(max(mfma.values()), 1),
+              "mfma_32x32x16_tflops": round(mfma["32x32x16"], 1),
+              "mfma_16x16x32_tflops": round(mfma["16x16x32"], 1),
+              "hbm_gbs": round(max(read_gbs, copy_gbs), 1),
+              "hbm_read_gbs": round(read_gbs, 1), "hbm_copy_gbs": round(copy_gbs, 1),
+              "how": "dsv4_peak_mfma (dense bf16 MFMA loops, both shapes) and dsv4_peak_stream "
+                     "(1 GiB read-only and 1 GiB copy); the larger rate of each kind"}
+    log(f"[bench] measured peaks: bf16 MFMA 32x32x16 {mfma['32x32x16']:.0f} / 16x16x32 "
+        f"{mfma['16x16x32']:.0f} TFLOP/s; HBM read {read_gbs:.0f} GB/s, copy {copy_gbs:.0f} GB/s")
+    return _PEAKS
+
+
+def emit(args, torch, result):
+    """Print the one JSON line; unless disabled, the roofline object also carries the
+    measured peaks and the fraction of the binding one that the kernel reached."""
+    roof = result.get("roofline")
+    if roof is not None and not args.no_measured_peaks and torch.cuda.is_available():
+        pk = measured_peaks(torch)
+        peak = pk["mfma_tflops"] if roof["bound"] == "mfma" else pk["hbm_gbs"]
+        roof["measured_peaks"] = pk
+        roof["frac_measured"] = round(roof["achieved"] / peak, 4) if peak > 0 else None
+    print(json.dumps(result), flush=True)
 
 
 def settle(args, torch, replay):

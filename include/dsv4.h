@@ -466,6 +466,33 @@ int dsv4_sparse_mla_decode_split_noalloc(const void* q, const uint8_t* kv_cache,
 int dsv4_gather_dequant(const uint8_t* kv_cache, int num_pages, int page_size, int kv_dtype,
                         float kv_scale, const int32_t* slots, int n, void* out, void* stream);
 
+/*
+ * ---------------------------------------------------------------------------------
+ * Measurement probes (not steps of the method).  The roofline of each kernel is
+ * reported against the chip's published peaks and, separately, against the peaks these
+ * probes reach on the GPU at hand.
+ *
+ * dsv4_peak_mfma — matrix-core throughput: `workgroups` workgroups of 4 waves, each wave
+ * issuing iters x 8 dense bf16 MFMAs with fp32 accumulation on 8 independent
+ * accumulators (shape 0: v_mfma_f32_32x32x16_bf16, the P.V shape; shape 1:
+ * v_mfma_f32_16x16x32_bf16, the QK^T shape).  Every lane holds the operands
+ * a_i = (i + 1) / 8, b_i = 1 / 8 and accumulator k starts at k, so sink[j] =
+ * 448 + 144 * iters (shape 0) or 112 + 72 * iters (shape 1) exactly.
+ *   sink float [workgroups * 256] (device);  *flops (host) = the launch's dense FLOPs.
+ *   workgroups in [1, 65536], iters in [1, 2^20]; shape outside {0, 1} is
+ *   DSV4_ERR_UNSUPPORTED.
+ *
+ * dsv4_peak_stream — HBM throughput: reads `bytes` (a multiple of 16) from src in 16-byte
+ * units, grid-stride over `workgroups` x 256 threads; dst == NULL: read only, sink[j] =
+ * the xor of every 32-bit word thread j read; else copies src to dst (sink[j] = 0).
+ *   src, dst 16-byte aligned device buffers; sink uint32 [workgroups * 256] (device).
+ * ---------------------------------------------------------------------------------
+ */
+int dsv4_peak_mfma(int shape, int workgroups, int iters, float* sink, double* flops,
+                   void* stream);
+int dsv4_peak_stream(const void* src, void* dst, size_t bytes, uint32_t* sink, int workgroups,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,12 +60,14 @@ _lib.dsv4_indexer_topk.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, 
                                    _vp]
 _lib.dsv4_gather_workspace.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp,
                                        _i32, _i32, _i32, _i32, _vp, _i32, _vp]
+_lib.dsv4_peak_mfma.argtypes = [_i32, _i32, _i32, _vp, ctypes.POINTER(ctypes.c_double), _vp]
+_lib.dsv4_peak_stream.argtypes = [_vp, _vp, ctypes.c_size_t, _vp, _i32, _vp]
 for _f in (_lib.dsv4_kv_insert, _lib.dsv4_combine_indices, _lib.dsv4_sparse_mla_decode,
            _lib.dsv4_sparse_mla_prefill, _lib.dsv4_gather_dequant, _lib.dsv4_sparse_mla_decode_split,
            _lib.dsv4_combine_indices_compressed, _lib.dsv4_gather_workspace,
            _lib.dsv4_indexer_topk, _lib.dsv4_sparse_mla_decode_topk,
            _lib.dsv4_sparse_mla_decode_step, _lib.dsv4_sparse_mla_decode_step_split,
-           _lib.dsv4_sparse_mla_decode_split_noalloc):
+           _lib.dsv4_sparse_mla_decode_split_noalloc, _lib.dsv4_peak_mfma, _lib.dsv4_peak_stream):
     _f.restype = _i32
 
 EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4_kv_insert",
@@ -74,7 +76,8 @@ EXPORTED = ["dsv4_status_str", "dsv4_last_error", "dsv4_cache_page_bytes", "dsv4
             "dsv4_sparse_mla_decode_split", "dsv4_combine_indices_compressed",
             "dsv4_gather_workspace", "dsv4_indexer_topk", "dsv4_sparse_mla_decode_topk",
             "dsv4_sparse_mla_decode_step", "dsv4_sparse_mla_decode_step_split",
-            "dsv4_sparse_mla_workspace_bytes", "dsv4_sparse_mla_decode_split_noalloc"]
+            "dsv4_sparse_mla_workspace_bytes", "dsv4_sparse_mla_decode_split_noalloc",
+            "dsv4_peak_mfma", "dsv4_peak_stream"]
 
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -379,3 +382,24 @@ def dsv4_gather_dequant(kv_cache, slots, out, page_size=64, stream=None, kv_dtyp
                                     float(kv_scale), _ptr(slots), slots.shape[0], _ptr(out),
                                     _stream(stream)))
     return out
+
+
+def dsv4_peak_mfma(shape, iters, sink, stream=None):
+    """Matrix-core probe: sink fp32 [workgroups * 256] (workgroups = sink.numel() // 256);
+    shape 0 = 32x32x16, 1 = 16x16x32 bf16 MFMAs.  Returns the launch's dense FLOPs."""
+    _want(sink, torch.float32, "sink")
+    flops = ctypes.c_double(0.0)
+    _check(_lib.dsv4_peak_mfma(int(shape), sink.numel() // 256, int(iters), _ptr(sink),
+                               ctypes.byref(flops), _stream(stream)))
+    return flops.value
+
+
+def dsv4_peak_stream(src, sink, dst=None, stream=None):
+    """HBM probe: reads src (its bytes) and, if dst is given, copies it there; sink int32
+    [workgroups * 256] receives each thread's xor of what it read (read-only)."""
+    _want(sink, torch.int32, "sink")
+    n = _nbytes(src)
+    if dst is not None and _nbytes(dst) < n:
+        raise ValueError("dst is smaller than src")
+    _check(_lib.dsv4_peak_stream(_ptr(src), None if dst is None else _ptr(dst), n, _ptr(sink),
+                                 sink.numel() // 256, _stream(stream)))

@@ -20,7 +20,7 @@ OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libdsv4.so")
 ARCH = "gfx950"
 SOURCES = ["api.cpp", "combine.hip", "insert.hip", "gather.hip", "attention.hip",
-           "workspace.hip", "indexer.hip"]
+           "workspace.hip", "indexer.hip", "peaks.hip"]
 # Packed FP32 instructions are disabled for all device code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Wno-unused-result", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

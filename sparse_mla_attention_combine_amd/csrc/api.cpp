@@ -12,6 +12,7 @@
 
 #include "../../include/dsv4.h"
 #include "launch.hpp"
+#include "peaks.hpp"
 
 namespace {
 
@@ -526,6 +527,35 @@ int dsv4_gather_dequant(const uint8_t* kv_cache, int num_pages, int page_size, i
   return hip_status(dsv4::launch_gather(kv_cache, num_pages, dsv4::page_shift_of(page_size),
                                         kv_dtype, kv_scale, slots, n, out,
                                         static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int dsv4_peak_mfma(int shape, int workgroups, int iters, float* sink, double* flops,
+                   void* stream) {
+  const char* fn = "dsv4_peak_mfma";
+  if (shape != 0 && shape != 1)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: shape %d not supported (0 32x32x16, 1 16x16x32)", fn, shape);
+  if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 20))
+    return fail(DSV4_ERR_SHAPE, "%s: workgroups %d not in [1, 65536] or iters %d not in [1, 2^20]",
+                fn, workgroups, iters);
+  if (!sink || !flops) return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(sink, 4)) return fail(DSV4_ERR_ALIGN, "%s: sink must be 4-byte aligned", fn);
+  return hip_status(dsv4::launch_peak_mfma(shape, workgroups, iters, sink, flops,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int dsv4_peak_stream(const void* src, void* dst, size_t bytes, uint32_t* sink, int workgroups,
+                     void* stream) {
+  const char* fn = "dsv4_peak_stream";
+  if (bytes % 16 != 0) return fail(DSV4_ERR_SHAPE, "%s: bytes %zu not a multiple of 16", fn, bytes);
+  if (workgroups < 1 || workgroups > 65536)
+    return fail(DSV4_ERR_SHAPE, "%s: workgroups %d not in [1, 65536]", fn, workgroups);
+  if (!sink || (!src && bytes > 0)) return fail(DSV4_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if ((src && !aligned(src, 16)) || (dst && !aligned(dst, 16)) || !aligned(sink, 4))
+    return fail(DSV4_ERR_ALIGN, "%s: src and dst must be 16-byte aligned, sink 4-byte", fn);
+  return hip_status(dsv4::launch_peak_stream(src, dst, bytes, sink, workgroups,
+                                             static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -359,3 +359,26 @@ def test_binding_rejects_host_tensors(dsv4):
                                     torch.zeros(1, 128, dtype=torch.int32),
                                     torch.zeros(1, dtype=torch.int32), None, 0.04,
                                     torch.zeros(1, 16, 512, dtype=torch.bfloat16))
+
+
+def test_peak_probe_validation(dsv4):
+    """The measurement probes check shape, sizes, pointers and alignment on the host."""
+    lib = dsv4.library()
+    keep, p = _fake()
+    fl = ctypes.c_double(0.0)
+    lib.dsv4_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    lib.dsv4_peak_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert lib.dsv4_peak_mfma(2, 4, 10, p, ctypes.byref(fl), None) == 4  # UNSUPPORTED
+    assert lib.dsv4_peak_mfma(0, 0, 10, p, ctypes.byref(fl), None) == 2  # SHAPE
+    assert lib.dsv4_peak_mfma(1, 4, 0, p, ctypes.byref(fl), None) == 2
+    assert lib.dsv4_peak_mfma(0, 4, 10, None, ctypes.byref(fl), None) == 1  # NULL
+    assert lib.dsv4_peak_mfma(0, 4, 10, p, None, None) == 1
+    assert lib.dsv4_peak_mfma(0, 4, 10, ctypes.c_void_p(p.value + 2), ctypes.byref(fl), None) == 3
+    assert lib.dsv4_peak_stream(p, None, 17, p, 4, None) == 2
+    assert lib.dsv4_peak_stream(p, None, 1024, p, 0, None) == 2
+    assert lib.dsv4_peak_stream(None, None, 1024, p, 4, None) == 1
+    assert lib.dsv4_peak_stream(p, None, 1024, None, 4, None) == 1
+    assert lib.dsv4_peak_stream(ctypes.c_void_p(p.value + 8), None, 1024, p, 4, None) == 3
+    assert lib.dsv4_peak_stream(p, ctypes.c_void_p(p.value + 4), 1024, p, 4, None) == 3
