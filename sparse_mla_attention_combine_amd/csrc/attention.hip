@@ -111,27 +111,8 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   const int lim = FUSED ? kIdxBlock : beg + min(split_len, idx_stride - beg);
 
   AttnState<NHB> st;
-  // STEP: wave w < 2*NHB owns q heads h0 + 8w .. +7 (8 lanes a row, the insert kernel's
-  // partition, so the bits match it); every wave w owns the new latent rows t - w, t - w - 4,
-  // ... of the request.  The q rows, positions and the first latent row are requested here,
-  // beside the combine step's loads.
   const int c8 = lane & 7;
-  u32x4 qraw[9];  // (a native vector: copies of the struct type would keep it in memory)
-  int64_t qp = -1, kvp = -1, kvs = -1;
-  KvLane kvv;
   const float* const no_row = reinterpret_cast<const float*>(g_zero_page);  // unused values
-  if constexpr (STEP) {
-    if (w < 2 * NHB) {
-      const uint16_t* qr = sti.q + ((int64_t)t * H + h0 + 8 * w + (lane >> 3)) * kLatent;
-#pragma unroll
-      for (int k = 0; k < 9; ++k) qraw[k] = *reinterpret_cast<const u32x4*>(qr + 8 * (c8 + 8 * k));
-    }
-    qp = sti.positions[t];
-    const int64_t t1 = t >= w ? t - w : t;  // in bounds; used only if in the request
-    kvv = kv_lane_load(sti.kv + t1 * kLatent, lane);
-    kvp = sti.positions[t1];
-    kvs = sti.slot_mapping[t1];
-  }
   // Q^T fragments from memory (all but STEP): lane (head l16 of block hb, k-group g);
   // k-step s pairs with the K-fragment dims chosen in load_raw (nope: 64u+16g+8h, rope:
   // 32r+8g).  Requested after the loads that build the index row: vector-memory loads
@@ -156,57 +137,85 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.o32[mb][r] = 0.f;
 
+  // Chunks of records in flight per lane: two (buffers A and B, odd chunks in B), or one
+  // for bf16 records at 32 heads (72 registers a chunk beside Q for 32 heads).
+  constexpr int kAhead = (KV == kKvBf16 && NHB == 2) ? 1 : 2;
+  RawT<KV> A, B;
+  RawT<KV>& odd = kAhead == 2 ? B : A;
+  const int row = 16 * w + l16;
+  const CacheRef cr{STEP ? sti.cache : cache, num_slots, ps};
+
   // Index blocks of up to 4096 entries are staged in LDS.  Inside a block chunk c lives
   // in register buffer c&1 and LDS tiles c&1; a buffer is refilled with chunk c+2 as
   // soon as staging has consumed it, so two chunks of records are always in flight.
   // Rows from memory: the first block is requested together with the row length and
   // then Q (entries past the length are staged but never used), so the prologue waits
-  // for memory only once, and only for the row.  Rows built here: the top-k row and the
-  // request lookup take one round of loads, the block-table lookups a second, and Q is
-  // requested after them (FUSED; STEP adds its insert work to those two rounds and reads
-  // Q from LDS).
+  // for memory only once, and only for the row.  Rows built here (FUSED): the request
+  // search's loads, the top-k row and (STEP) the q rows, the first new latent row and
+  // the norm weights take one round of memory, issued in the order their values are
+  // needed; the block-table entries (one contiguous copy into LDS) and the cos/sin rows
+  // a second.
   int end;
   if constexpr (STEP) {
+    // Wave w < 2*NHB owns q heads h0 + 8w .. +7 (8 lanes a row, the insert kernel's
+    // partition, so the bits match it); every wave w owns the new latent rows t - w,
+    // t - w - 4, ... of the request.
+    const CombSearch cs = combine_search_load(tin, tid);
+    const int64_t t1 = t >= w ? t - w : t;  // in bounds; used only if in the request
+    const int64_t qp = vload(sti.positions + t);
+    const int64_t kvp = vload(sti.positions + t1);
+    const int64_t kvs = vload(sti.slot_mapping + t1);
     int32_t xv[kCombPer];
     int tl;
-    combine_request(sm, tin, t, tid, xv, tl);
-    // The first round of loads is in.  The q rows wait in LDS (the second value-tile
-    // buffer, first written by chunk 1's staging); the weight chunks and the cos/sin rows
-    // are requested beside the block-table loads, so the insert work below waits for no
-    // further round.
-    const bool qok = qp >= 0 && qp < sti.max_pos;
-    u32x4 wq[9];
-    u32x4* ql = reinterpret_cast<u32x4*>(&sm.v[1][0][0]) + (8 * w + (lane >> 3)) * (kLatent / 8) + c8;
+    combine_topk_load(tin, t, tid, xv, tl);
+    u32x4 qraw[9], wq[9];  // (native vectors: copies of a struct type would stay in memory)
     if (w < 2 * NHB) {  // chunk k of this lane's row: 16-byte unit c8 + 8k of the row
+      const uint16_t* qr = sti.q + ((int64_t)t * H + h0 + 8 * w + (lane >> 3)) * kLatent;
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
-        ql[8 * k] = qraw[k];
+        qraw[k] = *reinterpret_cast<const u32x4*>(qr + 8 * (c8 + 8 * k));
         wq[k] = *reinterpret_cast<const u32x4*>(sti.weight + 8 * (c8 + 8 * k));
       }
     }
+    const KvLane kvv = kv_lane_load(sti.kv + t1 * kLatent, lane);
+    combine_find(sm, tin, t, tid, cs);
+    // second round: the block-table entries into the first value tile (free until chunk
+    // 0 is staged) and the cos/sin rows of the two positions
+    const bool qok = qp >= 0 && qp < sti.max_pos;
     const RopeCs qrot = rope_cs_load(qok ? sti.cos_sin + qp * kRope : no_row, c8);
     const RopeCs kvrot =
         rope_cs_load(kvp >= 0 && kvp < sti.max_pos ? sti.cos_sin + kvp * kRope : no_row, lane);
-    end = combine_rows(sm, tin, t, ps, tid, xv, tl);
-    // this wave's q rows normalised and rotated in LDS (each lane rereads its own chunks)
-    // and, when the row is not cut into pieces, written back in place.  With pieces, the
+    int32_t* const bt = reinterpret_cast<int32_t*>(&sm.v[0][0][0]);
+    const bool staged = combine_stage_bt(sm, tin, t, ps, bt, w, lane);
+    asm volatile("" ::: "memory");  // every load above is issued before the wait
+    __builtin_amdgcn_s_waitcnt(0);  // (includes the copy into LDS)
+    __syncthreads();
+    end = combine_rows(sm, tin, t, ps, tid, xv, tl, bt, staged);
+    // this wave's q rows normalised and rotated into LDS (for the Q fragments) and, when
+    // the row is not cut into pieces, written back in place.  With pieces, the
     // workgroups of a token's other pieces may still be about to read the raw rows (a
     // grid of several dispatch rounds starts them at different times), so every piece
     // reads raw q and only the merge launch, stream-ordered after all of them, writes
     // the normalised rows.
     const bool q_writer = splits == 1;
-    if (w < 2 * NHB && qok) {
-      u32x4* qg = reinterpret_cast<u32x4*>(sti.q + ((int64_t)t * H + h0 + 8 * w + (lane >> 3)) *
-                                                       kLatent) + c8;
-      float ss = 0.f;
+    u32x4* ql = reinterpret_cast<u32x4*>(&sm.v[1][0][0]) + (8 * w + (lane >> 3)) * (kLatent / 8) + c8;
+    if (w < 2 * NHB) {
+      if (qok) {
+        u32x4* qg = reinterpret_cast<u32x4*>(sti.q + ((int64_t)t * H + h0 + 8 * w + (lane >> 3)) *
+                                                         kLatent) + c8;
+        float ss = 0.f;
 #pragma unroll
-      for (int k = 0; k < 9; ++k) ss = qn_sum_sq(ql[8 * k], ss);
-      const float inv = qn_inv(ss, sti.eps);
+        for (int k = 0; k < 9; ++k) ss = qn_sum_sq(qraw[k], ss);
+        const float inv = qn_inv(ss, sti.eps);
 #pragma unroll
-      for (int k = 0; k < 9; ++k) {
-        const u32x4 y = qn_chunk(ql[8 * k], wq[k], inv, qrot, k == 8);
-        ql[8 * k] = y;
-        if (q_writer) qg[8 * k] = y;
+        for (int k = 0; k < 9; ++k) {
+          const u32x4 y = qn_chunk(qraw[k], wq[k], inv, qrot, k == 8);
+          ql[8 * k] = y;
+          if (q_writer) qg[8 * k] = y;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 9; ++k) ql[8 * k] = qraw[k];  // token left untouched
       }
     }
     // the new rows this token may read: its request's tokens up to itself (only itself for
@@ -223,7 +232,17 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
                          sti.kv_scale, lane);
     }
   } else if constexpr (FUSED) {
-    end = stage_combined(sm, tin, t, ps, tid);
+    const CombSearch cs = combine_search_load(tin, tid);
+    int32_t xv[kCombPer];
+    int tl;
+    combine_topk_load(tin, t, tid, xv, tl);
+    combine_find(sm, tin, t, tid, cs);
+    int32_t* const bt = reinterpret_cast<int32_t*>(&sm.v[0][0][0]);
+    const bool staged = combine_stage_bt(sm, tin, t, ps, bt, w, lane);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);  // (includes the copy into LDS)
+    __syncthreads();
+    end = combine_rows(sm, tin, t, ps, tid, xv, tl, bt, staged);
     load_q_global();
   } else {
     int32_t iv[kStagePer];
@@ -266,8 +285,6 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
 #pragma unroll
     for (int k = 0; k < 18; ++k) asm volatile("" : "+a"(st.qf[1][k]));
   }
-  const int row = 16 * w + l16;
-  const CacheRef cr{STEP ? sti.cache : cache, num_slots, ps};
   for (int blk0 = beg; blk0 < end; blk0 += kIdxBlock) {
     const int n_blk = min(end - blk0, kIdxBlock);
     if (blk0 != beg) {
@@ -276,11 +293,6 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
       __syncthreads();
     }
     const int nch = (n_blk + kChunk - 1) / kChunk;
-    // Chunks of records in flight per lane: two (buffers A and B, odd chunks in B), or
-    // one for bf16 records at 32 heads (72 registers a chunk beside Q for 32 heads).
-    constexpr int kAhead = (KV == kKvBf16 && NHB == 2) ? 1 : 2;
-    RawT<KV> A, B;
-    RawT<KV>& odd = kAhead == 2 ? B : A;
     load_raw<KV>(A, cr, idx_at(sm.idx, row, n_blk), g);
     if constexpr (kAhead == 2) load_raw<KV>(B, cr, idx_at(sm.idx, kChunk + row, n_blk), g);
     {  // prologue: stage chunk 0 and settle its probabilities
@@ -448,23 +460,10 @@ struct AttnSmemP {
 };
 static_assert(sizeof(AttnSmemP) <= 160 * 1024, "fits the LDS of a compute unit");
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Entry jj of a row buffer of kPIdx entries (-1 at or past n).
 __device__ __forceinline__ int64_t idx_at_p(const int32_t* idx, int jj, int n) {
   const int32_t v = idx[min(jj, kPIdx - 1)];
   return jj < n ? (int64_t)v : -1;
-}
-
-// Entries [0, n) of a row into `dst` (kPIdx entries), memory to LDS without registers:
-// wave w copies entries 256u + 64w .. +63 with one 4-byte load per lane (lanes past n
-// copy entry n - 1 into slots that are never read).  Complete after s_waitcnt vmcnt(0).
-__device__ __forceinline__ void copy_row_to_lds(int32_t* dst, const int32_t* __restrict__ src,
-                                                int n, int w, int lane) {
-  for (int e0 = 64 * w; e0 < n; e0 += 256) {
-    const int e = min(e0 + lane, n - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(src + e), (lds_void*)(dst + e0), 4, 0, 0);
-  }
 }
 
 // The normalised output rows and lse of a (token, 32 heads) item: the waves' partial

@@ -236,93 +236,177 @@ __device__ __forceinline__ void stage_idx_store(int32_t* dst, const int32_t (&v)
 }
 constexpr int kStagePer = kIdxBlock / 256;
 
+// A vector (not scalar) load of a value at a uniform address: its wait is then ordered
+// with the vector loads around it instead of joining every LDS wait (lgkmcnt).
+template <class T>
+__device__ __forceinline__ T vload(const T* p) {
+  uint64_t a = reinterpret_cast<uint64_t>(p);
+  asm volatile("" : "+v"(a));
+  return *reinterpret_cast<const __attribute__((address_space(1))) T*>(a);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Entries [0, n) of a row into LDS at `dst`, memory to LDS without registers: wave w
+// copies entries 256u + 64w .. +63 with one 4-byte load per lane (lanes past n copy
+// entry n - 1 into slots up to the next multiple of 64, never read).  Complete after
+// s_waitcnt vmcnt(0) and a barrier.
+__device__ __forceinline__ void copy_row_to_lds(int32_t* dst, const int32_t* __restrict__ src,
+                                                int n, int w, int lane) {
+  for (int e0 = 64 * w; e0 < n; e0 += 256) {
+    const int e = min(e0 + lane, n - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(src + e), (lds_void*)(dst + e0), 4, 0, 0);
+  }
+}
+
 // The combine step for token t, written straight into the LDS index block (the rules of
 // combine_kernel: valid top-k entries outside the window, then the window ascending, each
-// mapped through the request's block table; -1 for the rest).  The top-k row is requested
-// before the token's request is known; returns the row length tk + sw (0 for a token of
-// no request), the same in every thread.  Contains barriers: call from all threads.
-// Every load is unconditional at a clamped, in-bounds address (only uniform conditions
-// skip one) and its value is selected afterwards: a load under a per-lane condition is
-// waited for on the spot, which would serialise them.
-// In two parts: combine_request issues the top-k row loads and finds the token's request
-// (sm.req); combine_rows, after whatever the caller does in between (loads issued there
-// overlap the block-table loads), builds the row.
+// mapped through the request's block table; -1 for the rest).  Every load is
+// unconditional at a clamped, in-bounds address (only uniform conditions skip one) and
+// its value is selected afterwards: a load under a per-lane condition is waited for on
+// the spot, which would serialise them.  Vector loads complete in order, so the parts
+// are issued by their caller in the order their values are needed:
+//   combine_search_load  the request search's loads (thread r tests request r), first;
+//   combine_topk_load    the top-k row (and whatever else the caller requests after it);
+//   combine_find         waits for the search loads only, records the token's request
+//                        in sm.req (two barriers);
+//   combine_stage_bt     copies the request's block-table entries for logical pages
+//                        0 .. pos >> ps into LDS (memory to LDS, no registers; at most
+//                        kBtStage entries, else the lookups below go to memory): one
+//                        contiguous row instead of a scattered lookup per entry;
+//   combine_rows         after s_waitcnt vmcnt(0) and a barrier, builds the row into
+//                        sm.idx and returns its length tk + sw (0 for a token of no
+//                        request), the same in every thread.
 constexpr int kCombPer = kIdxBlock / 256;
+constexpr int kBtStage = 16384;  // block-table entries staged in LDS (64 KB)
 
-template <int NT = 256, class SM>
-__device__ __forceinline__ void combine_request(SM& sm, const TopkIn& c, int64_t t,
-                                                int tid, int32_t (&xv)[kIdxBlock / NT], int& tl) {
+struct CombSearch {
+  int32_t base, lo, hi, len;  // qsl[0], and qsl[r], qsl[r+1], seq_lens[r] of request r
+};
+
+template <int NT = 256>
+__device__ __forceinline__ CombSearch combine_search_load(const TopkIn& c, int tid) {
+  CombSearch cs{0, 0, 0, 0};
+  if (c.B > 0) {
+    const int r = min(tid, c.B - 1);
+    cs.base = vload(c.qsl);
+    cs.lo = c.qsl[r];
+    cs.hi = c.qsl[r + 1];
+    cs.len = c.seq_lens[r];
+  }
+  return cs;
+}
+
+template <int NT = 256>
+__device__ __forceinline__ void combine_topk_load(const TopkIn& c, int64_t t, int tid,
+                                                  int32_t (&xv)[kIdxBlock / NT], int& tl) {
   constexpr int kPer = kIdxBlock / NT;
   const int kmax = min(c.top_k, c.topk_width);
   const int32_t* trow = c.topk + t * c.topk_stride;
+  // Every load unconditional and none of the values touched here: entries j >= kmax
+  // (clamped reads of entry kmax - 1, or of a zero word when the row is empty) are
+  // ignored by combine_rows.  A branch around the loads would let the compiler convert
+  // the values inside it, with a wait for each load.
+  const int32_t* src = kmax > 0 ? trow : reinterpret_cast<const int32_t*>(g_zero_page);
+  const int last = max(kmax - 1, 0);
 #pragma unroll
-  for (int u = 0; u < kPer; ++u)
-    xv[u] = NT * u < kmax ? trow[min(tid + NT * u, kmax - 1)] : -1;
-  tl = c.topk_lens ? c.topk_lens[t] : c.top_k;
+  for (int u = 0; u < kPer; ++u) xv[u] = src[min(tid + NT * u, last)];
+  tl = c.topk_lens ? vload(c.topk_lens + t) : c.top_k;
+}
+
+template <int NT = 256, class SM>
+__device__ __forceinline__ void combine_find(SM& sm, const TopkIn& c, int64_t t, int tid,
+                                             const CombSearch& cs) {
   if (tid == 0) sm.req[0] = -1;
   __syncthreads();
-  const int base = c.qsl[0];
   // thread r tests request r and brings its length along, so the token's position is
-  // known right after one round of loads
-  for (int r = tid; r < c.B; r += NT) {
-    const int lo = c.qsl[r] - base, hi = c.qsl[r + 1] - base;
-    const int L = c.seq_lens[r];
+  // known right after the first loads
+  auto test = [&](int r, int lo, int hi, int L) {
     if (t >= lo && t < hi) {  // at most one request holds the token
       sm.req[0] = r;
       sm.req[1] = lo;
       sm.req[2] = hi - lo;
       sm.req[3] = L;
     }
-  }
+  };
+  if (tid < c.B) test(tid, cs.lo - cs.base, cs.hi - cs.base, cs.len);
+  for (int r = tid + NT; r < c.B; r += NT)  // batches of more than NT requests
+    test(r, c.qsl[r] - cs.base, c.qsl[r + 1] - cs.base, c.seq_lens[r]);
   __syncthreads();
+}
+
+// Returns whether the entries were staged (the same in every thread).
+template <class SM>
+__device__ __forceinline__ bool combine_stage_bt(SM& sm, const TopkIn& c, int64_t t, int ps,
+                                                 int32_t* bt_lds, int w, int lane) {
+  const int b = sm.req[0];
+  if (b < 0 || c.bt_stride <= 0) return false;
+  const int64_t pos = (int64_t)sm.req[3] - sm.req[2] + (t - sm.req[1]);
+  const int64_t np = min((int64_t)c.bt_stride, (max(pos, (int64_t)0) >> ps) + 1);
+  if (np > kBtStage) return false;
+  copy_row_to_lds(bt_lds, c.block_table + (int64_t)b * c.bt_stride, (int)np, w, lane);
+  return true;
 }
 
 template <int NT = 256, class SM>
 __device__ __forceinline__ int combine_rows(SM& sm, const TopkIn& c, int64_t t, int ps,
-                                           int tid, const int32_t (&xv)[kIdxBlock / NT], int tl) {
+                                           int tid, const int32_t (&xv)[kIdxBlock / NT], int tl,
+                                           const int32_t* bt_lds, bool staged) {
   constexpr int kPer = kIdxBlock / NT;
   const int kmax = min(c.top_k, c.topk_width);
-  const int b = sm.req[0];
+  const int b = __builtin_amdgcn_readfirstlane(sm.req[0]);
   if (b < 0) return 0;
-  const int64_t pos = (int64_t)sm.req[3] - sm.req[2] + (t - sm.req[1]);
+  const int64_t pos = (int64_t)__builtin_amdgcn_readfirstlane(sm.req[3]) -
+                      __builtin_amdgcn_readfirstlane(sm.req[2]) +
+                      (t - __builtin_amdgcn_readfirstlane(sm.req[1]));
   int64_t tk = min(pos + 1, (int64_t)c.top_k);
   tk = min(tk, (int64_t)tl);
   tk = max(tk, (int64_t)0);
   const int64_t sw = max(min(pos + 1, (int64_t)c.window), (int64_t)0);
-  const int64_t lo = pos - sw + 1;
-  const int32_t* bt_row = c.block_table + (int64_t)b * c.bt_stride;
   const int n = (int)(tk + sw);
-  int64_t xs[kPer];
-  int32_t pg[kPer];
+  if (n <= 0) return 0;
+  // n > 0 means pos >= 0, and pos < 2^31 (seq_lens are int32): every position and page
+  // below fits in 32 bits
+  const int lo = (int)(pos - sw + 1), tk32 = (int)tk;
+  const int32_t* bt_row = c.block_table + (int64_t)b * c.bt_stride;
+  // staged entries: logical pages 0 .. np - 1 (every valid entry's page lies there)
+  const int np = (int)min((int64_t)c.bt_stride, (pos >> ps) + 1);
+  // per entry, branch-free: the value of a top-k entry or the window position, then
+  // its page from the staged entries (or from memory), all lanes reading
+  int32_t xs[kPer], pg[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int j = tid + NT * u;
-    int64_t x = j < tk ? (j < kmax ? (int64_t)xv[u] : -1) : lo + (j - tk);
-    if (j < tk && !(x >= 0 && x < lo)) x = -1;  // invalid, beyond pos, or in the window
-    if (j >= n) x = -1;
-    xs[u] = x;
-    const int64_t lp = x >> ps;
-    pg[u] = (NT * u < n && c.bt_stride > 0)
-                ? bt_row[lp < 0 ? 0 : (lp < c.bt_stride ? lp : c.bt_stride - 1)] : -1;
+    int x = j < kmax ? xv[u] : -1;
+    x = (x >= 0 && x < lo) ? x : -1;  // invalid, beyond pos, or in the window
+    x = j < tk32 ? x : lo + (j - tk32);
+    xs[u] = j < n ? x : -1;
+  }
+  // the staged entries are read unconditionally (clamped into the staged range) and,
+  // when the row was too long to stage, replaced by lookups in memory: an if / else
+  // would let the compiler fold both into one generic-address (flat) path
+  const int nps = min(np, kBtStage);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int lp = xs[u] >> ps;
+    pg[u] = bt_lds[lp < 0 ? 0 : (lp < nps ? lp : nps - 1)];
+  }
+  if (!staged) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int lp = xs[u] >> ps;
+      pg[u] = c.bt_stride > 0 ? bt_row[lp < 0 ? 0 : (lp < c.bt_stride ? lp : c.bt_stride - 1)] : -1;
+    }
   }
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int j = tid + NT * u;
-    const int64_t x = xs[u];
+    const int x = xs[u];
     const bool ok = x >= 0 && (x >> ps) < c.bt_stride && pg[u] >= 0;
     if (j < n) sm.idx[j] = ok ? (int32_t)(((int64_t)pg[u] << ps) + (x & ((1 << ps) - 1))) : -1;
   }
   return n;
 }
-
-template <int NT = 256, class SM>
-__device__ __forceinline__ int stage_combined(SM& sm, const TopkIn& c, int64_t t, int ps, int tid) {
-  int32_t xv[kIdxBlock / NT];
-  int tl;
-  combine_request<NT>(sm, c, t, tid, xv, tl);
-  return combine_rows<NT>(sm, c, t, ps, tid, xv, tl);
-}
-
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
