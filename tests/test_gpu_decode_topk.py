@@ -88,6 +88,45 @@ def test_decode_topk_equals_combine_then_decode(dsv4, seed):
         assert torch.all(torch.isneginf(lse1[-2:]))
 
 
+@pytest.mark.parametrize("P", [32, 64])
+def test_decode_topk_long_block_tables(dsv4, P):
+    """Requests whose block-table rows are longer than the entries a workgroup stages in
+    LDS (16384 pages: positions past 2^19 at 32 slots a page, 2^20 at 64) take the
+    per-entry lookups in memory; shorter ones the staged copy.  Both against the separate
+    combine + decode, bit for bit.  The logical pages map into a small pool of physical
+    pages (with holes), so the cache stays small."""
+    rng = np.random.default_rng(2400 + P)
+    npg = 48
+    seq_lens = np.array([16384 * P + 977, 16384 * P - 5, 16384 * P + 1, 3000], np.int32)
+    B = seq_lens.size
+    qlens = np.array([1, 2, 1, 1])
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qsl[-1])
+    pages = (seq_lens.astype(np.int64) + P - 1) // P
+    bt = rng.integers(0, npg, size=(B, int(pages.max()))).astype(np.int32)
+    bt[rng.random(bt.shape) < 0.01] = -1  # holes
+    cache = np.zeros(npg * P * 648, np.uint8)
+    slots = np.arange(npg * P, dtype=np.int64)
+    oracle.kv_insert(np.zeros((slots.size, 0, 576), np.uint16), bf16_normal(rng, (slots.size, 576)),
+                     slots % 3000, slots, rope_table(3000), np.zeros(576, np.uint16), 1e-6, cache,
+                     npg, P, inplace=True)
+    top_k, window, H = 512, 64, 64
+    pos = np.concatenate([L - ql + np.arange(ql) for L, ql in zip(seq_lens, qlens)])
+    topk = np.stack([rng.integers(0, p + 1, size=top_k) for p in pos]).astype(np.int32)
+    topk[:, -7:] = -1
+    q = bf16_normal(rng, (T, H, 576))
+    sinks = rng.standard_normal(H).astype(np.float32)
+    W = (top_k + window + 127) // 128 * 128
+    log(f"decode_topk long block tables P={P} rows of {pages.tolist()} pages")
+    args = (dev_bf16(q), dev(cache), dev(topk), None, dev(qsl), dev(seq_lens), dev(bt), top_k,
+            window, dev(sinks))
+    out2, lse2, _, lens = _two_step(dsv4, *args, P, W)
+    out1, lse1 = _fused(dsv4, *args, P)
+    torch.cuda.synchronize()
+    assert _same(out1, out2) and _same(lse1, lse2)
+    assert int(lens.min().item()) > 0
+
+
 def test_decode_topk_benchmark_workload(dsv4):
     wl = attention_workload(2, seed=11, instances=1)
     it = wl["instances"][0]
