@@ -137,13 +137,6 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.o32[mb][r] = 0.f;
 
-  // Chunks of records in flight per lane: two (buffers A and B, odd chunks in B), or one
-  // for bf16 records at 32 heads (72 registers a chunk beside Q for 32 heads).
-  constexpr int kAhead = (KV == kKvBf16 && NHB == 2) ? 1 : 2;
-  RawT<KV> A, B;
-  RawT<KV>& odd = kAhead == 2 ? B : A;
-  const int row = 16 * w + l16;
-  const CacheRef cr{STEP ? sti.cache : cache, num_slots, ps};
 
   // Index blocks of up to 4096 entries are staged in LDS.  Inside a block chunk c lives
   // in register buffer c&1 and LDS tiles c&1; a buffer is refilled with chunk c+2 as
@@ -190,7 +183,7 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     asm volatile("" ::: "memory");  // every load above is issued before the wait
     __builtin_amdgcn_s_waitcnt(0);  // (includes the copy into LDS)
     __syncthreads();
-    end = combine_rows(sm, tin, t, ps, tid, xv, tl, bt, staged);
+    end = __builtin_amdgcn_readfirstlane(combine_rows(sm, tin, t, ps, tid, xv, tl, bt, staged));
     // this wave's q rows normalised and rotated into LDS (for the Q fragments) and, when
     // the row is not cut into pieces, written back in place.  With pieces, the
     // workgroups of a token's other pieces may still be about to read the raw rows (a
@@ -242,7 +235,7 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);  // (includes the copy into LDS)
     __syncthreads();
-    end = combine_rows(sm, tin, t, ps, tid, xv, tl, bt, staged);
+    end = __builtin_amdgcn_readfirstlane(combine_rows(sm, tin, t, ps, tid, xv, tl, bt, staged));
     load_q_global();
   } else {
     int32_t iv[kStagePer];
@@ -285,6 +278,8 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
 #pragma unroll
     for (int k = 0; k < 18; ++k) asm volatile("" : "+a"(st.qf[1][k]));
   }
+  const int row = 16 * w + l16;
+  const CacheRef cr{STEP ? sti.cache : cache, num_slots, ps};
   for (int blk0 = beg; blk0 < end; blk0 += kIdxBlock) {
     const int n_blk = min(end - blk0, kIdxBlock);
     if (blk0 != beg) {
@@ -293,6 +288,11 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
       __syncthreads();
     }
     const int nch = (n_blk + kChunk - 1) / kChunk;
+    // Chunks of records in flight per lane: two (buffers A and B, odd chunks in B), or
+    // one for bf16 records at 32 heads (72 registers a chunk beside Q for 32 heads).
+    constexpr int kAhead = (KV == kKvBf16 && NHB == 2) ? 1 : 2;
+    RawT<KV> A, B;
+    RawT<KV>& odd = kAhead == 2 ? B : A;
     load_raw<KV>(A, cr, idx_at(sm.idx, row, n_blk), g);
     if constexpr (kAhead == 2) load_raw<KV>(B, cr, idx_at(sm.idx, kChunk + row, n_blk), g);
     {  // prologue: stage chunk 0 and settle its probabilities
