@@ -271,12 +271,18 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
   }
   if constexpr (NHB == 2 && STEP) {
     // The step's prologue leaves more values live than the other variants, and the
-    // register allocator would otherwise spill the second head block's Q fragments to
-    // AGPRs and copy each one back into VGPRs before every use (72 copies per chunk).
-    // Placing them in AGPRs from the start lets the MFMAs read them there directly (an
-    // MFMA accepts AGPR A/B operands); the empty asm only fixes the register class.
+    // register allocator would otherwise spill Q fragments to AGPRs and copy each one
+    // back into VGPRs before every use (72 copies per chunk for the second head block,
+    // then 12 for the first block's first three).  Placing the second block and the
+    // first ten fragments of the first in AGPRs from the start lets the MFMAs read them
+    // there directly (an MFMA accepts AGPR A/B operands); the empty asm only fixes the
+    // register class.  Measured: step 63.9 -> 61.5 us (B = 64, H = 128), MTP step 581
+    // -> 578 us; 3, 6 or 13 of the first block's fragments were slower, all 18 much
+    // slower (66.7 us).
 #pragma unroll
     for (int k = 0; k < 18; ++k) asm volatile("" : "+a"(st.qf[1][k]));
+#pragma unroll
+    for (int k = 0; k < 10; ++k) asm volatile("" : "+a"(st.qf[0][k]));
   }
   const int row = 16 * w + l16;
   const CacheRef cr{STEP ? sti.cache : cache, num_slots, ps};

@@ -71,8 +71,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x);
 }
 
+// Two fp32 values -> two bf16 (round to nearest even) in one dword, a in the low half: one
+// v_cvt_pk_bf16_f32 (two scalar conversions would also shift and merge the halves).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 }  // namespace dsv4
