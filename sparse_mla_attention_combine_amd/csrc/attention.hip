@@ -191,7 +191,7 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
     // reads raw q and only the merge launch, stream-ordered after all of them, writes
     // the normalised rows.
     const bool q_writer = splits == 1;
-    u32x4* ql = reinterpret_cast<u32x4*>(&sm.v[1][0][0]) + (8 * w + (lane >> 3)) * (kLatent / 8) + c8;
+    u32x4* ql = reinterpret_cast<u32x4*>(&sm.v[1][0][0]) + (8 * w + (lane >> 3)) * (kQRow / 8) + c8;
     if (w < 2 * NHB) {
       if (qok) {
         u32x4* qg = reinterpret_cast<u32x4*>(sti.q + ((int64_t)t * H + h0 + 8 * w + (lane >> 3)) *
@@ -267,7 +267,7 @@ __global__ void __launch_bounds__(256) sparse_mla_kernel(
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
       load_q_frags(st.qf[hb], reinterpret_cast<const uint16_t*>(&sm.v[1][0][0]) +
-                                  (16 * hb + l16) * kLatent, g);
+                                  (16 * hb + l16) * kQRow, g);
   }
   if constexpr (NHB == 2 && STEP) {
     // The step's prologue leaves more values live than the other variants, and the
