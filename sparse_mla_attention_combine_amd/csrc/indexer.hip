@@ -52,11 +52,24 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int* wsum) {
 
 template <int NT, bool STAGE>
 struct SelSmem {
-  uint32_t keys[STAGE ? kStageMax : 1];
+  alignas(16) uint32_t keys[STAGE ? kStageMax : 1];
   uint32_t hist[kBins];
   int wsum[NT / 64];
+  int wtab[NT / 64 * 4];   // compaction: (gt, eq) count of wave w in round r at 4w + r ...
+  int wbase[NT / 64 * 4];  // ... and of everything before it in emission order
   uint32_t sh_digit, sh_above;
 };
+
+// Inclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
 
 // One histogram pass that reads the keys from memory (keeping them in LDS if `staged`):
 // ITEMS keys per thread are requested before any is used, at clamped indices (a load
@@ -103,9 +116,15 @@ __device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm, int n, int 
     for (int d = tid; d < kBins; d += NT) sm.hist[d] = 0;
     __syncthreads();
     if (staged && pass > 0) {
-      for (int j = tid; j < n; j += NT) {
-        const uint32_t key = sm.keys[j];
-        if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & dmask], 1u);
+      // eight keys per thread read before any is tested, so their LDS latencies overlap
+      for (int j0 = 0; j0 < n; j0 += NT * kSelItems) {
+        uint32_t v[kSelItems];
+#pragma unroll
+        for (int u = 0; u < kSelItems; ++u) v[u] = sm.keys[min(j0 + u * NT + tid, n - 1)];
+#pragma unroll
+        for (int u = 0; u < kSelItems; ++u)
+          if (j0 + u * NT + tid < n && (v[u] & mask) == prefix)
+            atomicAdd(&sm.hist[(v[u] >> shift) & dmask], 1u);
       }
     } else {
       bool done = false;
@@ -149,6 +168,69 @@ __device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm, int n, int 
   }
   const uint32_t K = prefix;
   const int m = remaining;  // keys equal to K that are taken, the smallest indices first
+  if constexpr (STAGE && kStageMax / (NT * kSelItems) * (NT / 64) <= 64) {
+    if (staged) {
+      // The same ordered emission with the keys in LDS, in fewer barriers: every round's
+      // (gt, eq) counts per wave first, one wave's scan of them in emission order (rounds
+      // outer, waves inner), then the emission, each thread recounting its 8 keys.
+      const int rounds = (n + NT * kSelItems - 1) / (NT * kSelItems);
+      const int lane = tid & 63, w = tid >> 6;
+      // a thread's 8 keys as two 16 B reads (8 single reads of one thread's consecutive
+      // keys put 64 lanes on 8 banks); entries past n hold stale keys and are masked
+      auto keys8 = [&](int first, uint32_t (&key)[kSelItems]) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&sm.keys[first]);
+        const uint4 b = *reinterpret_cast<const uint4*>(&sm.keys[first + 4]);
+        key[0] = a.x; key[1] = a.y; key[2] = a.z; key[3] = a.w;
+        key[4] = b.x; key[5] = b.y; key[6] = b.z; key[7] = b.w;
+      };
+      auto count = [&](int r) {
+        const int first = r * NT * kSelItems + tid * kSelItems;
+        uint32_t key[kSelItems];
+        keys8(first, key);
+        int cgt = 0, ceq = 0;
+#pragma unroll
+        for (int j = 0; j < kSelItems; ++j) {
+          cgt += (first + j < n && key[j] > K) ? 1 : 0;
+          ceq += (first + j < n && key[j] == K) ? 1 : 0;
+        }
+        return cgt | (ceq << 16);  // at most NT * kSelItems of each per round
+      };
+#pragma unroll 1
+      for (int r = 0; r < rounds; ++r) {
+        const int incl = wave_inclusive_scan(count(r));
+        if (lane == 63) sm.wtab[4 * w + r] = incl;
+      }
+      __syncthreads();
+      if (tid < 64) {  // entry r * (NT / 64) + w of the emission order
+        const int r = tid / (NT / 64), ww = tid % (NT / 64);
+        const int v = r < rounds ? sm.wtab[4 * ww + r] : 0;
+        sm.wbase[4 * ww + r] = wave_inclusive_scan(v) - v;  // totals stay below 2^16 each
+      }
+      __syncthreads();
+#pragma unroll 1
+      for (int r = 0; r < rounds; ++r) {
+        const int packed = count(r);
+        const int excl = sm.wbase[4 * w + r] + wave_inclusive_scan(packed) - packed;
+        const int gt_before = excl & 0xFFFF, eq_before = excl >> 16;
+        int p = gt_before + min(eq_before, m);
+        int eq_rank = eq_before;
+        const int first = r * NT * kSelItems + tid * kSelItems;
+        uint32_t key[kSelItems];
+        keys8(first, key);
+#pragma unroll
+        for (int j = 0; j < kSelItems; ++j) {
+          if (first + j >= n) break;
+          if (key[j] > K) {
+            emit(p++, first + j, key[j]);
+          } else if (key[j] == K) {
+            if (eq_rank < m) emit(p++, first + j, key[j]);
+            ++eq_rank;
+          }
+        }
+      }
+      return;
+    }
+  }
   int gt_run = 0, eq_run = 0;
   for (int c0 = 0; c0 < n; c0 += NT * kSelItems) {
     const int first = c0 + tid * kSelItems;
