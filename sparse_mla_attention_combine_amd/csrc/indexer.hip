@@ -32,15 +32,26 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive scan over the 64 lanes of a wave, in DPP moves (no LDS round trip): shifts
+// by 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from outside the row
+// add 0), then row 0's total into row 1 and row 2's into row 3 (broadcast of lane 15 of
+// each row to the next, rows 1 and 3 only), then lane 31's running total into rows 2
+// and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Inclusive scan over the block of NT threads; `wsum` holds one int per wave.
 template <int NT>
 __device__ __forceinline__ int block_inclusive_scan(int x, int* wsum) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  x = wave_inclusive_scan(x);
   if (lane == 63) wsum[w] = x;
   __syncthreads();
   int add = 0;
@@ -59,17 +70,6 @@ struct SelSmem {
   int wbase[NT / 64 * 4];  // ... and of everything before it in emission order
   uint32_t sh_digit, sh_above;
 };
-
-// Inclusive scan over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
 
 // One histogram pass that reads the keys from memory (keeping them in LDS if `staged`):
 // ITEMS keys per thread are requested before any is used, at clamped indices (a load
