@@ -11,9 +11,11 @@
 // wide enough that similar logits rarely collide on one bin) finds the k-th largest
 // key K and how many keys equal to K are taken (m); one ordered pass then emits every
 // id with key > K and the first m ids with key == K.  Each thread owns 8 consecutive
-// candidates per compaction pass, so a block-wide scan of its counts (packed into one
-// 32-bit value) gives every thread its output position.  Integer decisions on fp32
-// keys only: bit-exact with the oracle's fp32 comparisons.
+// candidates per round, so a scan of per-wave counts (gt and eq packed into one 32-bit
+// value) gives every thread its output position.  When few keys share K's first two
+// digits, the third pass already counts the rest per wave and lists those few, and the
+// emission needs no counting sweep.  Integer decisions on fp32 keys only: bit-exact
+// with the oracle's fp32 comparisons.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -22,6 +24,7 @@ namespace dsv4 {
 constexpr int kSelItems = 8;
 constexpr int kStageMax = 32768;  // rows up to this many candidates keep their keys in LDS
 constexpr int kBins = 2048;       // radix digits of 11, 11 and 10 bits
+constexpr int kListMax = 512;     // staged rows: keys sharing K's first two digits listed up to this many
 
 // Larger key <=> larger logit; -0 and +0 share a key (they compare equal), NaN takes the
 // key of -inf.
@@ -69,16 +72,18 @@ struct SelSmem {
   int wtab[NT / 64 * 4];   // compaction: (gt, eq) count of wave w in round r at 4w + r ...
   int wbase[NT / 64 * 4];  // ... and of everything before it in emission order
   uint32_t sh_digit, sh_above;
+  uint32_t lkey[STAGE ? kListMax : 1];  // staged rows: the keys sharing K's first two digits
+  int lidx[STAGE ? kListMax : 1];       // ... and their indices
+  int lcount;
 };
 
-// One histogram pass that reads the keys from memory (keeping them in LDS if `staged`):
-// ITEMS keys per thread are requested before any is used, at clamped indices (a load
-// under a per-lane condition is waited for on the spot); entries past n are ignored.
-// Each round of ITEMS loads costs one memory latency, so a staged row goes in one round.
+// One histogram pass that reads the keys from memory (rows that are not staged): ITEMS
+// keys per thread are requested before any is used, at clamped indices (a load under a
+// per-lane condition is waited for on the spot); entries past n are ignored.
 template <int ITEMS, int NT, bool STAGE, typename KeyAt>
 __device__ __forceinline__ void hist_from_memory(SelSmem<NT, STAGE>& sm, int n, int tid,
-                                                 bool staged, uint32_t mask, uint32_t prefix,
-                                                 int shift, uint32_t dmask, KeyAt key_at) {
+                                                 uint32_t mask, uint32_t prefix, int shift,
+                                                 uint32_t dmask, KeyAt key_at) {
   for (int j0 = 0; j0 < n; j0 += NT * ITEMS) {
     uint32_t v[ITEMS];
 #pragma unroll
@@ -86,55 +91,129 @@ __device__ __forceinline__ void hist_from_memory(SelSmem<NT, STAGE>& sm, int n, 
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u) {
       const int j = j0 + u * NT + tid;
+      if (j < n && (v[u] & mask) == prefix) atomicAdd(&sm.hist[(v[u] >> shift) & dmask], 1u);
+    }
+  }
+}
+
+// The first pass of a staged row: every key into LDS and its first digit into the
+// histogram.  The row is read as a raw buffer of n floats whose whole offset is the
+// range-checked vector offset, so a load past the row's end returns 0 and reads nothing
+// (no index clamping, one offset register per load); eight loads per thread in flight
+// (measured: 8 beat 4, 16 and 32 a round).
+template <int NT>
+__device__ __forceinline__ void stage_row(SelSmem<NT, true>& sm, const float* row, int n,
+                                          int tid) {
+  // the row address and n are the same in every lane; said so, the buffer resource is
+  // built in scalar registers
+  const uint64_t ra = reinterpret_cast<uint64_t>(row);
+  const uint64_t ua =
+      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ra >> 32)) << 32) |
+      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ra);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<float*>(ua), (short)0, __builtin_amdgcn_readfirstlane(n) * 4, 0x00020000);
+#pragma unroll 1
+  for (int j0 = 0; j0 < n; j0 += NT * kSelItems) {
+    float x[kSelItems];
+#pragma unroll
+    for (int u = 0; u < kSelItems; ++u)
+      x[u] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rs, (j0 + u * NT + tid) * 4, 0, 0));
+#pragma unroll
+    for (int u = 0; u < kSelItems; ++u) {
+      const int j = j0 + u * NT + tid;
       if (j < n) {
-        if (staged) sm.keys[j] = v[u];
-        if ((v[u] & mask) == prefix) atomicAdd(&sm.hist[(v[u] >> shift) & dmask], 1u);
+        const uint32_t v = order_key(x[u]);
+        sm.keys[j] = v;
+        atomicAdd(&sm.hist[v >> 21], 1u);
       }
     }
   }
 }
 
-// The k largest of n keys (0 < k < n), ties to the smaller index j: a radix select of the
-// k-th largest key K (digits of 11, 11 and 10 bits, most significant first) and how many
-// keys equal to K are taken (m), then one ordered pass that calls emit(p, j, key) for
-// every j with key > K and the first m with key == K, p = the pick's rank in ascending j.
-// key_at(j) gives key j for 0 <= j < n; the first pass calls it for every j (eight per
-// thread in flight, at clamped indices) and, with STAGE and n <= kStageMax, keeps the
-// keys in LDS for the other passes; otherwise every pass calls it again.  NT threads,
-// all of which must call; barriers inside.
-template <int NT, bool STAGE, typename KeyAt, typename Emit>
-__device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm, int n, int k, KeyAt key_at,
+// The k largest of n keys (0 < k < n) of `row`, ties to the smaller index j: a radix
+// select of the k-th largest key K (digits of 11, 11 and 10 bits, most significant first)
+// and how many keys equal to K are taken (m), then one ordered pass that calls
+// emit(p, j) for every j with key > K and the first m with key == K, p = the pick's rank
+// in ascending j.  With STAGE and n <= kStageMax the first pass keeps the keys in LDS
+// for the other passes; otherwise every pass reads the row again.  NT threads, all of
+// which must call; barriers inside.
+template <int NT, bool STAGE, typename Emit>
+__device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm,
+                                             const float* __restrict__ row, int n, int k,
                                              Emit emit) {
-  const int tid = threadIdx.x;
+  static_assert(!STAGE || (kStageMax <= 4 * NT * kSelItems && NT <= 1024),
+                "a staged row is at most 4 rounds of 8 keys per thread; the emission table "
+                "(4 rounds x NT / 64 waves) is scanned by one wave");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const bool staged = STAGE && n <= kStageMax;
+  auto key_at = [&](int j) { return order_key(row[j]); };
+  // staged rows are read in rounds of 8 consecutive keys per thread (keys
+  // r * 8 NT + 8 tid ..+7 in round r), the emission's order; a thread's 8 keys as two
+  // 16 B reads (8 single reads of one thread's consecutive keys put 64 lanes on 8
+  // banks); entries past n hold stale keys and are masked
+  const int rounds = (n + NT * kSelItems - 1) / (NT * kSelItems);
+  auto keys8 = [&](int first, uint32_t (&key)[kSelItems]) {
+    const uint4 a = *reinterpret_cast<const uint4*>(&sm.keys[first]);
+    const uint4 b = *reinterpret_cast<const uint4*>(&sm.keys[first + 4]);
+    key[0] = a.x; key[1] = a.y; key[2] = a.z; key[3] = a.w;
+    key[4] = b.x; key[5] = b.y; key[6] = b.z; key[7] = b.w;
+  };
   uint32_t prefix = 0, mask = 0;
   int remaining = k;
+  // List mode (staged rows where at most kListMax keys share K's first two digits, known
+  // from the second histogram): the third pass also counts, per emission group (round,
+  // wave), the keys whose first two digits beat K's (all larger than K) and lists the
+  // keys that share them; the emission's counts then come from that list.
+  bool use_list = false;
 #pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const uint32_t dmask = pass == 2 ? 1023u : 2047u;
     for (int d = tid; d < kBins; d += NT) sm.hist[d] = 0;
+    if (STAGE && tid == 0) sm.lcount = 0;
     __syncthreads();
-    if (staged && pass > 0) {
-      // eight keys per thread read before any is tested, so their LDS latencies overlap
-      for (int j0 = 0; j0 < n; j0 += NT * kSelItems) {
-        uint32_t v[kSelItems];
+    if (!staged) {
+      hist_from_memory<kSelItems>(sm, n, tid, mask, prefix, shift, dmask, key_at);
+    } else if constexpr (STAGE) {
+      if (pass == 0) {
+        stage_row<NT>(sm, row, n, tid);
+      } else if (pass == 2 && use_list) {
+        const uint32_t top = prefix >> 10;  // K's first two digits
+#pragma unroll 1
+        for (int r = 0; r < rounds; ++r) {
+          const int first = r * NT * kSelItems + tid * kSelItems;
+          uint32_t key[kSelItems];
+          keys8(first, key);
+          int ca = 0;
 #pragma unroll
-        for (int u = 0; u < kSelItems; ++u) v[u] = sm.keys[min(j0 + u * NT + tid, n - 1)];
+          for (int i = 0; i < kSelItems; ++i) {
+            const bool valid = first + i < n;
+            ca += (valid && (key[i] >> 10) > top) ? 1 : 0;
+            if (valid && (key[i] >> 10) == top) {
+              atomicAdd(&sm.hist[key[i] & 1023u], 1u);
+              const int pos = atomicAdd(&sm.lcount, 1);
+              if (pos < kListMax) {
+                sm.lkey[pos] = key[i];
+                sm.lidx[pos] = first + i;
+              }
+            }
+          }
+          const int incl = wave_inclusive_scan(ca);
+          if (lane == 63) sm.wtab[4 * w + r] = incl;  // the group's (gt, eq) so far: eq 0
+        }
+      } else {
+#pragma unroll 1
+        for (int r = 0; r < rounds; ++r) {
+          const int first = r * NT * kSelItems + tid * kSelItems;
+          uint32_t key[kSelItems];
+          keys8(first, key);
 #pragma unroll
-        for (int u = 0; u < kSelItems; ++u)
-          if (j0 + u * NT + tid < n && (v[u] & mask) == prefix)
-            atomicAdd(&sm.hist[(v[u] >> shift) & dmask], 1u);
-      }
-    } else {
-      bool done = false;
-      if constexpr (STAGE) {
-        if (staged && n > NT * kSelItems) {  // a long staged row: twice the keys per round
-          hist_from_memory<2 * kSelItems>(sm, n, tid, true, mask, prefix, shift, dmask, key_at);
-          done = true;
+          for (int i = 0; i < kSelItems; ++i)
+            if (first + i < n && (key[i] & mask) == prefix)
+              atomicAdd(&sm.hist[(key[i] >> shift) & dmask], 1u);
         }
       }
-      if (!done) hist_from_memory<kSelItems>(sm, n, tid, staged, mask, prefix, shift, dmask, key_at);
     }
     __syncthreads();
     // thread i owns the kBins/NT digits below dmask - (kBins/NT)*i (from the top); after
@@ -161,6 +240,8 @@ __device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm, int n, int 
       above += cnt[r];
     }
     __syncthreads();
+    if (staged && pass == 1)  // how many keys share the first two digits of K
+      use_list = (int)sm.hist[sm.sh_digit] <= kListMax;
     prefix |= sm.sh_digit << shift;
     mask |= dmask << shift;
     remaining -= (int)sm.sh_above;
@@ -168,37 +249,37 @@ __device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm, int n, int 
   }
   const uint32_t K = prefix;
   const int m = remaining;  // keys equal to K that are taken, the smallest indices first
-  if constexpr (STAGE && kStageMax / (NT * kSelItems) * (NT / 64) <= 64) {
+  if constexpr (STAGE) {
     if (staged) {
-      // The same ordered emission with the keys in LDS, in fewer barriers: every round's
-      // (gt, eq) counts per wave first, one wave's scan of them in emission order (rounds
-      // outer, waves inner), then the emission, each thread recounting its 8 keys.
-      const int rounds = (n + NT * kSelItems - 1) / (NT * kSelItems);
-      const int lane = tid & 63, w = tid >> 6;
-      // a thread's 8 keys as two 16 B reads (8 single reads of one thread's consecutive
-      // keys put 64 lanes on 8 banks); entries past n hold stale keys and are masked
-      auto keys8 = [&](int first, uint32_t (&key)[kSelItems]) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&sm.keys[first]);
-        const uint4 b = *reinterpret_cast<const uint4*>(&sm.keys[first + 4]);
-        key[0] = a.x; key[1] = a.y; key[2] = a.z; key[3] = a.w;
-        key[4] = b.x; key[5] = b.y; key[6] = b.z; key[7] = b.w;
-      };
-      auto count = [&](int r) {
-        const int first = r * NT * kSelItems + tid * kSelItems;
-        uint32_t key[kSelItems];
-        keys8(first, key);
-        int cgt = 0, ceq = 0;
-#pragma unroll
-        for (int j = 0; j < kSelItems; ++j) {
-          cgt += (first + j < n && key[j] > K) ? 1 : 0;
-          ceq += (first + j < n && key[j] == K) ? 1 : 0;
+      // The ordered emission with the keys in LDS: every round's (gt, eq) counts per wave
+      // first, one wave's scan of them in emission order (rounds outer, waves inner),
+      // then the emission, each thread recounting its 8 keys.
+      if (use_list) {
+        // the listed keys that are picks join their groups' counts
+        const int nl = sm.lcount;
+        for (int i = tid; i < nl; i += NT) {
+          const uint32_t v = sm.lkey[i];
+          const int j = sm.lidx[i];
+          const int r = j / (NT * kSelItems), ww = (j % (NT * kSelItems)) / (64 * kSelItems);
+          if (v > K) atomicAdd(&sm.wtab[4 * ww + r], 1);
+          else if (v == K) atomicAdd(&sm.wtab[4 * ww + r], 1 << 16);
         }
-        return cgt | (ceq << 16);  // at most NT * kSelItems of each per round
-      };
+      } else {
 #pragma unroll 1
-      for (int r = 0; r < rounds; ++r) {
-        const int incl = wave_inclusive_scan(count(r));
-        if (lane == 63) sm.wtab[4 * w + r] = incl;
+        for (int r = 0; r < rounds; ++r) {
+          const int first = r * NT * kSelItems + tid * kSelItems;
+          uint32_t key[kSelItems];
+          keys8(first, key);
+          int cgt = 0, ceq = 0;
+#pragma unroll
+          for (int i = 0; i < kSelItems; ++i) {
+            cgt += (first + i < n && key[i] > K) ? 1 : 0;
+            ceq += (first + i < n && key[i] == K) ? 1 : 0;
+          }
+          // at most NT * kSelItems of each per round
+          const int incl = wave_inclusive_scan(cgt | (ceq << 16));
+          if (lane == 63) sm.wtab[4 * w + r] = incl;
+        }
       }
       __syncthreads();
       if (tid < 64) {  // entry r * (NT / 64) + w of the emission order
@@ -209,23 +290,34 @@ __device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm, int n, int 
       __syncthreads();
 #pragma unroll 1
       for (int r = 0; r < rounds; ++r) {
-        const int packed = count(r);
-        const int excl = sm.wbase[4 * w + r] + wave_inclusive_scan(packed) - packed;
-        const int gt_before = excl & 0xFFFF, eq_before = excl >> 16;
-        int p = gt_before + min(eq_before, m);
-        int eq_rank = eq_before;
         const int first = r * NT * kSelItems + tid * kSelItems;
         uint32_t key[kSelItems];
         keys8(first, key);
+        uint32_t gtm = 0, eqm = 0;  // bit i: key first + i is above K / equal to K
 #pragma unroll
-        for (int j = 0; j < kSelItems; ++j) {
-          if (first + j >= n) break;
-          if (key[j] > K) {
-            emit(p++, first + j, key[j]);
-          } else if (key[j] == K) {
-            if (eq_rank < m) emit(p++, first + j, key[j]);
-            ++eq_rank;
-          }
+        for (int i = 0; i < kSelItems; ++i) {
+          const bool valid = first + i < n;
+          gtm |= (valid && key[i] > K) ? 1u << i : 0u;
+          eqm |= (valid && key[i] == K) ? 1u << i : 0u;
+        }
+        const int packed = __popc(gtm) | (__popc(eqm) << 16);
+        const int excl = sm.wbase[4 * w + r] + wave_inclusive_scan(packed) - packed;
+        const int gt_before = excl & 0xFFFF, eq_before = excl >> 16;
+        // the thread's equal keys that are still wanted: the first m - eq_before of them
+        const int want = m - eq_before;
+        uint32_t pm = gtm;
+        int seen = 0;
+#pragma unroll
+        for (int i = 0; i < kSelItems; ++i) {
+          const bool e = (eqm >> i) & 1u;
+          pm |= (e && seen < want) ? 1u << i : 0u;
+          seen += e ? 1 : 0;
+        }
+        int p = gt_before + min(eq_before, m);
+        while (pm) {  // the thread's picks in ascending index
+          const int i = __builtin_ctz(pm);
+          pm &= pm - 1u;
+          emit(p++, first + i);
         }
       }
       return;
@@ -236,13 +328,8 @@ __device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm, int n, int 
     const int first = c0 + tid * kSelItems;
     uint32_t key[kSelItems];
     int cgt = 0, ceq = 0;
-    if (staged) {
 #pragma unroll
-      for (int j = 0; j < kSelItems; ++j) key[j] = first + j < n ? sm.keys[first + j] : 0u;
-    } else {
-#pragma unroll
-      for (int j = 0; j < kSelItems; ++j) key[j] = key_at(min(first + j, n - 1));
-    }
+    for (int j = 0; j < kSelItems; ++j) key[j] = key_at(min(first + j, n - 1));
 #pragma unroll
     for (int j = 0; j < kSelItems; ++j) {
       cgt += (first + j < n && key[j] > K) ? 1 : 0;
@@ -260,9 +347,9 @@ __device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm, int n, int 
     for (int j = 0; j < kSelItems; ++j) {
       if (first + j >= n) break;
       if (key[j] > K) {
-        emit(p++, first + j, key[j]);
+        emit(p++, first + j);
       } else if (key[j] == K) {
-        if (eq_rank < m) emit(p++, first + j, key[j]);
+        if (eq_rank < m) emit(p++, first + j);
         ++eq_rank;
       }
     }
@@ -319,12 +406,11 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(
     if (k == n) {
       for (int j = tid; j < n; j += NT) out[j] = j;
     } else if (k > 0) {
-      radix_select<NT, STAGE>(sm, n, k, [&](int j) { return order_key(row[j]); },
-                              [&](int p, int j, uint32_t) { out[p] = j; });
+      radix_select<NT, STAGE>(sm, row, n, k, [&](int p, int j) { out[p] = j; });
     }
     for (int j = k + tid; j < topk_stride; j += NT) out[j] = -1;
     if (tid == 0) topk_lens[tk.t] = k;
-    __syncthreads();  // LDS reuse by the next token of this workgroup
+    if (i + (int)gridDim.y < qlen) __syncthreads();  // LDS reuse by this workgroup's next token
   }
 }
 

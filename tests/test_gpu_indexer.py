@@ -142,11 +142,12 @@ def test_indexer_topk_zero_width_output(dsv4):
     assert lens.cpu().tolist() == [0, 0]
 
 
-@pytest.mark.parametrize("ties", [1, 1023, 1024, 1025, 5000])
+@pytest.mark.parametrize("ties", [1, 511, 512, 513, 1023, 1024, 1025, 5000])
 def test_indexer_threshold_bin_sizes(dsv4, ties):
-    """Rows staged in LDS resolve the threshold bin by ranking its keys when it holds at
-    most 1024 of them, and by a radix select otherwise: a row of 99 logits 10.0, `ties`
-    logits 5.0 (the k-th largest, all in one bin) and -1.0 elsewhere, k = 100, on both
+    """Rows staged in LDS list the keys that share the k-th largest key's first two radix
+    digits when there are at most 512 of them (the emission's counts then come from the
+    list), and count them with a sweep over the row otherwise: a row of 99 logits 10.0,
+    `ties` logits 5.0 (the k-th largest, all equal) and -1.0 elsewhere, k = 100, on both
     sides of that limit; ids must match the oracle bit for bit (ties to the smaller id)."""
     rng = np.random.default_rng(1400 + ties)
     T, L, top_k = 3, 8192, 100
