@@ -22,7 +22,10 @@
 namespace dsv4 {
 
 constexpr int kSelItems = 8;
-constexpr int kStageMax = 32768;  // rows up to this many candidates keep their keys in LDS
+// rows of up to 4 rounds of 8 keys per thread (32 NT candidates: 32768 with 1024 threads,
+// 8192 with 256) keep their keys in LDS
+template <int NT>
+constexpr int stage_max() { return 4 * NT * 8; }
 constexpr int kBins = 2048;       // radix digits of 11, 11 and 10 bits
 constexpr int kListMax = 512;     // staged rows: keys sharing K's first two digits listed up to this many
 
@@ -66,7 +69,7 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int* wsum) {
 
 template <int NT, bool STAGE>
 struct SelSmem {
-  alignas(16) uint32_t keys[STAGE ? kStageMax : 1];
+  alignas(16) uint32_t keys[STAGE ? stage_max<NT>() : 1];
   uint32_t hist[kBins];
   int wsum[NT / 64];
   int wtab[NT / 64 * 4];   // compaction: (gt, eq) count of wave w in round r at 4w + r ...
@@ -135,18 +138,18 @@ __device__ __forceinline__ void stage_row(SelSmem<NT, true>& sm, const float* ro
 // select of the k-th largest key K (digits of 11, 11 and 10 bits, most significant first)
 // and how many keys equal to K are taken (m), then one ordered pass that calls
 // emit(p, j) for every j with key > K and the first m with key == K, p = the pick's rank
-// in ascending j.  With STAGE and n <= kStageMax the first pass keeps the keys in LDS
+// in ascending j.  With STAGE and n <= stage_max<NT>() the first pass keeps the keys in LDS
 // for the other passes; otherwise every pass reads the row again.  NT threads, all of
 // which must call; barriers inside.
 template <int NT, bool STAGE, typename Emit>
 __device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm,
                                              const float* __restrict__ row, int n, int k,
                                              Emit emit) {
-  static_assert(!STAGE || (kStageMax <= 4 * NT * kSelItems && NT <= 1024),
+  static_assert(kSelItems == 8 && NT <= 1024,
                 "a staged row is at most 4 rounds of 8 keys per thread; the emission table "
                 "(4 rounds x NT / 64 waves) is scanned by one wave");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const bool staged = STAGE && n <= kStageMax;
+  const bool staged = STAGE && n <= stage_max<NT>();
   auto key_at = [&](int j) { return order_key(row[j]); };
   // staged rows are read in rounds of 8 consecutive keys per thread (keys
   // r * 8 NT + 8 tid ..+7 in round r), the emission's order; a thread's 8 keys as two
@@ -282,10 +285,12 @@ __device__ __forceinline__ void radix_select(SelSmem<NT, STAGE>& sm,
         }
       }
       __syncthreads();
-      if (tid < 64) {  // entry r * (NT / 64) + w of the emission order
+      if (tid < 64) {  // lane r * (NT / 64) + w: entry (r, w) of the emission order
         const int r = tid / (NT / 64), ww = tid % (NT / 64);
-        const int v = r < rounds ? sm.wtab[4 * ww + r] : 0;
-        sm.wbase[4 * ww + r] = wave_inclusive_scan(v) - v;  // totals stay below 2^16 each
+        const bool entry = r < 4;  // 4 rounds x NT / 64 waves: all 64 lanes at NT = 1024
+        const int v = entry && r < rounds ? sm.wtab[4 * ww + r] : 0;
+        const int e = wave_inclusive_scan(v) - v;  // totals stay below 2^16 each
+        if (entry) sm.wbase[4 * ww + r] = e;
       }
       __syncthreads();
 #pragma unroll 1
@@ -385,9 +390,8 @@ __device__ __forceinline__ IdxTok indexer_token(const int32_t* __restrict__ qsl,
   return r;
 }
 
-// NT threads per token; STAGE keeps the keys of rows up to kStageMax candidates in LDS
-// (few tokens, long rows: one large workgroup per CU), otherwise every pass rereads the
-// row from the caches (many tokens: several small workgroups per CU).
+// NT threads per token; STAGE keeps the keys of rows up to 32 NT candidates in LDS
+// (longer rows: every pass rereads the row from the caches).
 template <int NT, bool STAGE>
 __global__ void __launch_bounds__(NT) indexer_topk_kernel(
     const float* __restrict__ logits, int logits_stride, const int32_t* __restrict__ qsl,
@@ -421,14 +425,15 @@ hipError_t launch_indexer_topk(const float* logits, int logits_stride, const int
   if (B == 0 || T == 0) return hipSuccess;
   int per_req = (T + B - 1) / B;
   int Y = per_req < 1 ? 1 : (per_req > 4096 ? 4096 : per_req);
-  // few tokens: one 16-wave workgroup per token with the row's keys in LDS; many tokens:
-  // 4-wave workgroups without staging, several per CU
+  // few tokens: one 16-wave workgroup per token, rows of up to 32768 candidates in LDS
+  // (128 KB); many tokens: 4-wave workgroups, rows of up to 8192 in LDS (32 KB), three
+  // workgroups per CU
   if (T < 1024)
     hipLaunchKernelGGL((indexer_topk_kernel<1024, true>), dim3(B, Y), dim3(1024), 0, stream,
                        logits, logits_stride, qsl, seq_lens, T, ratio, top_k, topk, topk_stride,
                        topk_lens);
   else
-    hipLaunchKernelGGL((indexer_topk_kernel<256, false>), dim3(B, Y), dim3(256), 0, stream,
+    hipLaunchKernelGGL((indexer_topk_kernel<256, true>), dim3(B, Y), dim3(256), 0, stream,
                        logits, logits_stride, qsl, seq_lens, T, ratio, top_k, topk, topk_stride,
                        topk_lens);
   return hipGetLastError();

@@ -103,8 +103,8 @@ def test_indexer_combine_decode_chain(dsv4):
 
 
 def test_indexer_topk_many_tokens(dsv4):
-    """T >= 1024 takes the small-workgroup schedule (no LDS staging): a 1500-token
-    prefill, causal candidates, coarse logits with ties."""
+    """T >= 1024 takes the small-workgroup schedule: a 1500-token prefill, causal
+    candidates, coarse logits with ties."""
     rng = np.random.default_rng(1500)
     L, top_k = 1500, 300
     qsl = np.array([0, L], np.int32)
@@ -114,6 +114,31 @@ def test_indexer_topk_many_tokens(dsv4):
     log("indexer many tokens 1500 x 1500")
     ref, rlen = oracle.indexer_topk(logits, qsl, seq, L, 1, top_k, top_k)
     got, glen = _gpu_topk(dsv4, logits, qsl, seq, L, 1, top_k, top_k)
+    assert np.array_equal(glen, rlen) and np.array_equal(got, ref)
+
+
+def test_indexer_topk_many_tokens_staged_and_reread(dsv4):
+    """T >= 1024 takes the 4-wave schedule, which stages rows of up to 8192 candidates in
+    LDS and rereads longer ones: a 1100-token request whose causal rows hold 7501..8600
+    candidates, coarse logits with ties, NaN and -inf, top-k 2048; two staged rows whose
+    2048th-largest logit is shared by 512 and by 513 keys (either side of the list limit
+    of keys sharing its first two radix digits)."""
+    rng = np.random.default_rng(1700)
+    T, width, top_k = 1100, 8700, 2048
+    qsl = np.array([0, T], np.int32)
+    seq = np.array([8600], np.int32)  # token i at position 7500 + i: n = 7501 + i
+    logits = (np.round(rng.standard_normal((T, width)) * 16) / 16).astype(np.float32)
+    logits[rng.random((T, width)) < 0.01] = np.nan
+    logits[rng.random((T, width)) < 0.01] = -np.inf
+    for t, ties in ((3, 512), (4, 513)):
+        n = 7501 + t
+        perm = rng.permutation(n)
+        logits[t, :] = -1.0
+        logits[t, perm[:top_k - 1]] = 10.0
+        logits[t, perm[top_k - 1:top_k - 1 + ties]] = 5.0
+    log("indexer many tokens 1100 x 7501..8600 (staged and reread)")
+    ref, rlen = oracle.indexer_topk(logits, qsl, seq, T, 1, top_k, top_k)
+    got, glen = _gpu_topk(dsv4, logits, qsl, seq, T, 1, top_k, top_k)
     assert np.array_equal(glen, rlen) and np.array_equal(got, ref)
 
 
