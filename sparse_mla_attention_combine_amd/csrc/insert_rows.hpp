@@ -42,11 +42,22 @@ __device__ __forceinline__ float qn_sum_sq(u32x4 c, float ss) {
   return ss;
 }
 
+// Partner values within each aligned group of 8 lanes, in DPP moves (no LDS round
+// trip): lane i ^ 1 and lane i ^ 2 (quad permutations), then lane 7 - i of the group
+// (half-row mirror), which lies in the other quad.  After the two quad steps every lane
+// of a quad holds the quad's result, so the mirror step gives every lane the same value
+// as an xor-4 step would.
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
+
 // All 8 lanes of a row must take part.
 __device__ __forceinline__ float qn_inv(float ss, float eps) {
-  ss += __shfl_xor(ss, 1, 8);
-  ss += __shfl_xor(ss, 2, 8);
-  ss += __shfl_xor(ss, 4, 8);
+  ss += dpp_partner<kDppXor1>(ss);
+  ss += dpp_partner<kDppXor2>(ss);
+  ss += dpp_partner<kDppHalfMirror>(ss);
   return 1.0f / sqrtf(ss * (1.0f / kLatent) + eps);
 }
 
@@ -125,9 +136,9 @@ __device__ __forceinline__ void kv_quant_store(const KvLane& v, const RopeCs& ro
     k[2 * e + 1] = bf16_bits_to_f32(u[e] >> 16);
     amax = fmaxf(amax, fmaxf(fabsf(k[2 * e]), fabsf(k[2 * e + 1])));
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+  amax = fmaxf(amax, dpp_partner<kDppXor1>(amax));
+  amax = fmaxf(amax, dpp_partner<kDppXor2>(amax));
+  amax = fmaxf(amax, dpp_partner<kDppHalfMirror>(amax));
   // smallest e with amax <= 448 * 2^e: amax = m * 2^k, m in [1,2): e = k-8 if m <= 1.75
   // else k-7; zero and fp32-subnormal amax (< 2^-126 < 448 * 2^-127) give e = -127.
   const uint32_t ab = __float_as_uint(amax);
