@@ -5,8 +5,10 @@
 // the result is the min(n, top_k) ids with the largest logits, ties to the smaller id
 // (a NaN logit counts as -inf), listed in ascending id order, -1 after them.
 //
-// One workgroup (16 waves) per token.  Logits map to order-preserving 32-bit keys,
-// staged in LDS by the first pass for rows of up to 32768 candidates; a radix select
+// One workgroup per token: 16 waves when there are few tokens, 4 waves (three
+// workgroups per CU) when there are many.  Logits map to order-preserving 32-bit keys,
+// staged in LDS by the first pass for rows of up to 32 keys per thread (32768 or 8192
+// candidates; longer rows are read again by every pass); a radix select
 // (digits of 11, 11 and 10 bits, most significant first, 2048-bin histograms in LDS:
 // wide enough that similar logits rarely collide on one bin) finds the k-th largest
 // key K and how many keys equal to K are taken (m); one ordered pass then emits every
